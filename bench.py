@@ -1,0 +1,239 @@
+"""MoE-layer forward benchmark on one MI355X.
+
+One step = one pass of the whole layer (route -> permute -> expert FFN ->
+combine, plus the shared expert where the workload has one) over one batch,
+inputs already resident in HBM.  Weight sets of several layers are rotated so
+that the touched expert bytes of consecutive steps do not sit in the 256 MB
+last-level cache (a model walks its layers the same way), and every step gets
+a fresh batch of logits and activations.
+
+Prints ONE JSON line: tokens/s of the whole job, the dominant kernel's
+roofline fraction (HIP events around the expert-FFN call on its stream inside
+the timed region), and the CPU oracle timed on a bounded sample as baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+LLC_BYTES = 256 << 20           # Infinity Cache
+
+DEFAULTS = {  # workload -> (steps, warmup, batches)
+    "tiny_bf16": (200, 20, 16),
+    "decode_mxfp4": (400, 40, 64),
+    "prefill_nvfp4": (50, 5, 8),
+    "fp8_lru_pool": (24, 2, 12),
+    "large_prefill_mxfp4": (10, 2, 2),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode_mxfp4")
+    ap.add_argument("--rot", type=int, default=0, help="weight sets rotated (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--variant", default="auto")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer has no "
+              "multi-GPU path in this build.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import moe_expert_ffn_router_amd as moe
+    import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    steps_d, warm_d, nb = DEFAULTS[wl.name]
+    steps = args.steps if args.steps is not None else steps_d
+    warmup = args.warmup if args.warmup is not None else warm_d
+    dev = torch.device("cuda")
+    torch.cuda.set_device(0)
+
+    lay = synth.record_layout(wl.fmt, wl.H, wl.I)
+    stride, payload = lay["stride"], lay["payload"]
+
+    # ---- inputs, resident in HBM -------------------------------------------
+    t0 = time.time()
+    base_set = synth.make_expert_records(wl.fmt, wl.E, wl.H, wl.I, wl.seed, device=dev)
+    logits = [torch.from_numpy(synth.make_logits(wl, b)).to(dev) for b in range(nb)]
+    xs = [torch.from_numpy(synth.make_x(wl, b).view(np.int16)).to(dev).view(torch.bfloat16)
+          for b in range(nb)]
+    shared = None
+    if wl.shared_I:
+        shared = synth.make_shared_record(wl.seed, wl.H, wl.shared_I, device=dev)
+
+    layer = moe.MoELayer(wl.fmt, wl.E, wl.H, wl.I, wl.k, wl.T, stride, shared_I=wl.shared_I,
+                         shared_stride=shared.shape[1] if shared is not None else 0)
+    Ws = moe.experts("bf16", 1, wl.H, wl.shared_I, shared, shared.shape[1]) if shared is not None else None
+
+    # touched experts per batch (from the device routing) -> algorithmic bytes
+    touched = []
+    for b in range(nb):
+        layer.route(logits[b])
+        layer.permute(wl.T)
+        touched.append(int((layer.counts[:wl.E] > 0).sum().item()))
+    touched_bytes = float(np.mean(touched)) * payload
+
+    rot = args.rot or max(1, int(np.ceil(4 * LLC_BYTES / max(touched_bytes, 1))))
+    rot = min(rot, max(1, int(0.5 * torch.cuda.mem_get_info()[0] // (wl.E * stride))))
+    sets = [base_set] + [base_set.clone() for _ in range(rot - 1)]
+    Wsets = [layer.weights(s) for s in sets]
+    setup_s = time.time() - t0
+
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        b = i % nb
+        layer.route(logits[b])
+        layer.permute(wl.T)
+        if ev is not None:
+            ev[0].record(stream)
+        layer.expert_ffn(Wsets[i % rot], xs[b], wl.T, variant=args.variant)
+        if ev is not None:
+            ev[1].record(stream)
+        if Ws is not None:
+            layer.shared_ffn(Ws, xs[b], wl.T, variant=args.variant)
+        layer.combine(wl.T, Ws is not None)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        step(warmup + i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ms_per_step = total_ms / steps
+    tokens_per_s = wl.T * steps / (total_ms / 1e3)
+
+    # ---- roofline of the dominant kernel (expert FFN) -------------------------
+    A = wl.T * wl.k
+    step_batches = [(warmup + i) % nb for i in range(steps)]
+    t_mean = float(np.mean([touched[b] for b in step_batches]))
+    ffn_bytes = t_mean * payload + wl.T * wl.H * 2 + 2 * A * wl.I * 2 + A * wl.H * 2
+    ffn_flops = 2.0 * A * 3 * wl.H * wl.I
+    decode = wl.T * wl.k <= 2 * wl.E
+    if decode:
+        achieved = ffn_bytes / (ffn_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        achieved = ffn_flops / (ffn_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": None}
+    roof.update({"kernel": "moe_expert_ffn", "ffn_ms": round(ffn_ms, 5),
+                 "algorithmic_bytes_per_launch": int(ffn_bytes),
+                 "algorithmic_flops_per_launch": int(ffn_flops),
+                 "touched_experts_mean": round(t_mean, 2)})
+
+    # ---- CPU baseline: the oracle on a bounded sample ---------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, base_set, shared, args.cpu_seconds)
+
+    out = {
+        "metric": "MoE-layer tokens/s at 1 GPU; % HBM roofline (decode), % MFMA peak (prefill)",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "I": wl.I, "k": wl.k,
+                   "weights": wl.fmt, "shared_I": wl.shared_I, "global_batch": wl.T,
+                   "weight_sets_rotated": rot, "batches_rotated": nb,
+                   "boundary": "route->permute->expert_ffn->combine on one stream, eager launches",
+                   "parallelism": "none (1 GPU)", "setup_s": round(setup_s, 1)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, base_set, shared, budget_s):
+    """Time the CPU oracle (float64 numpy) on whole batches of the same workload."""
+    import torch
+    from oracle import layer as OL
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    recs = {}
+
+    def rec(e):
+        if e not in recs:
+            recs[e] = base_set[e].cpu().numpy()
+        return recs[e]
+
+    sh = None
+    if shared is not None:
+        s_host = shared[0].cpu().numpy()
+        sh = OL.ExpertSet("bf16", wl.H, wl.shared_I, lambda e: s_host)
+    T_sample = wl.T
+    # large batches: a token subset of the batch (per-token outputs are independent)
+    if wl.T * wl.k * 3 * wl.H * wl.I * 2 > 2e11:
+        T_sample = max(1, int(2e11 / (wl.k * 3 * wl.H * wl.I * 2)))
+    done_tokens, t0, b = 0, time.time(), 0
+    while True:
+        ex = OL.ExpertSet(wl.fmt, wl.H, wl.I, rec)
+        lg = synth_logits(wl, b)[:T_sample]
+        xb = synth_x(wl, b)[:T_sample]
+        OL.forward(lg, xb, wl.k, ex, shared=sh)
+        done_tokens += T_sample
+        b += 1
+        recs.clear()
+        if time.time() - t0 >= budget_s:
+            break
+    el = time.time() - t0
+    del torch
+    return {"value": round(done_tokens / el, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{b} batch(es) of {T_sample} of {wl.T} tokens, {wl.name} weights "
+                      f"(float64 numpy, weights decoded per call), {el:.1f} s"}
+
+
+def synth_logits(wl, b):
+    import synth
+    return synth.make_logits(wl, b)
+
+
+def synth_x(wl, b):
+    import synth
+    return synth.make_x(wl, b)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,237 @@
+/*
+ * moe_layer.h — C ABI of the MI355X (gfx950) MoE-layer forward library.
+ *
+ * One Mixture-of-Experts layer forward as used by an edge MoE serving engine
+ * (FreeToken pages: supported-models guide, sections "MoE strategies",
+ * "expert bank & LRU slot cache", "minimum cache constraint", "how
+ * quantizations land"; README feature list; fork README, production
+ * configuration): route each token to k experts, group the (token, slot)
+ * assignments by expert, run each expert's SwiGLU FFN over its rows with
+ * weights stored as BF16 / MXFP4 / NVFP4 / FP8, and combine the k outputs of
+ * every token with its routing weights.  Experts are addressed through a slot
+ * table into a fixed HBM pool that an LRU policy refills from a pinned host
+ * bank.
+ *
+ * Conventions shared by every call
+ *  - All pointers are owned by the caller.  "device" pointers are HIP device
+ *    memory (or host memory mapped for the device), "host" pointers ordinary
+ *    host memory.  No call allocates device memory; scratch space is passed
+ *    in as `ws` after sizing it with the matching *_workspace query.
+ *  - Calls enqueue work on the given stream and return without waiting, so
+ *    route / permute / expert_ffn / combine can be captured into a HIP graph.
+ *  - Every call validates its arguments before enqueueing anything and
+ *    returns a moe_status; nothing aborts or throws across the ABI.  On an
+ *    error, moe_last_error() returns a message for the calling thread.
+ *  - Device pointers must be 16-byte aligned.  Results are deterministic:
+ *    there are no floating-point atomics, so repeated calls on the same
+ *    inputs give identical bits.
+ *  - bf16 tensors are passed as uint16_t bit patterns; fp32 as float.
+ */
+#ifndef MOE_LAYER_H
+#define MOE_LAYER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* moe_stream_t; /* a hipStream_t; NULL = null stream */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* bad size, null pointer, misalignment, bad id      */
+  MOE_ERR_UNSUPPORTED = 2, /* shape or format outside the supported set         */
+  MOE_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed        */
+  MOE_ERR_CAPACITY = 4,    /* cache: more distinct experts needed than slots    */
+  MOE_ERR_WORKSPACE = 5    /* ws too small (see the *_workspace queries)         */
+} moe_status;
+
+/* Expert weight storage formats (README "Broad MoE & ecosystem support";
+ * guide "CPU layer split" lists bf16, nvfp4, mxfp4 and fp8 experts). */
+typedef enum {
+  MOE_W_BF16 = 0,     /* plain bf16                                             */
+  MOE_W_MXFP4 = 1,    /* E2M1 codes, one E8M0 scale per 32 along K              */
+  MOE_W_NVFP4 = 2,    /* E2M1 codes, one E4M3 scale per 16 along K, and one
+                         fp32 scale per (expert, projection)                    */
+  MOE_W_FP8_B128 = 3  /* E4M3 codes, one fp32 scale per 128 x 128 block         */
+} moe_wfmt;
+
+/* Byte offsets of the sections inside one expert record; -1 = absent.
+ *
+ * One expert = one record; sections start at 256-byte aligned offsets in the
+ * order w13, w13_scale, w2, w2_scale, tensor_scale, and the record stride is
+ * the payload rounded up to 256.  All matrices are row-major with K (the
+ * reduction index) contiguous:
+ *   w13  [2I][H]  rows 0..I-1 = gate projection, rows I..2I-1 = up projection
+ *   w2   [H][I]   down projection
+ *   E2M1 codes: two per byte, element 2i in the low nibble, 2i+1 in the high
+ *   MXFP4 scales [rows][K/32] E8M0;  NVFP4 scales [rows][K/16] E4M3 (>= 0)
+ *   NVFP4 tensor_scale fp32[3] = (gate, up, down)
+ *   FP8 scales fp32 [rows/128][K/128]                                         */
+typedef struct {
+  int64_t w13, w13_scale, w2, w2_scale, tensor_scale;
+  int64_t payload_bytes; /* bytes that carry data (sum of section sizes)      */
+  int64_t stride;        /* record size in memory (payload rounded to 256)    */
+} moe_expert_layout;
+
+/* Fill *out for format fmt and sizes H (hidden), I (expert intermediate).
+ * Supported: H and I multiples of 128, 128 <= H, I <= 16384.               */
+int moe_expert_layout_query(int32_t fmt, int32_t H, int32_t I, moe_expert_layout* out);
+
+/* One layer's experts.  Record of expert e is at
+ *   base + (slot_of_expert ? slot_of_expert[e] : e) * stride                 */
+typedef struct {
+  int32_t fmt;        /* moe_wfmt                                             */
+  int32_t E;          /* experts in the layer, 1..1024                        */
+  int32_t H, I;       /* hidden size, expert intermediate size                */
+  const void* base;   /* device: E records, or the S records of a slot pool   */
+  int64_t stride;     /* bytes between records, == moe_expert_layout.stride   */
+} moe_experts;
+
+/* ---------------------------------------------------------------------------
+ * moe_route — router top-k with renormalised weights.
+ * The pages state that each token activates a few experts of the layer
+ * (guide, "MoE strategies") and give no router formula; this computes, per
+ * token t, the k experts with the largest logits (ties -> lower index wins,
+ * -0.0 == +0.0), in that order, and the softmax over those k logits
+ * (renorm = 1) or the full-softmax probabilities of those k (renorm = 0).
+ *   logits   device fp32 [T][E] row-major
+ *   topk_ids device int32 [T][k] (out)     topk_w device fp32 [T][k] (out)
+ * 1 <= k <= min(E, 16), 1 <= E <= 1024, T >= 0 (T = 0 is a no-op).
+ * NaN logits give unspecified (but in-range) ids.                           */
+int moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t renorm,
+              int32_t* topk_ids, float* topk_w, moe_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_permute — group the A = T*k assignments a = t*k + j by expert
+ * (stable counting sort; the fork README's per-layer prefill MoE kernel works
+ * on per-expert row blocks):
+ *   counts[e]     = #{a : topk_ids[a] == e}               device int32 [E]
+ *   offsets[e]    = sum of counts[0..e-1], offsets[E] = A   device int32 [E+1]
+ *   sorted_idx[p] = assignments in expert order, ascending a in each expert
+ *                                                           device int32 [A]
+ *   inv_idx[a]    = p with sorted_idx[p] == a                device int32 [A]
+ * Ids must lie in [0, E) (an id outside gives unspecified output but no
+ * out-of-bounds access).  ws: device, >= moe_permute_workspace(T, k, E).    */
+size_t moe_permute_workspace(int32_t T, int32_t k, int32_t E);
+int moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* counts,
+                int32_t* offsets, int32_t* sorted_idx, int32_t* inv_idx, void* ws,
+                size_t ws_bytes, moe_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_expert_ffn — per-expert SwiGLU FFN over the permuted rows.
+ * For every expert e with rows p in [offsets[e], offsets[e+1]):
+ *   x_p      = x[sorted_idx[p] / k]                       (bf16 row, H)
+ *   h_p      = SiLU(x_p W_gate[e]^T) * (x_p W_up[e]^T)    (I values)
+ *   y_perm_p = h_p W_down[e]^T                            (H values, bf16)
+ * with SiLU(z) = z / (1 + e^-z), fp32 accumulation, weights decoded exactly
+ * (MXFP4, NVFP4 block part and FP8 values are exact in bf16; FP8 block scales
+ * and NVFP4 tensor scales are applied to fp32 partial sums).  The activation
+ * is not named on the pages; SwiGLU is the plainest reading for the MoE
+ * families the guide lists.
+ *   slot_of_expert  device int32 [E] or NULL (identity); only entries of
+ *                   experts with counts[e] > 0 are read and must lie in
+ *                   [0, pool slots)
+ *   x               device bf16 [T][H]
+ *   counts, offsets, sorted_idx   from moe_permute
+ *   y_perm          device bf16 [T*k][H] (out, permuted order)
+ *   variant         0 = choose by size, 1 = small-batch (decode) kernels,
+ *                   2 = tiled (prefill) kernels; all give the same result up
+ *                   to fp32 summation order
+ * ws: device, >= moe_expert_ffn_workspace(W, T, k).                         */
+size_t moe_expert_ffn_workspace(const moe_experts* W, int32_t T, int32_t k);
+int moe_expert_ffn(const moe_experts* W, const int32_t* slot_of_expert, const uint16_t* x,
+                   int32_t T, int32_t k, const int32_t* counts, const int32_t* offsets,
+                   const int32_t* sorted_idx, uint16_t* y_perm, int32_t variant, void* ws,
+                   size_t ws_bytes, moe_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_combine — weighted sum of each token's k expert outputs:
+ *   y[t] = sum_{j<k} topk_w[t][j] * y_perm[inv_idx[t*k+j]]  (+ y_shared[t])
+ * summed in j order in fp32, rounded once to bf16 (nearest-even).
+ *   y_perm device bf16 [T*k][H]; inv_idx device int32 [T*k];
+ *   topk_w device fp32 [T][k]; y_shared device bf16 [T][H] or NULL (the
+ *   always-on shared expert, weight 1.0); y device bf16 [T][H] (out).
+ * H a multiple of 8.                                                        */
+int moe_combine(const uint16_t* y_perm, const int32_t* inv_idx, const float* topk_w, int32_t T,
+                int32_t k, int32_t H, const uint16_t* y_shared, uint16_t* y,
+                moe_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_dequant_expert — decode one expert record to fp32 with the same device
+ * decoders the FFN kernels use (for checking every code on the device).
+ *   w13 device fp32 [2I][H] (out), w2 device fp32 [H][I] (out); the NVFP4
+ *   tensor scales are applied, the FP8 block scales too (one fp32 product).  */
+int moe_dequant_expert(const moe_experts* W, int32_t expert, float* w13, float* w2,
+                       moe_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Expert-slot cache (guide, "expert bank & LRU slot cache", "MoE strategies"
+ * offload, "minimum cache constraint").  A fixed pool of S slots in HBM,
+ * shared by all layers, holds expert records; the slot table maps
+ * (layer, expert) to a slot.  The handle owns host metadata only.
+ *
+ * Policy (deterministic LRU; the pages give only "LRU" and "most recent active
+ * step" per (layer, expert)):
+ *   needed  = experts with counts[e] > 0, ascending
+ *   |needed| > S            -> MOE_ERR_CAPACITY, state unchanged
+ *   misses  = needed not resident, ascending; each takes the lowest empty
+ *             slot, else the slot whose owner is not needed now with the
+ *             smallest (last-active step, slot index)
+ *   every needed slot's last-active step := the step clock; clock += 1
+ *
+ * moe_cache_create
+ *   pool_dev        device, S * slot_bytes bytes (slot s at s * slot_bytes)
+ *   bank_host       host memory allocated pinned (hipHostMalloc / torch
+ *                   pin_memory), n_layers * E records of slot_bytes, record of
+ *                   (layer, e) at (layer * E + e) * slot_bytes
+ *   slot_table_dev  device int32 [n_layers][E]; the cache writes the slot of
+ *                   every expert it makes resident (other entries untouched)
+ *   The cache starts empty.  1 <= S, slot_bytes > 0 and a multiple of 256.  */
+typedef struct moe_cache* moe_cache_t;
+
+int moe_cache_create(moe_cache_t* out, int32_t n_layers, int32_t E, int32_t S,
+                     int64_t slot_bytes, void* pool_dev, const void* bank_host,
+                     int32_t* slot_table_dev);
+void moe_cache_destroy(moe_cache_t cache);
+
+/* expert_cache_lookup — run the policy for one (layer-)step.
+ *   counts_host  host int32 [E] (the caller's copy of moe_permute's counts)
+ *   miss_expert, miss_slot   host int32 [E] (out): the fills to make, in order
+ *   n_miss, n_hit            host (out)
+ *   slot_row_host            host int32 [E] (out, may be NULL): the layer's
+ *                            slot table row after this step (-1 = not resident)
+ * On MOE_ERR_CAPACITY nothing changes.  Host-only; touches no device memory. */
+int expert_cache_lookup(moe_cache_t cache, int32_t layer, const int32_t* counts_host,
+                        int32_t* miss_expert, int32_t* miss_slot, int32_t* n_miss,
+                        int32_t* n_hit, int32_t* slot_row_host);
+
+/* expert_cache_fill — make the lookup's misses resident and publish the slot
+ * table row for `layer`:
+ *   1. `side` waits for all work already enqueued on `compute` (so a victim
+ *      slot is never overwritten while an earlier FFN still reads it);
+ *   2. one hipMemcpyAsync host->device per miss, bank -> pool slot, on `side`;
+ *   3. the layer's slot-table row is copied host->device on `side`;
+ *   4. `compute` waits for `side`.
+ * Work enqueued on `compute` afterwards sees the filled slots.  miss arrays
+ * as returned by expert_cache_lookup for the same layer.                     */
+int expert_cache_fill(moe_cache_t cache, int32_t layer, const int32_t* miss_expert,
+                      const int32_t* miss_slot, int32_t n_miss, moe_stream_t side,
+                      moe_stream_t compute);
+
+/* Counters since creation: steps, hits, misses, bytes copied host->device. */
+int moe_cache_stats(moe_cache_t cache, int64_t* steps, int64_t* hits, int64_t* misses,
+                    int64_t* bytes_filled);
+
+/* ---------------------------------------------------------------------------
+ * Diagnostics. */
+const char* moe_status_str(int status);
+const char* moe_last_error(void); /* thread-local; "" when none */
+int moe_version(void);            /* ABI version, currently 1 */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_LAYER_H */

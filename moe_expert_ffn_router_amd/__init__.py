@@ -1,0 +1,228 @@
+"""MI355X (gfx950) MoE-layer forward: Python binding of libmoe_mi355x.so.
+
+Thin ctypes marshalling over the C ABI declared in include/moe_layer.h: every
+function here has the name of the C entry point it calls, turns torch tensors
+into device pointers and the current torch stream into a hipStream_t, and
+raises MoeError on a non-zero status.  Every step of the layer runs in the
+library's HIP kernels; there is no Python or CPU fallback — importing this
+package fails if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP, MOE_ERR_CAPACITY, \
+    MOE_ERR_WORKSPACE = range(6)
+FMT = {"bf16": 0, "mxfp4": 1, "nvfp4": 2, "fp8_b128": 3}
+VARIANT = {"auto": 0, "decode": 1, "prefill": 2}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()' "
+        "or python moe_expert_ffn_router_amd/build.py)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_p, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+
+
+class ExpertLayout(ctypes.Structure):
+    _fields_ = [("w13", _i64), ("w13_scale", _i64), ("w2", _i64), ("w2_scale", _i64),
+                ("tensor_scale", _i64), ("payload_bytes", _i64), ("stride", _i64)]
+
+
+class Experts(ctypes.Structure):
+    _fields_ = [("fmt", _i32), ("E", _i32), ("H", _i32), ("I", _i32), ("base", _p),
+                ("stride", _i64)]
+
+
+_SIGS = {
+    "moe_expert_layout_query": (ctypes.c_int, [_i32, _i32, _i32, ctypes.POINTER(ExpertLayout)]),
+    "moe_route": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _p, _p, _p]),
+    "moe_permute_workspace": (_sz, [_i32, _i32, _i32]),
+    "moe_permute": (ctypes.c_int, [_p, _i32, _i32, _i32, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_expert_ffn_workspace": (_sz, [ctypes.POINTER(Experts), _i32, _i32]),
+    "moe_expert_ffn": (ctypes.c_int, [ctypes.POINTER(Experts), _p, _p, _i32, _i32, _p, _p, _p, _p,
+                                      _i32, _p, _sz, _p]),
+    "moe_combine": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _p, _p, _p]),
+    "moe_dequant_expert": (ctypes.c_int, [ctypes.POINTER(Experts), _i32, _p, _p, _p]),
+    "moe_cache_create": (ctypes.c_int, [ctypes.POINTER(_p), _i32, _i32, _i32, _i64, _p, _p, _p]),
+    "moe_cache_destroy": (None, [_p]),
+    "expert_cache_lookup": (ctypes.c_int, [_p, _i32, _p, _p, _p, _p, _p, _p]),
+    "expert_cache_fill": (ctypes.c_int, [_p, _i32, _p, _p, _i32, _p, _p]),
+    "moe_cache_stats": (ctypes.c_int, [_p, _p, _p, _p, _p]),
+    "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_version": (ctypes.c_int, []),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+def exported_symbols() -> list[str]:
+    return sorted(_SIGS)
+
+
+def _check(status: int, what: str) -> None:
+    if status != MOE_OK:
+        msg = _lib.moe_last_error().decode(errors="replace")
+        name = _lib.moe_status_str(status).decode()
+        raise MoeError(status, f"{what}: {name}: {msg}")
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"expected a tensor, got {type(t)}")
+    if t.numel() and not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr() if t.numel() else None
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dev_check(*ts):
+    for t in ts:
+        if isinstance(t, torch.Tensor) and t.numel() and not t.is_cuda:
+            raise ValueError("device tensor expected")
+
+
+# ---------------------------------------------------------------------------
+def moe_expert_layout_query(fmt: str | int, H: int, I: int) -> dict:
+    out = ExpertLayout()
+    _check(_lib.moe_expert_layout_query(FMT.get(fmt, fmt), H, I, ctypes.byref(out)),
+           "moe_expert_layout_query")
+    return {f: getattr(out, f) for f, _ in ExpertLayout._fields_}
+
+
+def experts(fmt: str | int, E: int, H: int, I: int, base: torch.Tensor | int, stride: int) -> Experts:
+    """moe_experts descriptor over `base` (a device tensor or a raw pointer)."""
+    return Experts(FMT.get(fmt, fmt), E, H, I, _ptr(base), stride)
+
+
+def moe_route(logits, k: int, topk_ids, topk_w, renorm: bool = True, stream=None) -> None:
+    _dev_check(logits, topk_ids, topk_w)
+    T, E = logits.shape
+    _check(_lib.moe_route(_ptr(logits), T, E, k, int(renorm), _ptr(topk_ids), _ptr(topk_w),
+                          _stream(stream)), "moe_route")
+
+
+def moe_permute_workspace(T: int, k: int, E: int) -> int:
+    return int(_lib.moe_permute_workspace(T, k, E))
+
+
+def moe_permute(topk_ids, T: int, k: int, E: int, counts, offsets, sorted_idx, inv_idx, ws,
+                stream=None) -> None:
+    _dev_check(topk_ids, counts, offsets, sorted_idx, inv_idx, ws)
+    _check(_lib.moe_permute(_ptr(topk_ids), T, k, E, _ptr(counts), _ptr(offsets),
+                            _ptr(sorted_idx), _ptr(inv_idx), _ptr(ws),
+                            ws.numel() * ws.element_size() if ws is not None else 0,
+                            _stream(stream)), "moe_permute")
+
+
+def moe_expert_ffn_workspace(W: Experts, T: int, k: int) -> int:
+    return int(_lib.moe_expert_ffn_workspace(ctypes.byref(W), T, k))
+
+
+def moe_expert_ffn(W: Experts, slot_of_expert, x, T: int, k: int, counts, offsets, sorted_idx,
+                   y_perm, ws, variant: str | int = "auto", stream=None) -> None:
+    _dev_check(slot_of_expert, x, counts, offsets, sorted_idx, y_perm, ws)
+    _check(_lib.moe_expert_ffn(ctypes.byref(W), _ptr(slot_of_expert), _ptr(x), T, k, _ptr(counts),
+                               _ptr(offsets), _ptr(sorted_idx), _ptr(y_perm),
+                               VARIANT.get(variant, variant), _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_expert_ffn")
+
+
+def moe_combine(y_perm, inv_idx, topk_w, T: int, k: int, H: int, y_shared, y, stream=None) -> None:
+    _dev_check(y_perm, inv_idx, topk_w, y_shared, y)
+    _check(_lib.moe_combine(_ptr(y_perm), _ptr(inv_idx), _ptr(topk_w), T, k, H, _ptr(y_shared),
+                            _ptr(y), _stream(stream)), "moe_combine")
+
+
+def moe_dequant_expert(W: Experts, expert: int, w13, w2, stream=None) -> None:
+    _dev_check(w13, w2)
+    _check(_lib.moe_dequant_expert(ctypes.byref(W), expert, _ptr(w13), _ptr(w2), _stream(stream)),
+           "moe_dequant_expert")
+
+
+class ExpertCache:
+    """Owner of a moe_cache_t handle (host metadata only)."""
+
+    def __init__(self, n_layers: int, E: int, S: int, slot_bytes: int, pool=None, bank=None,
+                 slot_table=None):
+        h = ctypes.c_void_p()
+        _check(_lib.moe_cache_create(ctypes.byref(h), n_layers, E, S, slot_bytes, _ptr(pool),
+                                     _ptr(bank), _ptr(slot_table)), "moe_cache_create")
+        self._h = h
+        self.E, self.S = E, S
+        self._keep = (pool, bank, slot_table)
+        self.miss_e = torch.zeros(E, dtype=torch.int32)
+        self.miss_s = torch.zeros(E, dtype=torch.int32)
+        self.row = torch.zeros(E, dtype=torch.int32)
+
+    def close(self):
+        if self._h:
+            _lib.moe_cache_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def expert_cache_lookup(self, layer: int, counts_host: torch.Tensor):
+        c = counts_host.to(torch.int32).contiguous()
+        nm, nh = ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib.expert_cache_lookup(self._h, layer, _ptr(c), _ptr(self.miss_e),
+                                        _ptr(self.miss_s), ctypes.byref(nm), ctypes.byref(nh),
+                                        _ptr(self.row)), "expert_cache_lookup")
+        n = nm.value
+        return (self.miss_e[:n].clone(), self.miss_s[:n].clone(), n, nh.value, self.row.clone())
+
+    def expert_cache_fill(self, layer: int, miss_expert, miss_slot, side=None, compute=None):
+        me = miss_expert.to(torch.int32).contiguous()
+        ms = miss_slot.to(torch.int32).contiguous()
+        _check(_lib.expert_cache_fill(self._h, layer, _ptr(me), _ptr(ms), int(me.numel()),
+                                      _stream(side), _stream(compute)), "expert_cache_fill")
+
+    def stats(self) -> dict:
+        v = [ctypes.c_int64() for _ in range(4)]
+        _check(_lib.moe_cache_stats(self._h, *[ctypes.byref(x) for x in v]), "moe_cache_stats")
+        return dict(zip(("steps", "hits", "misses", "bytes_filled"), (x.value for x in v)))
+
+
+def moe_version() -> int:
+    return int(_lib.moe_version())
+
+
+from .layer import MoELayer  # noqa: E402,F401
+
+
+def moe_status_str_py(status: int) -> str:
+    return _lib.moe_status_str(status).decode()

@@ -1,0 +1,214 @@
+// Expert-slot cache: host-side LRU over a fixed HBM pool of expert records,
+// refilled from a pinned host bank (FreeToken guide, "expert bank & LRU slot
+// cache", "MoE strategies" offload, "minimum cache constraint").
+//
+// The handle owns host metadata only: slot owners, last-active steps, the
+// step clock and a small ring of pinned slot-table rows used as sources of
+// the host->device slot-table updates (a row is never rewritten while an
+// earlier copy from it may still be pending).
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "moe_internal.h"
+
+namespace {
+
+constexpr int kRing = 8;
+
+struct Cache {
+  int L = 0, E = 0, S = 0;
+  int64_t slot_bytes = 0;
+  uint8_t* pool = nullptr;
+  const uint8_t* bank = nullptr;
+  int32_t* table_dev = nullptr;
+  std::vector<int64_t> owner;    // per slot: layer*E + expert, or -1
+  std::vector<int64_t> recency;  // per slot: last active step
+  std::vector<int32_t> where;    // per (layer, expert): slot or -1
+  int64_t clock = 0;
+  int64_t st_steps = 0, st_hits = 0, st_misses = 0, st_bytes = 0;
+  int32_t* ring = nullptr;  // pinned [kRing][E]
+  hipEvent_t ring_done[kRing] = {};
+  bool ring_used[kRing] = {};
+  int ring_next = 0;
+  hipEvent_t compute_mark = nullptr, side_done = nullptr;
+};
+
+}  // namespace
+
+struct moe_cache : Cache {};
+
+using moe::set_error;
+
+extern "C" int moe_cache_create(moe_cache_t* out, int32_t n_layers, int32_t E, int32_t S,
+                                int64_t slot_bytes, void* pool_dev, const void* bank_host,
+                                int32_t* slot_table_dev) {
+  if (!out) return set_error(MOE_ERR_INVALID_ARG, "moe_cache_create: out is NULL");
+  *out = nullptr;
+  if (n_layers < 1 || E < 1 || E > moe::kMaxE || S < 1 || slot_bytes <= 0 || slot_bytes % 256)
+    return set_error(MOE_ERR_INVALID_ARG,
+                     "moe_cache_create: need n_layers>=1, 1<=E<=%d, S>=1, slot_bytes>0 and a "
+                     "multiple of 256", moe::kMaxE);
+  moe_cache* c = new (std::nothrow) moe_cache();
+  if (!c) return set_error(MOE_ERR_INVALID_ARG, "moe_cache_create: out of host memory");
+  c->L = n_layers; c->E = E; c->S = S; c->slot_bytes = slot_bytes;
+  c->pool = static_cast<uint8_t*>(pool_dev);
+  c->bank = static_cast<const uint8_t*>(bank_host);
+  c->table_dev = slot_table_dev;
+  c->owner.assign(S, -1);
+  c->recency.assign(S, -1);
+  c->where.assign((size_t)n_layers * E, -1);
+  // Device-side pieces are only needed by expert_cache_fill; a handle without
+  // them still runs the policy (expert_cache_lookup is host-only).
+  if (pool_dev && bank_host && slot_table_dev) {
+    if (hipHostMalloc((void**)&c->ring, sizeof(int32_t) * kRing * E, hipHostMallocDefault) !=
+        hipSuccess) {
+      delete c;
+      return set_error(MOE_ERR_HIP, "moe_cache_create: hipHostMalloc failed");
+    }
+    bool ok = hipEventCreateWithFlags(&c->compute_mark, hipEventDisableTiming) == hipSuccess &&
+              hipEventCreateWithFlags(&c->side_done, hipEventDisableTiming) == hipSuccess;
+    for (int i = 0; ok && i < kRing; ++i)
+      ok = hipEventCreateWithFlags(&c->ring_done[i], hipEventDisableTiming) == hipSuccess;
+    if (!ok) {
+      moe_cache_destroy(c);
+      return set_error(MOE_ERR_HIP, "moe_cache_create: hipEventCreate failed");
+    }
+  }
+  *out = c;
+  return MOE_OK;
+}
+
+extern "C" void moe_cache_destroy(moe_cache_t c) {
+  if (!c) return;
+  for (int i = 0; i < kRing; ++i)
+    if (c->ring_done[i]) {
+      if (c->ring_used[i]) (void)hipEventSynchronize(c->ring_done[i]);
+      (void)hipEventDestroy(c->ring_done[i]);
+    }
+  if (c->compute_mark) (void)hipEventDestroy(c->compute_mark);
+  if (c->side_done) (void)hipEventDestroy(c->side_done);
+  if (c->ring) (void)hipHostFree(c->ring);
+  delete c;
+}
+
+extern "C" int expert_cache_lookup(moe_cache_t c, int32_t layer, const int32_t* counts_host,
+                                   int32_t* miss_expert, int32_t* miss_slot, int32_t* n_miss,
+                                   int32_t* n_hit, int32_t* slot_row_host) {
+  if (!c || !counts_host || !miss_expert || !miss_slot || !n_miss || !n_hit)
+    return set_error(MOE_ERR_INVALID_ARG, "expert_cache_lookup: null argument");
+  if (layer < 0 || layer >= c->L)
+    return set_error(MOE_ERR_INVALID_ARG, "expert_cache_lookup: layer %d of %d", layer, c->L);
+  const int E = c->E, S = c->S;
+  std::vector<int> needed;
+  needed.reserve(E);
+  for (int e = 0; e < E; ++e) {
+    if (counts_host[e] < 0)
+      return set_error(MOE_ERR_INVALID_ARG, "expert_cache_lookup: counts[%d] < 0", e);
+    if (counts_host[e] > 0) needed.push_back(e);
+  }
+  if ((int)needed.size() > S)
+    return set_error(MOE_ERR_CAPACITY,
+                     "expert_cache_lookup: layer %d needs %d distinct experts, pool has %d slots",
+                     layer, (int)needed.size(), S);
+  const int64_t key0 = (int64_t)layer * E;
+  std::vector<char> is_needed_slot(S, 0);
+  for (int e : needed) {
+    const int s = c->where[key0 + e];
+    if (s >= 0) is_needed_slot[s] = 1;
+  }
+  int nm = 0;
+  int next_empty = 0;
+  for (int e : needed) {
+    if (c->where[key0 + e] >= 0) continue;
+    int s = -1;
+    while (next_empty < S && c->owner[next_empty] >= 0) ++next_empty;
+    if (next_empty < S) {
+      s = next_empty;
+    } else {
+      int64_t best_r = 0;
+      for (int q = 0; q < S; ++q) {
+        if (is_needed_slot[q]) continue;
+        if (s < 0 || c->recency[q] < best_r) { s = q; best_r = c->recency[q]; }
+      }
+      // |needed| <= S guarantees a candidate; evict its owner
+      const int64_t old = c->owner[s];
+      c->where[old] = -1;
+    }
+    c->owner[s] = key0 + e;
+    c->where[key0 + e] = s;
+    is_needed_slot[s] = 1;
+    miss_expert[nm] = e;
+    miss_slot[nm] = s;
+    ++nm;
+  }
+  for (int e : needed) c->recency[c->where[key0 + e]] = c->clock;
+  c->clock += 1;
+  *n_miss = nm;
+  *n_hit = (int)needed.size() - nm;
+  if (slot_row_host)
+    for (int e = 0; e < E; ++e) slot_row_host[e] = c->where[key0 + e];
+  c->st_steps += 1;
+  c->st_hits += *n_hit;
+  c->st_misses += nm;
+  return MOE_OK;
+}
+
+extern "C" int expert_cache_fill(moe_cache_t c, int32_t layer, const int32_t* miss_expert,
+                                 const int32_t* miss_slot, int32_t n_miss, moe_stream_t side,
+                                 moe_stream_t compute) {
+  if (!c) return set_error(MOE_ERR_INVALID_ARG, "expert_cache_fill: null handle");
+  if (!c->pool || !c->bank || !c->table_dev || !c->ring)
+    return set_error(MOE_ERR_INVALID_ARG, "expert_cache_fill: handle has no pool/bank/table");
+  if (layer < 0 || layer >= c->L || n_miss < 0 || n_miss > c->E ||
+      (n_miss > 0 && (!miss_expert || !miss_slot)))
+    return set_error(MOE_ERR_INVALID_ARG, "expert_cache_fill: bad layer or miss list");
+  for (int i = 0; i < n_miss; ++i) {
+    const int e = miss_expert[i], s = miss_slot[i];
+    if (e < 0 || e >= c->E || s < 0 || s >= c->S ||
+        c->owner[s] != (int64_t)layer * c->E + e)
+      return set_error(MOE_ERR_INVALID_ARG,
+                       "expert_cache_fill: miss %d (expert %d -> slot %d) is not a pending fill "
+                       "of layer %d", i, e, s, layer);
+  }
+  hipStream_t sd = reinterpret_cast<hipStream_t>(side);
+  hipStream_t cp = reinterpret_cast<hipStream_t>(compute);
+  const int r = c->ring_next;
+  c->ring_next = (r + 1) % kRing;
+  if (c->ring_used[r] && hipEventSynchronize(c->ring_done[r]) != hipSuccess)
+    return set_error(MOE_ERR_HIP, "expert_cache_fill: ring wait failed");
+  int32_t* row = c->ring + (size_t)r * c->E;
+  const int64_t key0 = (int64_t)layer * c->E;
+  for (int e = 0; e < c->E; ++e) row[e] = c->where[key0 + e];
+
+  hipError_t err = hipEventRecord(c->compute_mark, cp);
+  if (err == hipSuccess) err = hipStreamWaitEvent(sd, c->compute_mark, 0);
+  for (int i = 0; err == hipSuccess && i < n_miss; ++i) {
+    const int e = miss_expert[i], s = miss_slot[i];
+    err = hipMemcpyAsync(c->pool + (size_t)s * c->slot_bytes,
+                         c->bank + ((size_t)layer * c->E + e) * c->slot_bytes, c->slot_bytes,
+                         hipMemcpyHostToDevice, sd);
+  }
+  if (err == hipSuccess)
+    err = hipMemcpyAsync(c->table_dev + key0, row, sizeof(int32_t) * c->E, hipMemcpyHostToDevice,
+                         sd);
+  if (err == hipSuccess) err = hipEventRecord(c->ring_done[r], sd);
+  if (err == hipSuccess) c->ring_used[r] = true;
+  if (err == hipSuccess) err = hipEventRecord(c->side_done, sd);
+  if (err == hipSuccess) err = hipStreamWaitEvent(cp, c->side_done, 0);
+  if (err != hipSuccess)
+    return set_error(MOE_ERR_HIP, "expert_cache_fill: %s", hipGetErrorString(err));
+  c->st_bytes += (int64_t)n_miss * c->slot_bytes;
+  return MOE_OK;
+}
+
+extern "C" int moe_cache_stats(moe_cache_t c, int64_t* steps, int64_t* hits, int64_t* misses,
+                               int64_t* bytes_filled) {
+  if (!c) return set_error(MOE_ERR_INVALID_ARG, "moe_cache_stats: null handle");
+  if (steps) *steps = c->st_steps;
+  if (hits) *hits = c->st_hits;
+  if (misses) *misses = c->st_misses;
+  if (bytes_filled) *bytes_filled = c->st_bytes;
+  return MOE_OK;
+}

@@ -1,0 +1,160 @@
+// Internal declarations shared by the library's translation units.
+// gfx950 (CDNA4) only: wave64, MFMA bf16 16x16x32, OCP FP8/FP4 conversions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe_layer.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// host-side status plumbing
+// ---------------------------------------------------------------------------
+int set_error(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int check_launch(const char* what);  // hipGetLastError after a launch
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 16;
+constexpr int kChunk = 1024;  // assignments per permutation block
+
+// Record layout (host); mirrors the header's description.
+struct Layout {
+  int64_t w13, w13s, w2, w2s, ts, payload, stride;
+};
+bool layout_of(int fmt, int H, int I, Layout* out);
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// E8M0 byte -> fp32 scale 2^(b-127).  b = 0 gives the fp32 subnormal 2^-127;
+// b = 255 (NaN) gives NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
+  if (b == 0) return __uint_as_float(0x00400000u);
+  if (b == 255) return __uint_as_float(0x7fc00000u);
+  return __uint_as_float(b << 23);
+}
+
+// OCP E4M3 byte -> fp32, decoded from its bit fields (bias 7, subnormals kept,
+// S.1111.111 = NaN).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t s = (b >> 7) & 1u, e = (b >> 3) & 15u, m = b & 7u;
+  float mag;
+  if (e == 0) {
+    mag = (float)m * 0.001953125f;  // m/8 * 2^-6 = m * 2^-9
+  } else if (e == 15 && m == 7) {
+    mag = __uint_as_float(0x7fc00000u);
+  } else {
+    mag = __uint_as_float(((e + 120u) << 23) | (m << 20));  // (1+m/8) * 2^(e-7)
+  }
+  return s ? -mag : mag;
+}
+
+// E2M1 code -> fp32 from its bit fields (bias 1, no Inf/NaN).
+__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
+  const uint32_t s = (c >> 3) & 1u, e = (c >> 1) & 3u, m = c & 1u;
+  float mag = (e == 0) ? 0.5f * (float)m : __uint_as_float(((e + 126u) << 23) | (m << 22));
+  return s ? -mag : mag;
+}
+
+__device__ __forceinline__ bf16x8 bits_to_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  i32x4 v = {(int)a, (int)b, (int)c, (int)d};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// 8 E2M1 codes of one dword (element 2i = low nibble of byte i) -> 8 bf16,
+// each multiplied by `scale`, which must be a power of two (an E8M0 scale):
+// the CDNA4 scaled FP4 -> bf16 conversion applies only the scale's exponent.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w, float scale) {
+  bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  bf16x8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// 8 E2M1 codes -> 8 bf16 times an arbitrary fp32 scale `s` whose products
+// with the E2M1 values are exact in bf16 (an E4M3 block scale: at most 6
+// significant bits).  The scaled conversion instructions use only the
+// exponent of their scale operand, so the product is formed in fp32 (exact)
+// and its upper half taken (exact, no rounding needed).
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16_mul(uint32_t w, float s) {
+  const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  auto hi2 = [s](float a, float b) {
+    return __builtin_amdgcn_perm(__float_as_uint(b * s), __float_as_uint(a * s), 0x07060302u);
+  };
+  return bits_to_bf16x8(hi2(p0[0], p0[1]), hi2(p1[0], p1[1]), hi2(p2[0], p2[1]),
+                        hi2(p3[0], p3[1]));
+}
+
+// 8 E4M3 bytes (two dwords, byte i = element i) -> 8 bf16 (exact).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  bf16x8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+
+// Exclusive scan over n <= 1024 ints held in LDS `v` (in place); returns the
+// total.  Called by all 256 threads of a workgroup, 4 consecutive entries each.
+__device__ __forceinline__ int block_exclusive_scan_256(int* v, int E, int* wave_tot) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int loc[4], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * 4 + i;
+    loc[i] = (e < E) ? v[e] : 0;
+    sum += loc[i];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wave_tot[w];
+  const int total = wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
+  int run = base + incl - sum;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * 4 + i;
+    if (e < E) v[e] = run;
+    run += loc[i];
+  }
+  __syncthreads();
+  return total;
+}
+
+}  // namespace moe

@@ -1,0 +1,112 @@
+"""MoELayer: buffers + the call sequence of one layer forward.
+
+Owns the device buffers of one layer (routing results, permutation,
+workspaces, outputs) and issues route -> permute -> expert_ffn -> combine on
+one stream through the C ABI.  With an expert cache, the slot-table path is
+route -> permute -> counts to host -> expert_cache_lookup -> expert_cache_fill
+-> expert_ffn (through the slot table) -> combine.  No arithmetic happens
+here; it only sequences library calls.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (Experts, experts, moe_combine, moe_expert_ffn, moe_expert_ffn_workspace,
+               moe_permute, moe_permute_workspace, moe_route)
+
+
+def _i32(n, dev):
+    return torch.empty(max(int(n), 1), dtype=torch.int32, device=dev)
+
+
+class MoELayer:
+    def __init__(self, fmt: str, E: int, H: int, I: int, k: int, T_max: int, stride: int,
+                 shared_I: int = 0, shared_stride: int = 0, renorm: bool = True,
+                 device: str | torch.device = "cuda"):
+        self.fmt, self.E, self.H, self.I, self.k = fmt, E, H, I, k
+        self.T_max, self.stride, self.renorm = T_max, stride, renorm
+        dev = torch.device(device)
+        self.device = dev
+        A = T_max * k
+        self.ids = _i32(A, dev)
+        self.w = torch.empty(max(A, 1), dtype=torch.float32, device=dev)
+        self.counts = _i32(E, dev)
+        self.offsets = _i32(E + 1, dev)
+        self.sorted_idx = _i32(A, dev)
+        self.inv_idx = _i32(A, dev)
+        self.perm_ws = torch.empty(max(moe_permute_workspace(T_max, k, E), 256), dtype=torch.uint8,
+                                   device=dev)
+        probe = Experts(0, E, H, I, None, stride)
+        from . import FMT
+        probe.fmt = FMT[fmt]
+        self.ffn_ws = torch.empty(max(moe_expert_ffn_workspace(probe, T_max, k), 256),
+                                  dtype=torch.uint8, device=dev)
+        self.y_perm = torch.empty((max(A, 1), H), dtype=torch.bfloat16, device=dev)
+        self.y = torch.empty((max(T_max, 1), H), dtype=torch.bfloat16, device=dev)
+        self.shared_I = shared_I
+        if shared_I:
+            self.shared_stride = shared_stride
+            self.s_counts = torch.tensor([T_max], dtype=torch.int32, device=dev)
+            self.s_offsets = torch.tensor([0, T_max], dtype=torch.int32, device=dev)
+            self.s_sorted = torch.arange(T_max, dtype=torch.int32, device=dev)
+            sp = Experts(0, 1, H, shared_I, None, shared_stride)
+            self.s_ws = torch.empty(max(moe_expert_ffn_workspace(sp, T_max, 1), 256),
+                                    dtype=torch.uint8, device=dev)
+            self.y_shared = torch.empty((T_max, H), dtype=torch.bfloat16, device=dev)
+
+    # -- individual steps ---------------------------------------------------
+    def route(self, logits: torch.Tensor, stream=None):
+        T = logits.shape[0]
+        moe_route(logits, self.k, self.ids, self.w, self.renorm, stream)
+        return T
+
+    def permute(self, T: int, stream=None):
+        moe_permute(self.ids, T, self.k, self.E, self.counts, self.offsets, self.sorted_idx,
+                    self.inv_idx, self.perm_ws, stream)
+
+    def expert_ffn(self, W: Experts, x: torch.Tensor, T: int, slot_of_expert=None,
+                   variant="auto", stream=None):
+        moe_expert_ffn(W, slot_of_expert, x, T, self.k, self.counts, self.offsets, self.sorted_idx,
+                       self.y_perm, self.ffn_ws, variant, stream)
+
+    def shared_ffn(self, Ws: Experts, x: torch.Tensor, T: int, variant="auto", stream=None):
+        if T != self.T_max:
+            self.s_counts.fill_(T)
+            self.s_offsets[1].fill_(T)
+        moe_expert_ffn(Ws, None, x, T, 1, self.s_counts, self.s_offsets, self.s_sorted,
+                       self.y_shared, self.s_ws, variant, stream)
+
+    def combine(self, T: int, with_shared: bool, stream=None):
+        moe_combine(self.y_perm, self.inv_idx, self.w, T, self.k, self.H,
+                    self.y_shared if with_shared else None, self.y, stream)
+
+    # -- whole layer ----------------------------------------------------------
+    def weights(self, base) -> Experts:
+        return experts(self.fmt, self.E, self.H, self.I, base, self.stride)
+
+    def forward(self, logits: torch.Tensor, x: torch.Tensor, W: Experts, Ws: Experts | None = None,
+                slot_of_expert=None, variant="auto", stream=None) -> torch.Tensor:
+        T = logits.shape[0]
+        assert T <= self.T_max and x.shape == (T, self.H)
+        self.route(logits, stream)
+        self.permute(T, stream)
+        self.expert_ffn(W, x, T, slot_of_expert, variant, stream)
+        if Ws is not None:
+            self.shared_ffn(Ws, x, T, variant, stream)
+        self.combine(T, Ws is not None, stream)
+        return self.y[:T]
+
+    def forward_cached(self, logits: torch.Tensor, x: torch.Tensor, layer: int, cache,
+                       pool_W: Experts, slot_table: torch.Tensor, side=None, variant="auto",
+                       stream=None) -> tuple[torch.Tensor, dict]:
+        """Slot-table path: misses are filled from the pinned bank before the FFN."""
+        T = logits.shape[0]
+        self.route(logits, stream)
+        self.permute(T, stream)
+        counts_host = self.counts[:self.E].to("cpu")          # the one host sync of the step
+        me, ms, n_miss, n_hit, _ = cache.expert_cache_lookup(layer, counts_host)
+        cache.expert_cache_fill(layer, me, ms, side=side, compute=stream)
+        row = slot_table[layer * self.E:(layer + 1) * self.E]
+        self.expert_ffn(pool_W, x, T, row, variant, stream)
+        self.combine(T, False, stream)
+        return self.y[:T], {"misses": n_miss, "hits": n_hit, "fills": list(zip(me.tolist(), ms.tolist()))}
