@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--variant", default="auto")
+    ap.add_argument("--eager", action="store_true", help="launch eagerly instead of graph replay")
     return ap.parse_args()
 
 
@@ -88,8 +89,7 @@ def main():
     # touched experts per batch (from the device routing) -> algorithmic bytes
     touched = []
     for b in range(nb):
-        layer.route(logits[b])
-        layer.permute(wl.T)
+        layer.route_permute(logits[b])
         touched.append(int((layer.counts[:wl.E] > 0).sum().item()))
     touched_bytes = float(np.mean(touched)) * payload
 
@@ -100,35 +100,55 @@ def main():
     setup_s = time.time() - t0
 
     stream = torch.cuda.current_stream()
+    use_graph = not args.eager
 
-    def step(i, ev=None):
+    def step(i):
         b = i % nb
-        layer.route(logits[b])
-        layer.permute(wl.T)
-        if ev is not None:
-            ev[0].record(stream)
+        layer.route_permute(logits[b])
         layer.expert_ffn(Wsets[i % rot], xs[b], wl.T, variant=args.variant)
-        if ev is not None:
-            ev[1].record(stream)
         if Ws is not None:
             layer.shared_ffn(Ws, xs[b], wl.T, variant=args.variant)
         layer.combine(wl.T, Ws is not None)
+
+    # per-batch routing state, so the FFN launches can be replayed on their own
+    perm = []
+    for b in range(nb):
+        layer.route_permute(logits[b])
+        perm.append((layer.counts.clone(), layer.offsets.clone(), layer.sorted_idx.clone()))
+
+    def ffn_only(i):
+        b = i % nb
+        c, o, sidx = perm[b]
+        moe.moe_expert_ffn(Wsets[i % rot], None, xs[b], wl.T, wl.k, c, o, sidx, layer.y_perm,
+                           layer.ffn_ws, args.variant)
 
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(steps):
-        step(warmup + i, evs[i])
-    end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    def timed(fn, first):
+        """Run fn(first .. first+steps-1) once as a captured graph (or eagerly) and return ms."""
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if use_graph:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(steps):
+                    fn(first + i)
+            g.replay()  # untimed warm replay (graph upload)
+            torch.cuda.synchronize()
+            start.record()
+            g.replay()
+            end.record()
+        else:
+            start.record()
+            for i in range(steps):
+                fn(first + i)
+            end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end)
+
+    total_ms = timed(step, warmup)
+    ffn_ms = timed(ffn_only, warmup) / steps
     ms_per_step = total_ms / steps
     tokens_per_s = wl.T * steps / (total_ms / 1e3)
 
@@ -148,7 +168,10 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": None}
-    roof.update({"kernel": "moe_expert_ffn", "ffn_ms": round(ffn_ms, 5),
+    roof.update({"kernel": "moe_expert_ffn (gate/up + down launches)",
+                 "ffn_ms": round(ffn_ms, 5),
+                 "timing": ("HIP events around one replay of a graph of the %d launches"
+                            % steps) if use_graph else "HIP events, eager",
                  "algorithmic_bytes_per_launch": int(ffn_bytes),
                  "algorithmic_flops_per_launch": int(ffn_flops),
                  "touched_experts_mean": round(t_mean, 2)})
@@ -174,7 +197,9 @@ def main():
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "I": wl.I, "k": wl.k,
                    "weights": wl.fmt, "shared_I": wl.shared_I, "global_batch": wl.T,
                    "weight_sets_rotated": rot, "batches_rotated": nb,
-                   "boundary": "route->permute->expert_ffn->combine on one stream, eager launches",
+                   "boundary": ("route->permute->expert_ffn->combine on one stream, "
+                                + ("one captured HIP graph of the K steps" if use_graph
+                                   else "eager launches")),
                    "parallelism": "none (1 GPU)", "setup_s": round(setup_s, 1)},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -121,6 +121,16 @@ int moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_
                 size_t ws_bytes, moe_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_route_permute — moe_route followed by moe_permute, same arguments and
+ * results as the two calls.  For decode-sized batches (T <= 64, T*k <= 256)
+ * both steps run in one workgroup (one launch); otherwise it issues the two
+ * calls' kernels.  ws as for moe_permute (unused on the one-launch path).    */
+int moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t k, int32_t renorm,
+                      int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* offsets,
+                      int32_t* sorted_idx, int32_t* inv_idx, void* ws, size_t ws_bytes,
+                      moe_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * moe_expert_ffn — per-expert SwiGLU FFN over the permuted rows.
  * For every expert e with rows p in [offsets[e], offsets[e+1]):
  *   x_p      = x[sorted_idx[p] / k]                       (bf16 row, H)

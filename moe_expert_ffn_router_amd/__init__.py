@@ -54,6 +54,8 @@ _SIGS = {
     "moe_route": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _p, _p, _p]),
     "moe_permute_workspace": (_sz, [_i32, _i32, _i32]),
     "moe_permute": (ctypes.c_int, [_p, _i32, _i32, _i32, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_route_permute": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p,
+                                         _sz, _p]),
     "moe_expert_ffn_workspace": (_sz, [ctypes.POINTER(Experts), _i32, _i32]),
     "moe_expert_ffn": (ctypes.c_int, [ctypes.POINTER(Experts), _p, _p, _i32, _i32, _p, _p, _p, _p,
                                       _i32, _p, _sz, _p]),
@@ -142,6 +144,16 @@ def moe_permute(topk_ids, T: int, k: int, E: int, counts, offsets, sorted_idx, i
                             _ptr(sorted_idx), _ptr(inv_idx), _ptr(ws),
                             ws.numel() * ws.element_size() if ws is not None else 0,
                             _stream(stream)), "moe_permute")
+
+
+def moe_route_permute(logits, k: int, topk_ids, topk_w, counts, offsets, sorted_idx, inv_idx, ws,
+                      renorm: bool = True, stream=None) -> None:
+    _dev_check(logits, topk_ids, topk_w, counts, offsets, sorted_idx, inv_idx, ws)
+    T, E = logits.shape
+    _check(_lib.moe_route_permute(_ptr(logits), T, E, k, int(renorm), _ptr(topk_ids), _ptr(topk_w),
+                                  _ptr(counts), _ptr(offsets), _ptr(sorted_idx), _ptr(inv_idx),
+                                  _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
+                                  _stream(stream)), "moe_route_permute")
 
 
 def moe_expert_ffn_workspace(W: Experts, T: int, k: int) -> int:

@@ -1,109 +1,283 @@
-// Per-expert SwiGLU FFN over the permuted rows: a grouped GEMM on the bf16
-// MFMA (V_MFMA_F32_16X16X32_BF16), one launch for gate/up (+ SiLU*mul
-// epilogue) and one for down.
+// Per-expert SwiGLU FFN over the permuted rows (grouped GEMM on the bf16 MFMA
+// V_MFMA_F32_16X16X32_BF16): one launch for gate/up with the SiLU*mul
+// epilogue, one for down.
 //
-// Work unit = (m-tile of one expert's rows, block of output columns).  The
-// m-tile list is built on the device from `counts` (no host sync), so the
-// whole call can be captured into a graph.
+// Work unit = (m-tile of one expert's rows, block of output columns).  Each
+// workgroup finds its (expert, first row) from `counts` itself (a wave-wide
+// prefix sum of per-expert tile counts), so no extra launch or host sync is
+// needed and the whole call can be captured into a graph.
 //
-// Operands.  A = activations, bf16 rows gathered by token (gate/up) or the
-// contiguous h rows (down), staged through LDS one 128-wide K chunk at a
-// time.  B = expert weights, read straight from HBM into registers in their
-// stored format and decoded there to bf16 (CDNA4 scaled FP4/FP8 -> bf16
-// conversions; every MXFP4 value, NVFP4 E2M1 x E4M3 product and E4M3 value
-// is exact in bf16).  FP8 block scales and NVFP4 tensor scales multiply fp32
-// partial sums.
+// Operands.  A = activations: bf16 rows gathered by token (gate/up) or the
+// contiguous h rows (down).  B = expert weights, read from HBM into registers
+// in their stored format and decoded there to bf16 (every MXFP4 value, NVFP4
+// E2M1 x E4M3 product and E4M3 value is exact in bf16); FP8 block scales and
+// NVFP4 tensor scales multiply fp32 partial sums.
 //
-// K mapping.  For a 128-wide chunk, lane group g = lane/16 owns the 32
+// K mapping.  For a 128-wide K chunk, lane group g = lane/16 owns the 32
 // consecutive K values [32g, 32g+32) of its row; MFMA step s consumes values
 // [32g+8s, 32g+8s+8).  A and B use the same mapping, so each output is the
-// full dot product regardless of the instruction's internal K order.
-#include "moe_internal.h"
+// full dot product whatever the instruction's internal K order.
+//
+// Two kernel families:
+//  * decode (few rows per expert): m-tile = 16 rows; the 4 waves of a
+//    workgroup split K (chunks w, w+4, ...), each wave issues the loads of
+//    up to 4 chunks before consuming any (16 KB in flight per wave), and the
+//    4 partial sums are added in wave order through LDS (deterministic).
+//    Bandwidth-bound: each touched expert's weights are read once.
+//  * prefill (many rows): m-tile = 64 rows staged in LDS, each wave owns
+//    16 x 4 output columns over the full K.
+#include "ffn_common.h"
 
 namespace moe {
 
-constexpr int KC = 128;          // K chunk
-constexpr int A_PITCH = KC + 8;  // LDS row pitch in bf16 (16-byte pad: no bank conflicts)
-
-struct FfnArgs {
-  int E, H, I, k, A;
-  const uint8_t* base;
-  int64_t stride;
-  const int* slot_of;
-  int64_t off_w13, off_w13s, off_w2, off_w2s, off_ts;
-  const uint16_t* x;
-  const int* counts;
-  const int* offsets;
-  const int* sorted_idx;
-  uint16_t* hbuf;
-  uint16_t* y_perm;
-  const int* tile_info;  // [0] = n_tiles, [1..] expert of tile, then m0 of tile
-  int max_tiles;
+// ---------------------------------------------------------------------------
+// tile lookup: the `tile`-th m-tile of BM rows, experts in ascending order
+// ---------------------------------------------------------------------------
+struct TileInfo {
+  int e, m0, rows, seg0;
 };
 
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// 32 consecutive K values [k0, k0+32) of weight row `row` -> 4 x bf16x8.
-// For FP8 also returns the row's 128x128 block scale in `bs`.
-template <int FMT>
-__device__ __forceinline__ void load_b(const uint8_t* __restrict__ w, const uint8_t* __restrict__ sc,
-                                       int row, int K, int k0, bf16x8 (&b)[4], float& bs) {
-  if constexpr (FMT == MOE_W_MXFP4) {
-    const uint4 q = *reinterpret_cast<const uint4*>(w + (((size_t)row * K + k0) >> 1));
-    const float s = e8m0_to_f32(sc[(size_t)row * (K / 32) + k0 / 32]);
-    b[0] = fp4x8_to_bf16(q.x, s); b[1] = fp4x8_to_bf16(q.y, s);
-    b[2] = fp4x8_to_bf16(q.z, s); b[3] = fp4x8_to_bf16(q.w, s);
-    bs = 1.0f;
-  } else if constexpr (FMT == MOE_W_NVFP4) {
-    const uint4 q = *reinterpret_cast<const uint4*>(w + (((size_t)row * K + k0) >> 1));
-    const uint32_t s2 = *reinterpret_cast<const uint16_t*>(sc + (size_t)row * (K / 16) + k0 / 16);
-    const float s0 = e4m3_to_f32(s2 & 0xffu), s1 = e4m3_to_f32(s2 >> 8);
-    b[0] = fp4x8_to_bf16_mul(q.x, s0); b[1] = fp4x8_to_bf16_mul(q.y, s0);
-    b[2] = fp4x8_to_bf16_mul(q.z, s1); b[3] = fp4x8_to_bf16_mul(q.w, s1);
-    bs = 1.0f;
-  } else if constexpr (FMT == MOE_W_FP8_B128) {
-    const uint4* p = reinterpret_cast<const uint4*>(w + (size_t)row * K + k0);
-    const uint4 q0 = p[0], q1 = p[1];
-    b[0] = fp8x8_to_bf16(q0.x, q0.y); b[1] = fp8x8_to_bf16(q0.z, q0.w);
-    b[2] = fp8x8_to_bf16(q1.x, q1.y); b[3] = fp8x8_to_bf16(q1.z, q1.w);
-    bs = reinterpret_cast<const float*>(sc)[(size_t)(row / 128) * (K / 128) + k0 / 128];
-  } else {
-    const uint4* p = reinterpret_cast<const uint4*>(w + ((size_t)row * K + k0) * 2);
+// Called by one whole wave; returns false (in every lane) if `tile` is past
+// the last tile.  E <= 1024: lane l owns experts [l*EPL, l*EPL + EPL).  The
+// counts and offsets of a lane's experts are loaded together (one round trip).
+template <int BM>
+__device__ __forceinline__ bool find_tile(const int* __restrict__ counts,
+                                          const int* __restrict__ offsets, int E, int tile,
+                                          int lane, TileInfo& ti) {
+  const int epl = (E + 63) >> 6;
+  const int e0 = lane * epl;
+  int c[16], o[16];
+  int tl = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 q = p[i];
-      b[i] = bits_to_bf16x8(q.x, q.y, q.z, q.w);
+  for (int i = 0; i < 16; ++i) {
+    const bool ok = i < epl && e0 + i < E;
+    c[i] = ok ? counts[e0 + i] : 0;
+    o[i] = ok ? offsets[e0 + i] : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) tl += (c[i] + BM - 1) / BM;
+  const int incl = wave_incl_scan(tl);
+  const int total = __builtin_amdgcn_readlane(incl, 63);
+  if (tile >= total) return false;
+  const int excl = incl - tl;
+  const uint64_t own = __ballot(excl <= tile && tile < incl);
+  const int ol = (int)__builtin_ctzll(own);
+  int e = 0, m0 = 0, cnt = 0, off = 0;
+  if (lane == ol) {
+    int t = tile - excl;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int n = (c[i] + BM - 1) / BM;
+      if (cnt == 0 && t < n) {
+        e = e0 + i;
+        m0 = t * BM;
+        cnt = c[i];
+        off = o[i];
+      }
+      t -= n;
     }
-    bs = 1.0f;
+  }
+  ti.e = __builtin_amdgcn_readlane(e, ol);
+  ti.m0 = __builtin_amdgcn_readlane(m0, ol);
+  ti.rows = min(BM, __builtin_amdgcn_readlane(cnt, ol) - ti.m0);
+  ti.seg0 = __builtin_amdgcn_readlane(off, ol) + ti.m0;
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// decode family (few rows per expert, bandwidth-bound)
+//   SPLIT = 4: the 4 waves of a workgroup share NSUB weight subtiles and split
+//              K (chunks w, w+4, ...); partial sums meet in LDS in wave order.
+//   SPLIT = 1: each wave owns NSUB subtiles over the whole K (no LDS).
+// Every wave looks its tile up itself and issues the weight loads of U chunks
+// before it needs the activation rows, so HBM requests start right away.
+// ---------------------------------------------------------------------------
+template <int FMT, bool GATED, int NSUB, int SPLIT, int U>
+__device__ __forceinline__ void ffn_decode_body(const FfnArgs& a) {
+  static_assert(!GATED || NSUB % 2 == 0, "gate/up subtiles come in pairs");
+  constexpr int WAVE_COLS = (GATED ? NSUB / 2 : NSUB) * 16;     // output columns per wave
+  constexpr int NCOL = SPLIT == 4 ? WAVE_COLS : 4 * WAVE_COLS;  // per workgroup
+  const int N_out = GATED ? a.I : a.H;
+  const int K = GATED ? a.H : a.I;
+  const int nnb = N_out / NCOL;
+  const int tile = blockIdx.x / nnb, nb = blockIdx.x - tile * nnb;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
+
+  TileInfo ti;
+  if (!find_tile<16>(a.counts, a.offsets, a.E, tile, lane, ti)) return;  // uniform per block
+  const uint8_t* rec = record_of(a, ti.e);
+  const uint8_t* w = rec + (GATED ? a.off_w13 : a.off_w2);
+  const uint8_t* sc = rec + (GATED ? a.off_w13s : a.off_w2s);
+
+  const int n0 = nb * NCOL + (SPLIT == 4 ? 0 : wave * WAVE_COLS);
+  int brow[NSUB];
+#pragma unroll
+  for (int j = 0; j < NSUB; ++j) {
+    if constexpr (GATED)
+      brow[j] = (j < NSUB / 2 ? n0 : a.I + n0) + (j % (NSUB / 2)) * 16 + l16;
+    else
+      brow[j] = n0 + j * 16 + l16;
+  }
+  const int nchunks = K / KC;
+  const int c_first = SPLIT == 4 ? wave : 0;
+  constexpr int CSTEP = SPLIT;  // chunk stride of one wave
+
+  f32x4 acc[NSUB];
+#pragma unroll
+  for (int j = 0; j < NSUB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // the row index is requested first: waits on it then leave the weight loads in flight
+  int tok = -1;
+  if (l16 < ti.rows) tok = GATED ? a.sorted_idx[ti.seg0 + l16] : ti.seg0 + l16;
+  const uint16_t* arow = nullptr;
+  bool have_row = false;
+  for (int c0 = c_first; c0 < nchunks; c0 += CSTEP * U) {
+    BRaw<FMT> raw[U][NSUB];
+    uint4 araw[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + CSTEP * u;
+      if (c < nchunks) {
+#pragma unroll
+        for (int j = 0; j < NSUB; ++j) load_b_raw<FMT>(w, sc, brow[j], K, c * KC + g * 32, raw[u][j]);
+      }
+    }
+    if (!have_row) {  // activation row of this lane, resolved after the weight loads are out
+      have_row = true;
+      if (tok >= 0)
+        arow = GATED ? a.x + (size_t)(tok / a.k) * a.H : a.hbuf + (size_t)tok * a.I;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + CSTEP * u;
+      if (c < nchunks) {
+        if (arow) {
+          const uint4* ap = reinterpret_cast<const uint4*>(arow + c * KC + g * 32);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) araw[u][s] = ap[s];
+        } else {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) araw[u][s] = uint4{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c0 + CSTEP * u < nchunks) {
+        bf16x8 av[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          av[s] = bits_to_bf16x8(araw[u][s].x, araw[u][s].y, araw[u][s].z, araw[u][s].w);
+#pragma unroll
+        for (int j = 0; j < NSUB; ++j) {
+          bf16x8 b[4];
+          decode_b<FMT>(raw[u][j], b);
+          if constexpr (FMT == MOE_W_FP8_B128) {
+            f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) t = mfma16(av[s], b[s], t);
+            const float bs = block_scale<FMT>(raw[u][j]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[j][r] = fmaf(bs, t[r], acc[j][r]);
+          } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) acc[j] = mfma16(av[s], b[s], acc[j]);
+          }
+        }
+      }
+    }
+  }
+
+  if constexpr (SPLIT == 4) {
+    __shared__ f32x4 red[4][NSUB][64];
+#pragma unroll
+    for (int j = 0; j < NSUB; ++j) red[wave][j][lane] = acc[j];
+    __syncthreads();
+    // wave q sums subtile(s) in wave order 0..3 (deterministic)
+    constexpr int NOUT = GATED ? NSUB / 2 : NSUB;
+    if (wave >= NOUT) return;
+#pragma unroll
+    for (int j = 0; j < NSUB; ++j) {
+      if (GATED ? (j % (NSUB / 2) == wave) : (j == wave)) {
+        f32x4 sum = red[0][j][lane];
+#pragma unroll
+        for (int q = 1; q < 4; ++q) {
+          const f32x4 v = red[q][j][lane];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sum[r] += v[r];
+        }
+        acc[j] = sum;
+      }
+    }
+  }
+
+  // lane holds column l16 of a subtile, rows 4g..4g+3 of the m-tile
+  const int subs_here = GATED ? NSUB / 2 : NSUB;
+#pragma unroll
+  for (int jo = 0; jo < subs_here; ++jo) {
+    if (SPLIT == 4 && jo != wave) continue;
+    if constexpr (GATED) {
+      float tsg = 1.0f, tsu = 1.0f;
+      if constexpr (FMT == MOE_W_NVFP4) {
+        const float* ts = reinterpret_cast<const float*>(rec + a.off_ts);
+        tsg = ts[0];
+        tsu = ts[1];
+      }
+      const f32x4 gs = acc[jo], us = acc[jo + NSUB / 2];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = g * 4 + r;
+        if (m < ti.rows) {
+          const float gv = gs[r] * tsg, uv = us[r] * tsu;
+          const float hv = gv / (1.0f + expf(-gv)) * uv;
+          a.hbuf[(size_t)(ti.seg0 + m) * a.I + n0 + jo * 16 + l16] = f32_to_bf16_rne(hv);
+        }
+      }
+    } else {
+      float tsd = 1.0f;
+      if constexpr (FMT == MOE_W_NVFP4) tsd = reinterpret_cast<const float*>(rec + a.off_ts)[2];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = g * 4 + r;
+        if (m < ti.rows)
+          a.y_perm[(size_t)(ti.seg0 + m) * a.H + n0 + jo * 16 + l16] =
+              f32_to_bf16_rne(acc[jo][r] * tsd);
+      }
+    }
   }
 }
 
-// Tile list: m-tiles of BM rows for every expert with rows, in expert order.
-__global__ __launch_bounds__(256) void build_tiles_kernel(const int* __restrict__ counts, int E,
-                                                          int BM, int max_tiles,
-                                                          int* __restrict__ info) {
-  __shared__ int pre[kMaxE];
-  __shared__ int wave_tot[4];
-  for (int e = threadIdx.x; e < E; e += 256) pre[e] = (counts[e] + BM - 1) / BM;
-  __syncthreads();
-  const int total = block_exclusive_scan_256(pre, E, wave_tot);
-  const int n = total < max_tiles ? total : max_tiles;
-  for (int t = threadIdx.x; t < n; t += 256) {
-    int lo = 0, hi = E;  // last e with pre[e] <= t
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (pre[mid] <= t) lo = mid; else hi = mid;
-    }
-    info[1 + t] = lo;
-    info[1 + max_tiles + t] = (t - pre[lo]) * BM;
-  }
-  if (threadIdx.x == 0) info[0] = n;
+#ifndef MOE_GU_NSUB
+#define MOE_GU_NSUB 4
+#define MOE_GU_SPLIT 4
+#define MOE_GU_U 2
+#endif
+#ifndef MOE_DN_NSUB
+#define MOE_DN_NSUB 2
+#define MOE_DN_SPLIT 1
+#define MOE_DN_U 4
+#endif
+// gate/up: 4 waves split K over NSUB/2 x 16 h-columns per workgroup
+constexpr int kGuNsub = MOE_GU_NSUB, kGuSplit = MOE_GU_SPLIT, kGuU = MOE_GU_U;
+// down: each wave owns NSUB x 16 output rows over the whole (short) K
+constexpr int kDnNsub = MOE_DN_NSUB, kDnSplit = MOE_DN_SPLIT, kDnU = MOE_DN_U;
+constexpr int kGuCols = (kGuSplit == 4 ? 1 : 4) * kGuNsub / 2 * 16;
+constexpr int kDnCols = (kDnSplit == 4 ? 1 : 4) * kDnNsub * 16;
+
+template <int FMT>
+__global__ __launch_bounds__(256) void ffn_gateup_decode_kernel(FfnArgs a) {
+  ffn_decode_body<FMT, true, kGuNsub, kGuSplit, kGuU>(a);
+}
+template <int FMT>
+__global__ __launch_bounds__(256) void ffn_down_decode_kernel(FfnArgs a) {
+  ffn_decode_body<FMT, false, kDnNsub, kDnSplit, kDnU>(a);
 }
 
+// ---------------------------------------------------------------------------
+// prefill family: 64-row m-tiles staged in LDS
+// ---------------------------------------------------------------------------
 template <int FMT, bool GATED, int MSUB, int NSUB>
-__global__ __launch_bounds__(256) void ffn_tile_kernel(FfnArgs a) {
+__device__ __forceinline__ void ffn_tile_body(const FfnArgs& a) {
   constexpr int BM = MSUB * 16;
   constexpr int NH = GATED ? NSUB / 2 : NSUB;  // output column subtiles per wave
   constexpr int NCOL_W = NH * 16;
@@ -112,20 +286,28 @@ __global__ __launch_bounds__(256) void ffn_tile_kernel(FfnArgs a) {
   const int K = GATED ? a.H : a.I;
   const int nnb = N_out / NCOL;
   const int tile = blockIdx.x / nnb, nb = blockIdx.x - tile * nnb;
-  if (tile >= a.tile_info[0]) return;
-  const int e = a.tile_info[1 + tile];
-  const int m0 = a.tile_info[1 + a.max_tiles + tile];
-  const int seg0 = a.offsets[e] + m0;
-  const int rows = min(BM, a.counts[e] - m0);
-  const int slot = a.slot_of ? a.slot_of[e] : e;
-  const uint8_t* rec = a.base + (size_t)slot * a.stride;
-  const uint8_t* w = rec + (GATED ? a.off_w13 : a.off_w2);
-  const uint8_t* sc = rec + (GATED ? a.off_w13s : a.off_w2s);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
 
   __shared__ __attribute__((aligned(16))) uint16_t As[BM * A_PITCH];
   __shared__ int src_row[BM];
+  __shared__ TileInfo s_ti;
+  __shared__ int s_valid;
+  if (wave == 0) {
+    TileInfo ti;
+    const bool ok = find_tile<BM>(a.counts, a.offsets, a.E, tile, lane, ti);
+    if (lane == 0) {
+      s_valid = ok;
+      if (ok) s_ti = ti;
+    }
+  }
+  __syncthreads();
+  if (!s_valid) return;
+  const TileInfo ti = s_ti;
+  const int seg0 = ti.seg0, rows = ti.rows;
+  const uint8_t* rec = record_of(a, ti.e);
+  const uint8_t* w = rec + (GATED ? a.off_w13 : a.off_w2);
+  const uint8_t* sc = rec + (GATED ? a.off_w13s : a.off_w2s);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
   for (int r = tid; r < BM; r += 256) {
     int v = -1;
     if (r < rows) v = GATED ? a.sorted_idx[seg0 + r] / a.k : seg0 + r;
@@ -156,11 +338,13 @@ __global__ __launch_bounds__(256) void ffn_tile_kernel(FfnArgs a) {
       if (sr >= 0) v = *reinterpret_cast<const uint4*>(Asrc + (size_t)sr * K + kc + c);
       *reinterpret_cast<uint4*>(&As[r * A_PITCH + c]) = v;
     }
-    bf16x8 b[NSUB][4];
-    float bs[NSUB];
+    BRaw<FMT> raw[NSUB];
 #pragma unroll
-    for (int j = 0; j < NSUB; ++j) load_b<FMT>(w, sc, brow[j], K, kc + g * 32, b[j], bs[j]);
+    for (int j = 0; j < NSUB; ++j) load_b_raw<FMT>(w, sc, brow[j], K, kc + g * 32, raw[j]);
     __syncthreads();
+    bf16x8 b[NSUB][4];
+#pragma unroll
+    for (int j = 0; j < NSUB; ++j) decode_b<FMT>(raw[j], b[j]);
     if constexpr (FMT == MOE_W_FP8_B128) {
 #pragma unroll
       for (int i = 0; i < MSUB; ++i) {
@@ -175,9 +359,11 @@ __global__ __launch_bounds__(256) void ffn_tile_kernel(FfnArgs a) {
           for (int j = 0; j < NSUB; ++j) t[j] = mfma16(av, b[j][s], t[j]);
         }
 #pragma unroll
-        for (int j = 0; j < NSUB; ++j)
+        for (int j = 0; j < NSUB; ++j) {
+          const float bs = block_scale<FMT>(raw[j]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(bs[j], t[j][r], acc[i][j][r]);
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(bs, t[j][r], acc[i][j][r]);
+        }
       }
     } else {
 #pragma unroll
@@ -194,7 +380,6 @@ __global__ __launch_bounds__(256) void ffn_tile_kernel(FfnArgs a) {
     __syncthreads();
   }
 
-  // epilogue: lane holds column l16 of each subtile, rows 4g..4g+3 of each m-subtile
   if constexpr (GATED) {
     float tsg = 1.0f, tsu = 1.0f;
     if constexpr (FMT == MOE_W_NVFP4) {
@@ -232,12 +417,21 @@ __global__ __launch_bounds__(256) void ffn_tile_kernel(FfnArgs a) {
   }
 }
 
-// Decode one expert record to fp32 with the same decoders as the GEMM.
+constexpr int kPreMSUB = 4;  // 64-row m-tiles
+template <int FMT>
+__global__ __launch_bounds__(256) void ffn_gateup_tile_kernel(FfnArgs a) {
+  ffn_tile_body<FMT, true, kPreMSUB, 4>(a);
+}
+template <int FMT>
+__global__ __launch_bounds__(256) void ffn_down_tile_kernel(FfnArgs a) {
+  ffn_tile_body<FMT, false, kPreMSUB, 2>(a);
+}
+
+// Decode one expert record to fp32 with the same decoders as the GEMMs.
 template <int FMT>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ rec, FfnArgs a,
                                                       float* __restrict__ w13,
                                                       float* __restrict__ w2) {
-  // one thread = 32 consecutive K values of one row; rows of w13 then w2
   const int rows13 = 2 * a.I, K13 = a.H, K2 = a.I;
   const long n13 = (long)rows13 * (K13 / 32), n2 = (long)a.H * (K2 / 32);
   for (long u = blockIdx.x * 256L + threadIdx.x; u < n13 + n2; u += (long)gridDim.x * 256) {
@@ -245,11 +439,12 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
     const long v = first ? u : u - n13;
     const int K = first ? K13 : K2;
     const int row = (int)(v / (K / 32)), k0 = (int)(v % (K / 32)) * 32;
-    const uint8_t* w = rec + (first ? a.off_w13 : a.off_w2);
-    const uint8_t* sc = rec + (first ? a.off_w13s : a.off_w2s);
+    BRaw<FMT> raw;
+    load_b_raw<FMT>(rec + (first ? a.off_w13 : a.off_w2), rec + (first ? a.off_w13s : a.off_w2s),
+                    row, K, k0, raw);
     bf16x8 b[4];
-    float bs;
-    load_b<FMT>(w, sc, row, K, k0, b, bs);
+    decode_b<FMT>(raw, b);
+    const float bs = block_scale<FMT>(raw);
     float ts = 1.0f;
     if constexpr (FMT == MOE_W_NVFP4) {
       const float* t = reinterpret_cast<const float*>(rec + a.off_ts);
@@ -290,25 +485,16 @@ static void fill_args(FfnArgs& a, const moe_experts* W, const Layout& L) {
   a.off_ts = L.ts < 0 ? 0 : L.ts;
 }
 
-constexpr int kBMSmall = 16, kBMLarge = 64;
-
-template <int FMT, int MSUB>
-static void launch_ffn(const FfnArgs& a, hipStream_t s) {
-  constexpr int BM = MSUB * 16;
-  const int n_gu = (a.I / 128) * a.max_tiles;  // gate/up: 4 waves x 2 h-subtiles = 128 columns
-  const int n_dn = (a.H / 128) * a.max_tiles;  // down: 4 waves x 2 subtiles = 128 columns
-  build_tiles_kernel<<<1, 256, 0, s>>>(a.counts, a.E, BM, a.max_tiles, const_cast<int*>(a.tile_info));
-  ffn_tile_kernel<FMT, true, MSUB, 4><<<n_gu, 256, 0, s>>>(a);
-  ffn_tile_kernel<FMT, false, MSUB, 2><<<n_dn, 256, 0, s>>>(a);
-}
-
-template <int MSUB>
-static void launch_fmt(int fmt, const FfnArgs& a, hipStream_t s) {
-  switch (fmt) {
-    case MOE_W_BF16: launch_ffn<MOE_W_BF16, MSUB>(a, s); break;
-    case MOE_W_MXFP4: launch_ffn<MOE_W_MXFP4, MSUB>(a, s); break;
-    case MOE_W_NVFP4: launch_ffn<MOE_W_NVFP4, MSUB>(a, s); break;
-    default: launch_ffn<MOE_W_FP8_B128, MSUB>(a, s); break;
+template <int FMT>
+static void launch_ffn(const FfnArgs& a, bool decode, hipStream_t s) {
+  if (decode) {
+    const int64_t mt = max_tiles_for(a.A, a.E, 16);
+    ffn_gateup_decode_kernel<FMT><<<(unsigned)(mt * (a.I / kGuCols)), 256, 0, s>>>(a);
+    ffn_down_decode_kernel<FMT><<<(unsigned)(mt * (a.H / kDnCols)), 256, 0, s>>>(a);
+  } else {
+    const int64_t mt = max_tiles_for(a.A, a.E, kPreMSUB * 16);
+    ffn_gateup_tile_kernel<FMT><<<(unsigned)(mt * (a.I / 128)), 256, 0, s>>>(a);
+    ffn_down_tile_kernel<FMT><<<(unsigned)(mt * (a.H / 128)), 256, 0, s>>>(a);
   }
 }
 
@@ -320,9 +506,7 @@ static size_t ws_h_bytes(int64_t A, int I) { return (size_t)((A * I * 2 + 255) /
 
 extern "C" size_t moe_expert_ffn_workspace(const moe_experts* W, int32_t T, int32_t k) {
   if (!W || T < 0 || k < 1 || W->E < 1) return 0;
-  const int64_t A = (int64_t)T * k;
-  const int64_t mt = max_tiles_for(A, W->E, kBMSmall);
-  return ws_h_bytes(A, W->I) + (size_t)((4 * (1 + 2 * mt) + 255) / 256 * 256);
+  return ws_h_bytes((int64_t)T * k, W->I) + 256;
 }
 
 extern "C" int moe_expert_ffn(const moe_experts* W, const int32_t* slot_of_expert,
@@ -348,8 +532,9 @@ extern "C" int moe_expert_ffn(const moe_experts* W, const int32_t* slot_of_exper
   if (ws_bytes < need)
     return set_error(MOE_ERR_WORKSPACE, "moe_expert_ffn: workspace %zu < %zu bytes", ws_bytes, need);
 
-  const bool small = variant == 1 || (variant == 0 && A <= 2 * (int64_t)W->E);
-  const int BM = small ? kBMSmall : kBMLarge;
+  // few rows per expert -> bandwidth-bound split-K kernels
+  const bool decode = (variant == 1 || (variant == 0 && A <= 2 * (int64_t)W->E)) &&
+                      W->I % kGuCols == 0 && W->H % kDnCols == 0;
   FfnArgs a;
   fill_args(a, W, L);
   a.k = k;
@@ -361,11 +546,13 @@ extern "C" int moe_expert_ffn(const moe_experts* W, const int32_t* slot_of_exper
   a.sorted_idx = sorted_idx;
   a.hbuf = static_cast<uint16_t*>(ws);
   a.y_perm = y_perm;
-  a.tile_info = reinterpret_cast<const int*>(static_cast<uint8_t*>(ws) + ws_h_bytes(A, W->I));
-  a.max_tiles = (int)max_tiles_for(A, W->E, BM);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (small) launch_fmt<1>(W->fmt, a, s);
-  else launch_fmt<4>(W->fmt, a, s);
+  switch (W->fmt) {
+    case MOE_W_BF16: launch_ffn<MOE_W_BF16>(a, decode, s); break;
+    case MOE_W_MXFP4: launch_ffn<MOE_W_MXFP4>(a, decode, s); break;
+    case MOE_W_NVFP4: launch_ffn<MOE_W_NVFP4>(a, decode, s); break;
+    default: launch_ffn<MOE_W_FP8_B128>(a, decode, s); break;
+  }
   return check_launch("moe_expert_ffn");
 }
 

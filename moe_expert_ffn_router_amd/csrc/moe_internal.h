@@ -124,6 +124,54 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
 }
 
 
+// ---------------------------------------------------------------------------
+// wave64 primitives on DPP lane moves (no LDS round trip).  gfx9 DPP controls:
+// quad_perm, row_shr:n (0x110+n), row_mirror, row_half_mirror, row_bcast15,
+// row_bcast31.  Results that end in lane 63 are broadcast with readlane.
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROW_MASK = 0xF, bool BOUND_ZERO = false>
+__device__ __forceinline__ int dpp_i32(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, BOUND_ZERO);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  int v = (int)x;
+  auto mx = [](int a, int b) { return (int)((uint32_t)a > (uint32_t)b ? (uint32_t)a : (uint32_t)b); };
+  v = mx(v, dpp_i32<0xB1>(v, v));         // quad_perm [1,0,3,2]
+  v = mx(v, dpp_i32<0x4E>(v, v));         // quad_perm [2,3,0,1]
+  v = mx(v, dpp_i32<0x141>(v, v));        // row_half_mirror
+  v = mx(v, dpp_i32<0x140>(v, v));        // row_mirror
+  v = mx(v, dpp_i32<0x142, 0xA>(v, v));   // row_bcast15 into rows 1, 3
+  v = mx(v, dpp_i32<0x143, 0xC>(v, v));   // row_bcast31 into rows 2, 3
+  return (uint32_t)__builtin_amdgcn_readlane(v, 63);
+}
+
+// Sum over the wave in a fixed order (identical result in every lane).
+__device__ __forceinline__ float wave_sum_f32(float x) {
+  int v = __float_as_int(x);
+  auto add = [](int a, int b) { return __float_as_int(__int_as_float(a) + __int_as_float(b)); };
+  v = add(v, dpp_i32<0xB1>(v, v));
+  v = add(v, dpp_i32<0x4E>(v, v));
+  v = add(v, dpp_i32<0x141>(v, v));
+  v = add(v, dpp_i32<0x140>(v, v));
+  v = add(v, dpp_i32<0x142, 0xA>(0, v));
+  v = add(v, dpp_i32<0x143, 0xC>(0, v));
+  return __int_as_float(__builtin_amdgcn_readlane(v, 63));
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp_i32<0x111, 0xF, true>(0, v);   // row_shr:1
+  v += dpp_i32<0x112, 0xF, true>(0, v);   // row_shr:2
+  v += dpp_i32<0x114, 0xF, true>(0, v);   // row_shr:4
+  v += dpp_i32<0x118, 0xF, true>(0, v);   // row_shr:8
+  v += dpp_i32<0x142, 0xA>(0, v);         // row_bcast15
+  v += dpp_i32<0x143, 0xC>(0, v);         // row_bcast31
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
 // Exclusive scan over n <= 1024 ints held in LDS `v` (in place); returns the
 // total.  Called by all 256 threads of a workgroup, 4 consecutive entries each.
 __device__ __forceinline__ int block_exclusive_scan_256(int* v, int E, int* wave_tot) {

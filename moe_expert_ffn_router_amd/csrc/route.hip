@@ -1,40 +1,18 @@
 // Router: top-k experts per token with renormalised softmax weights.
 //
 // One wavefront per token.  Lane l holds logits l, l+64, ... of its token as
-// 64-bit keys (order-preserving map of the fp32 value in the high half, the
-// complement of the expert index in the low half), so a single unsigned
-// max picks the largest logit and, among equal logits, the lowest index.
-// Each of the k rounds is a lane-local max plus a 6-step butterfly; the
-// winner's key is cleared in its owner lane.  Lane j < k keeps round j's
-// winner and finally computes exp(l_j - l_0) / sum.
-#include "moe_internal.h"
+// order-preserving 32-bit keys (-0.0 mapped to +0.0).  Each of the k rounds
+// takes the lane-local maximum, a DPP wave maximum, and then the lowest expert
+// index holding that key (ballot over the lane's slots in index order: index
+// e = lane + 64*slot, so the first slot with a hit and its lowest lane give
+// the lowest index).  The owner clears the winner; lane j < k keeps round j's
+// winner and finally computes exp(l_j - l_0) / sum over the k selected.
+//
+// Decode-sized batches (T <= 64, T*k <= 256) also have a fused kernel that
+// routes and permutes in one workgroup (one launch instead of two).
+#include "route_common.h"
 
 namespace moe {
-
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;  // -0.0 ranks equal to +0.0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ float key_value(uint32_t key) {
-  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
-}
-
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    unsigned long long o = __shfl_xor(v, m, 64);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
-}
 
 template <int VPL>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E,
@@ -43,76 +21,145 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const float* row = logits + (size_t)t * E;
-
-  unsigned long long key[VPL];
-  float val[VPL];
-#pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    const int e = lane + 64 * i;
-    val[i] = (e < E) ? row[e] : 0.0f;
-    key[i] = (e < E) ? (((unsigned long long)order_key(val[i]) << 32) | (uint32_t)(~(uint32_t)e))
-                     : 0ull;
+  int id;
+  float w;
+  route_token<VPL>(logits + (size_t)t * E, E, k, renorm, lane, id, w);
+  if (lane < k) {
+    ids[(size_t)t * k + lane] = id;
+    wts[(size_t)t * k + lane] = w;
   }
+}
 
-  int my_id = 0;
-  float my_val = 0.0f;
-  for (int r = 0; r < k; ++r) {
-    unsigned long long best = key[0];
+// Exclusive scan over n <= 1024 ints in LDS with 1024 threads (one each).
+__device__ __forceinline__ int block_exclusive_scan_1024(int* v, int n, int* wave_tot) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int x = tid < n ? v[tid] : 0;
+  const int incl = wave_incl_scan(x);
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int base = 0, total = 0;
 #pragma unroll
-    for (int i = 1; i < VPL; ++i) best = key[i] > best ? key[i] : best;
-    const unsigned long long g = wave_max_u64(best);
-#pragma unroll
-    for (int i = 0; i < VPL; ++i)
-      if (key[i] == g) key[i] = 0ull;
-    if (lane == r) {
-      my_id = (int)(~(uint32_t)g);
-      my_val = key_value((uint32_t)(g >> 32));
+  for (int w = 0; w < 16; ++w) {
+    const int t = wave_tot[w];
+    base += (w < wave) ? t : 0;
+    total += t;
+  }
+  if (tid < n) v[tid] = base + incl - x;
+  __syncthreads();
+  return total;
+}
+
+constexpr int kSmallA = 256;
+constexpr int kSmallT = 64;
+
+// Route + permute for T <= 64, T*k <= 256 in one workgroup of 16 waves.  The
+// stable rank of assignment a among equal experts is counted directly over
+// the earlier assignments (at most 255 LDS reads, broadcast to the wave).
+template <int VPL>
+__global__ __launch_bounds__(1024) void route_permute_small_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int renorm, int* __restrict__ ids,
+    float* __restrict__ wts, int* __restrict__ counts, int* __restrict__ offsets,
+    int* __restrict__ sorted_idx, int* __restrict__ inv_idx) {
+  __shared__ int sid[kSmallA];
+  __shared__ int hist[kMaxE];
+  __shared__ int wave_tot[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int A = T * k;
+  if (tid < E) hist[tid] = 0;
+  for (int t = wave; t < T; t += 16) {
+    int id;
+    float w;
+    route_token<VPL>(logits + (size_t)t * E, E, k, renorm, lane, id, w);
+    if (lane < k) {
+      ids[t * k + lane] = id;
+      wts[t * k + lane] = w;
+      sid[t * k + lane] = id;
     }
   }
+  __syncthreads();
+  int e = 0, rank = 0;
+  if (tid < A) {
+    e = sid[tid];
+    for (int q = 0; q < tid; ++q) rank += (sid[q] == e);
+    atomicAdd(&hist[e], 1);  // integer count: order-independent
+  }
+  __syncthreads();
+  if (tid < E) counts[tid] = hist[tid];
+  const int total = block_exclusive_scan_1024(hist, E, wave_tot);
+  if (tid < E) offsets[tid] = hist[tid];
+  if (tid == 0) offsets[E] = total;
+  if (tid < A) {
+    const int p = hist[e] + rank;
+    sorted_idx[p] = tid;
+    inv_idx[tid] = p;
+  }
+}
 
-  const float v0 = __shfl(my_val, 0, 64);
-  float z = (lane < k) ? expf(my_val - v0) : 0.0f;
-  float denom;
-  if (renorm) {
-    denom = wave_sum_f32(z);
-  } else {
-    float s = 0.0f;
-#pragma unroll
-    for (int i = 0; i < VPL; ++i)
-      if (lane + 64 * i < E) s += expf(val[i] - v0);
-    denom = wave_sum_f32(s);
+static int route_launch(const float* logits, int T, int E, int k, int renorm, int* ids, float* w,
+                        hipStream_t s) {
+  const dim3 grid((T + 3) / 4), block(256);
+  switch (vpl_of(E)) {
+    case 1: route_kernel<1><<<grid, block, 0, s>>>(logits, T, E, k, renorm, ids, w); break;
+    case 2: route_kernel<2><<<grid, block, 0, s>>>(logits, T, E, k, renorm, ids, w); break;
+    case 4: route_kernel<4><<<grid, block, 0, s>>>(logits, T, E, k, renorm, ids, w); break;
+    case 8: route_kernel<8><<<grid, block, 0, s>>>(logits, T, E, k, renorm, ids, w); break;
+    default: route_kernel<16><<<grid, block, 0, s>>>(logits, T, E, k, renorm, ids, w); break;
   }
-  if (lane < k) {
-    ids[(size_t)t * k + lane] = my_id;
-    wts[(size_t)t * k + lane] = z / denom;
-  }
+  return check_launch("moe_route");
+}
+
+static int check_route_args(const char* who, const float* logits, int T, int E, int k,
+                            const int* ids, const float* w) {
+  if (T < 0 || E < 1 || E > kMaxE || k < 1 || k > E || k > kMaxK)
+    return set_error(MOE_ERR_INVALID_ARG, "%s: need T>=0, 1<=E<=%d, 1<=k<=min(E,%d) "
+                     "(T=%d E=%d k=%d)", who, kMaxE, kMaxK, T, E, k);
+  if (T == 0) return MOE_OK;
+  if (!logits || !ids || !w) return set_error(MOE_ERR_INVALID_ARG, "%s: null pointer", who);
+  if (!aligned16(logits) || !aligned16(ids) || !aligned16(w))
+    return set_error(MOE_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", who);
+  return MOE_OK;
 }
 
 }  // namespace moe
 
+using namespace moe;
+
 extern "C" int moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t renorm,
                          int32_t* topk_ids, float* topk_w, moe_stream_t stream) {
-  using namespace moe;
-  if (T < 0 || E < 1 || E > kMaxE || k < 1 || k > E || k > kMaxK)
-    return set_error(MOE_ERR_INVALID_ARG, "moe_route: need T>=0, 1<=E<=%d, 1<=k<=min(E,%d) "
-                     "(T=%d E=%d k=%d)", kMaxE, kMaxK, T, E, k);
-  if (T == 0) return MOE_OK;
-  if (!logits || !topk_ids || !topk_w)
-    return set_error(MOE_ERR_INVALID_ARG, "moe_route: null pointer");
-  if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w))
-    return set_error(MOE_ERR_INVALID_ARG, "moe_route: pointers must be 16-byte aligned");
+  int st = check_route_args("moe_route", logits, T, E, k, topk_ids, topk_w);
+  if (st || T == 0) return st;
+  return route_launch(logits, T, E, k, renorm, topk_ids, topk_w,
+                      reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t k,
+                                 int32_t renorm, int32_t* topk_ids, float* topk_w,
+                                 int32_t* counts, int32_t* offsets, int32_t* sorted_idx,
+                                 int32_t* inv_idx, void* ws, size_t ws_bytes,
+                                 moe_stream_t stream) {
+  int st = check_route_args("moe_route_permute", logits, T, E, k, topk_ids, topk_w);
+  if (st) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const dim3 grid((T + 3) / 4), block(256);
-  if (E <= 64)
-    route_kernel<1><<<grid, block, 0, s>>>(logits, T, E, k, renorm, topk_ids, topk_w);
-  else if (E <= 128)
-    route_kernel<2><<<grid, block, 0, s>>>(logits, T, E, k, renorm, topk_ids, topk_w);
-  else if (E <= 256)
-    route_kernel<4><<<grid, block, 0, s>>>(logits, T, E, k, renorm, topk_ids, topk_w);
-  else if (E <= 512)
-    route_kernel<8><<<grid, block, 0, s>>>(logits, T, E, k, renorm, topk_ids, topk_w);
-  else
-    route_kernel<16><<<grid, block, 0, s>>>(logits, T, E, k, renorm, topk_ids, topk_w);
-  return check_launch("moe_route");
+  if (T > 0 && T <= kSmallT && T * k <= kSmallA) {
+    if (!counts || !offsets || !sorted_idx || !inv_idx || !aligned16(counts) ||
+        !aligned16(offsets) || !aligned16(sorted_idx) || !aligned16(inv_idx))
+      return set_error(MOE_ERR_INVALID_ARG, "moe_route_permute: permutation outputs");
+    switch (vpl_of(E)) {
+#define MOE_RP(V)                                                                         \
+  case V:                                                                                 \
+    route_permute_small_kernel<V><<<1, 1024, 0, s>>>(logits, T, E, k, renorm, topk_ids,   \
+                                                     topk_w, counts, offsets, sorted_idx, \
+                                                     inv_idx);                            \
+    break;
+      MOE_RP(1) MOE_RP(2) MOE_RP(4) MOE_RP(8) MOE_RP(16)
+#undef MOE_RP
+    }
+    return check_launch("moe_route_permute");
+  }
+  if (T > 0) {
+    st = route_launch(logits, T, E, k, renorm, topk_ids, topk_w, s);
+    if (st) return st;
+  }
+  return moe_permute(topk_ids, T, k, E, counts, offsets, sorted_idx, inv_idx, ws, ws_bytes,
+                     stream);
 }

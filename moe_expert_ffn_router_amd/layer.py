@@ -12,7 +12,7 @@ from __future__ import annotations
 import torch
 
 from . import (Experts, experts, moe_combine, moe_expert_ffn, moe_expert_ffn_workspace,
-               moe_permute, moe_permute_workspace, moe_route)
+               moe_permute, moe_permute_workspace, moe_route, moe_route_permute)
 
 
 def _i32(n, dev):
@@ -80,6 +80,11 @@ class MoELayer:
         moe_combine(self.y_perm, self.inv_idx, self.w, T, self.k, self.H,
                     self.y_shared if with_shared else None, self.y, stream)
 
+    def route_permute(self, logits: torch.Tensor, stream=None):
+        moe_route_permute(logits, self.k, self.ids, self.w, self.counts, self.offsets,
+                          self.sorted_idx, self.inv_idx, self.perm_ws, self.renorm, stream)
+        return logits.shape[0]
+
     # -- whole layer ----------------------------------------------------------
     def weights(self, base) -> Experts:
         return experts(self.fmt, self.E, self.H, self.I, base, self.stride)
@@ -88,8 +93,7 @@ class MoELayer:
                 slot_of_expert=None, variant="auto", stream=None) -> torch.Tensor:
         T = logits.shape[0]
         assert T <= self.T_max and x.shape == (T, self.H)
-        self.route(logits, stream)
-        self.permute(T, stream)
+        self.route_permute(logits, stream)
         self.expert_ffn(W, x, T, slot_of_expert, variant, stream)
         if Ws is not None:
             self.shared_ffn(Ws, x, T, variant, stream)
@@ -101,8 +105,7 @@ class MoELayer:
                        stream=None) -> tuple[torch.Tensor, dict]:
         """Slot-table path: misses are filled from the pinned bank before the FFN."""
         T = logits.shape[0]
-        self.route(logits, stream)
-        self.permute(T, stream)
+        self.route_permute(logits, stream)
         counts_host = self.counts[:self.E].to("cpu")          # the one host sync of the step
         me, ms, n_miss, n_hit, _ = cache.expert_cache_lookup(layer, counts_host)
         cache.expert_cache_fill(layer, me, ms, side=side, compute=stream)

@@ -159,6 +159,28 @@ def test_permute_edge_shapes(T, E, k):
         assert np.array_equal(g, r)
 
 
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (8, 256, 8), (64, 8, 2), (64, 1024, 4), (32, 512, 8),
+                                   (17, 100, 16), (65, 256, 2), (100, 64, 8)])
+def test_route_permute_fused(T, E, k):
+    """moe_route_permute (one workgroup when T <= 64 and T*k <= 256) == oracle."""
+    flush(f"[route-permute] T={T} E={E} k={k}")
+    rng = np.random.default_rng(T * 7 + E)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    lg[:, ::3] = np.round(lg[:, ::3])                      # exact ties
+    lg_d = torch.from_numpy(lg).to(DEV)
+    A = T * k
+    ids, w = _i32(A), torch.empty(A, dtype=torch.float32, device=DEV)
+    counts, offsets, sidx, inv = _i32(E), _i32(E + 1), _i32(A), _i32(A)
+    ws = torch.empty(max(moe.moe_permute_workspace(T, k, E), 256), dtype=torch.uint8, device=DEV)
+    moe.moe_route_permute(lg_d, k, ids, w, counts, offsets, sidx, inv, ws)
+    torch.cuda.synchronize()
+    oid, ow = OR.route(lg, k)
+    assert np.array_equal(ids.cpu().numpy().reshape(T, k), oid)
+    assert np.max(np.abs(w.cpu().numpy().reshape(T, k) - ow)) <= 1e-5
+    for g, r in zip((counts[:E], offsets[:E + 1], sidx[:A], inv[:A]), OP.permute(oid, E)):
+        assert np.array_equal(g.cpu().numpy(), r)
+
+
 def test_permute_all_to_one_expert():
     ids = np.zeros((5000, 1), np.int32)
     got = _permute_gpu(ids, 3)
