@@ -170,6 +170,26 @@ int moe_combine(const uint16_t* y_perm, const int32_t* inv_idx, const float* top
                 moe_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_forward_decode — the whole layer for decode-sized batches in two
+ * launches (route + permute + gate/up; down + combine).  Same results as
+ * moe_route_permute + moe_expert_ffn (decode kernels, variant 1) +
+ * moe_combine, bit for bit, and it writes every output of those calls:
+ * topk_ids / topk_w [T][k], counts [E], offsets [E+1], sorted_idx / inv_idx
+ * [T*k], y [T][H] (y_shared [T][H] nullable, added with weight 1).  The
+ * pages' "graph-compatible execution" (README feature list; fork production
+ * configuration, --cuda-graph-max-bs) is served with two graph nodes per
+ * layer.  Shapes outside moe_forward_decode_supported(H, I, T, k) return
+ * MOE_ERR_UNSUPPORTED (use the separate calls).
+ *   ws: device, >= moe_forward_decode_workspace(W, T, k) bytes (holds h).   */
+int moe_forward_decode_supported(int32_t H, int32_t I, int32_t T, int32_t k);
+size_t moe_forward_decode_workspace(const moe_experts* W, int32_t T, int32_t k);
+int moe_forward_decode(const moe_experts* W, const int32_t* slot_of_expert, const float* logits,
+                       const uint16_t* x, int32_t T, int32_t k, int32_t renorm, int32_t* topk_ids,
+                       float* topk_w, int32_t* counts, int32_t* offsets, int32_t* sorted_idx,
+                       int32_t* inv_idx, const uint16_t* y_shared, uint16_t* y, void* ws,
+                       size_t ws_bytes, moe_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * moe_dequant_expert — decode one expert record to fp32 with the same device
  * decoders the FFN kernels use (for checking every code on the device).
  *   w13 device fp32 [2I][H] (out), w2 device fp32 [H][I] (out); the NVFP4

@@ -60,6 +60,10 @@ _SIGS = {
     "moe_expert_ffn": (ctypes.c_int, [ctypes.POINTER(Experts), _p, _p, _i32, _i32, _p, _p, _p, _p,
                                       _i32, _p, _sz, _p]),
     "moe_combine": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _p, _p, _p]),
+    "moe_forward_decode_supported": (ctypes.c_int, [_i32, _i32, _i32, _i32]),
+    "moe_forward_decode_workspace": (_sz, [ctypes.POINTER(Experts), _i32, _i32]),
+    "moe_forward_decode": (ctypes.c_int, [ctypes.POINTER(Experts), _p, _p, _p, _i32, _i32, _i32, _p,
+                                          _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_dequant_expert": (ctypes.c_int, [ctypes.POINTER(Experts), _i32, _p, _p, _p]),
     "moe_cache_create": (ctypes.c_int, [ctypes.POINTER(_p), _i32, _i32, _i32, _i64, _p, _p, _p]),
     "moe_cache_destroy": (None, [_p]),
@@ -174,6 +178,28 @@ def moe_combine(y_perm, inv_idx, topk_w, T: int, k: int, H: int, y_shared, y, st
     _dev_check(y_perm, inv_idx, topk_w, y_shared, y)
     _check(_lib.moe_combine(_ptr(y_perm), _ptr(inv_idx), _ptr(topk_w), T, k, H, _ptr(y_shared),
                             _ptr(y), _stream(stream)), "moe_combine")
+
+
+def moe_forward_decode_supported(H: int, I: int, T: int, k: int) -> bool:
+    return bool(_lib.moe_forward_decode_supported(H, I, T, k))
+
+
+def moe_forward_decode_workspace(W: Experts, T: int, k: int) -> int:
+    return int(_lib.moe_forward_decode_workspace(ctypes.byref(W), T, k))
+
+
+def moe_forward_decode(W: Experts, slot_of_expert, logits, x, k: int, topk_ids, topk_w, counts,
+                       offsets, sorted_idx, inv_idx, y_shared, y, ws, renorm: bool = True,
+                       stream=None) -> None:
+    """Whole layer for decode-sized batches in two launches."""
+    _dev_check(slot_of_expert, logits, x, topk_ids, topk_w, counts, offsets, sorted_idx, inv_idx,
+               y_shared, y, ws)
+    T = logits.shape[0]
+    _check(_lib.moe_forward_decode(ctypes.byref(W), _ptr(slot_of_expert), _ptr(logits), _ptr(x), T,
+                                   k, int(renorm), _ptr(topk_ids), _ptr(topk_w), _ptr(counts),
+                                   _ptr(offsets), _ptr(sorted_idx), _ptr(inv_idx), _ptr(y_shared),
+                                   _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream)), "moe_forward_decode")
 
 
 def moe_dequant_expert(W: Experts, expert: int, w13, w2, stream=None) -> None:

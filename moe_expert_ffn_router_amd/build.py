@@ -18,7 +18,8 @@ OUT = os.path.join(PKG, "libmoe_mi355x.so")
 OBJ = os.path.join(ROOT, "_build", "obj")
 ARCH = "gfx950"
 
-SOURCES = ["status.cpp", "cache.cpp", "route.hip", "permute.hip", "ffn.hip", "combine.hip"]
+SOURCES = ["status.cpp", "cache.cpp", "route.hip", "permute.hip", "ffn.hip", "combine.hip",
+           "decode.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

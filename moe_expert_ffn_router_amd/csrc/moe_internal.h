@@ -172,35 +172,60 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 
 __device__ __forceinline__ int lane_id() { return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
-// Exclusive scan over n <= 1024 ints held in LDS `v` (in place); returns the
-// total.  Called by all 256 threads of a workgroup, 4 consecutive entries each.
-__device__ __forceinline__ int block_exclusive_scan_256(int* v, int E, int* wave_tot) {
+// Exclusive scan over E <= kMaxE ints in LDS by all NT threads of the
+// workgroup (each owns kMaxE/NT consecutive entries); returns the total.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int* v, int E, int* wave_tot) {
+  static_assert(NT % 64 == 0 && kMaxE % NT == 0 && NT / 64 <= 16, "scan shape");
+  constexpr int PER = kMaxE / NT, NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int loc[4], sum = 0;
+  int loc[PER], sum = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = tid * 4 + i;
+  for (int i = 0; i < PER; ++i) {
+    const int e = tid * PER + i;
     loc[i] = (e < E) ? v[e] : 0;
     sum += loc[i];
   }
-  int incl = sum;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += o;
-  }
+  const int incl = wave_incl_scan(sum);
   if (lane == 63) wave_tot[wave] = incl;
   __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += wave_tot[w];
-  const int total = wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int t = wave_tot[w];
+    base += (w < wave) ? t : 0;
+    total += t;
+  }
   int run = base + incl - sum;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = tid * 4 + i;
+  for (int i = 0; i < PER; ++i) {
+    const int e = tid * PER + i;
     if (e < E) v[e] = run;
     run += loc[i];
   }
+  __syncthreads();
+  return total;
+}
+
+__device__ __forceinline__ int block_exclusive_scan_256(int* v, int E, int* wave_tot) {
+  return block_exclusive_scan<256>(v, E, wave_tot);
+}
+
+// Exclusive scan over n <= 1024 ints in LDS with 1024 threads (one each).
+__device__ __forceinline__ int block_exclusive_scan_1024(int* v, int n, int* wave_tot) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int x = tid < n ? v[tid] : 0;
+  const int incl = wave_incl_scan(x);
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const int t = wave_tot[w];
+    base += (w < wave) ? t : 0;
+    total += t;
+  }
+  if (tid < n) v[tid] = base + incl - x;
   __syncthreads();
   return total;
 }

@@ -30,25 +30,6 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   }
 }
 
-// Exclusive scan over n <= 1024 ints in LDS with 1024 threads (one each).
-__device__ __forceinline__ int block_exclusive_scan_1024(int* v, int n, int* wave_tot) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int x = tid < n ? v[tid] : 0;
-  const int incl = wave_incl_scan(x);
-  if (lane == 63) wave_tot[wave] = incl;
-  __syncthreads();
-  int base = 0, total = 0;
-#pragma unroll
-  for (int w = 0; w < 16; ++w) {
-    const int t = wave_tot[w];
-    base += (w < wave) ? t : 0;
-    total += t;
-  }
-  if (tid < n) v[tid] = base + incl - x;
-  __syncthreads();
-  return total;
-}
-
 constexpr int kSmallA = 256;
 constexpr int kSmallT = 64;
 

@@ -12,6 +12,7 @@ from __future__ import annotations
 import torch
 
 from . import (Experts, experts, moe_combine, moe_expert_ffn, moe_expert_ffn_workspace,
+               moe_forward_decode, moe_forward_decode_supported, moe_forward_decode_workspace,
                moe_permute, moe_permute_workspace, moe_route, moe_route_permute)
 
 
@@ -53,6 +54,11 @@ class MoELayer:
             self.s_ws = torch.empty(max(moe_expert_ffn_workspace(sp, T_max, 1), 256),
                                     dtype=torch.uint8, device=dev)
             self.y_shared = torch.empty((T_max, H), dtype=torch.bfloat16, device=dev)
+        # decode-sized batches: the two-launch whole-layer path
+        self.decode_ws = None
+        if moe_forward_decode_supported(H, I, T_max, k):
+            self.decode_ws = torch.empty(max(moe_forward_decode_workspace(probe, T_max, k), 256),
+                                         dtype=torch.uint8, device=dev)
 
     # -- individual steps ---------------------------------------------------
     def route(self, logits: torch.Tensor, stream=None):
@@ -89,10 +95,21 @@ class MoELayer:
     def weights(self, base) -> Experts:
         return experts(self.fmt, self.E, self.H, self.I, base, self.stride)
 
+    def forward_decode(self, logits: torch.Tensor, x: torch.Tensor, W: Experts,
+                       slot_of_expert=None, y_shared=None, stream=None) -> torch.Tensor:
+        """Whole layer in two launches (decode-sized batches)."""
+        T = logits.shape[0]
+        moe_forward_decode(W, slot_of_expert, logits, x, self.k, self.ids, self.w, self.counts,
+                           self.offsets, self.sorted_idx, self.inv_idx, y_shared, self.y,
+                           self.decode_ws, self.renorm, stream)
+        return self.y[:T]
+
     def forward(self, logits: torch.Tensor, x: torch.Tensor, W: Experts, Ws: Experts | None = None,
                 slot_of_expert=None, variant="auto", stream=None) -> torch.Tensor:
         T = logits.shape[0]
         assert T <= self.T_max and x.shape == (T, self.H)
+        if self.decode_ws is not None and Ws is None and variant == "auto":
+            return self.forward_decode(logits, x, W, slot_of_expert, None, stream)
         self.route_permute(logits, stream)
         self.expert_ffn(W, x, T, slot_of_expert, variant, stream)
         if Ws is not None:

@@ -69,8 +69,12 @@ def _run_cache_workload(wl: synth.Workload, S: int, n_batches: int, n_layers: in
         assert info["fills"] == r["fills"], (b, info["fills"][:5], r["fills"][:5])
         assert (info["hits"], info["misses"]) == (r["hits"], r["misses"])
         assert np.array_equal(table[L * wl.E:(L + 1) * wl.E].cpu().numpy(), ora.slot_table(L, wl.E))
-        # all-resident run of the same layer
-        y_r = layer.forward(lg, x, layer.weights(dev_sets[L])).clone()
+        # all-resident run through the same separate calls (same kernels, same bits)
+        W_r = layer.weights(dev_sets[L])
+        layer.route_permute(lg)
+        layer.expert_ffn(W_r, x, wl.T)
+        layer.combine(wl.T, False)
+        y_r = layer.y[:wl.T].clone()
         torch.cuda.synchronize()
         assert torch.equal(y_c.view(torch.int16), y_r.view(torch.int16)), f"batch {b}"
         flush(f"   batch {b} layer {L}: hits {r['hits']} misses {r['misses']}")
