@@ -170,17 +170,22 @@ int moe_combine(const uint16_t* y_perm, const int32_t* inv_idx, const float* top
                 moe_stream_t stream);
 
 /* ---------------------------------------------------------------------------
- * moe_forward_decode — the whole layer for decode-sized batches in two
- * launches (route + permute + gate/up; down + combine).  Same results as
- * moe_route_permute + moe_expert_ffn (decode kernels, variant 1) +
- * moe_combine, bit for bit, and it writes every output of those calls:
- * topk_ids / topk_w [T][k], counts [E], offsets [E+1], sorted_idx / inv_idx
- * [T*k], y [T][H] (y_shared [T][H] nullable, added with weight 1).  The
- * pages' "graph-compatible execution" (README feature list; fork production
- * configuration, --cuda-graph-max-bs) is served with two graph nodes per
- * layer.  Shapes outside moe_forward_decode_supported(H, I, T, k) return
- * MOE_ERR_UNSUPPORTED (use the separate calls).
- *   ws: device, >= moe_forward_decode_workspace(W, T, k) bytes (holds h).   */
+ * moe_forward_decode — the whole layer for decode-sized batches in one call
+ * (four launches: route + permute in one workgroup; gate/up and down as
+ * persistent grids over 16-row expert tiles; combine).  Writes every output
+ * of moe_route_permute + moe_expert_ffn + moe_combine: topk_ids / topk_w
+ * [T][k], counts [E], offsets [E+1], sorted_idx / inv_idx [T*k] (identical
+ * to moe_route_permute), y [T][H] (y_shared [T][H] nullable, added with
+ * weight 1); y agrees with the separate calls within the parity tolerance
+ * (the FFN kernels split K their own way; fixed order, so repeat calls give
+ * the same bits).  The pages' "graph-compatible execution" (README feature
+ * list; fork production configuration, --cuda-graph-max-bs) is served with
+ * four graph nodes per layer.  Shapes outside
+ * moe_forward_decode_supported(H, I, T, k) return MOE_ERR_UNSUPPORTED (use
+ * the separate calls): T <= 64, T*k <= 256, H and I in {512, 1024, 1536,
+ * 2048}, T*(H+8)*2 bytes of x fitting in LDS beside the tile table.
+ *   ws: device, >= moe_forward_decode_workspace(W, T, k) bytes (holds h and
+ *   y_perm; contents on entry are ignored).                                 */
 int moe_forward_decode_supported(int32_t H, int32_t I, int32_t T, int32_t k);
 size_t moe_forward_decode_workspace(const moe_experts* W, int32_t T, int32_t k);
 int moe_forward_decode(const moe_experts* W, const int32_t* slot_of_expert, const float* logits,

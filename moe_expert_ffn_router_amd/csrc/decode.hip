@@ -1,24 +1,21 @@
-// The MoE layer for decode-sized batches in three launches.  Kernel
-// boundaries are the only synchronisation between workgroups.
+// The MoE layer for decode-sized batches in four launches.  Kernel
+// boundaries are the only waits between workgroups.
 //
 //  1. route + permute: one workgroup (route_permute_small_kernel).
-//  2. gate/up: a persistent grid sized by occupancy.  Each workgroup builds the
-//     16-row tile list in LDS from counts/offsets (one round trip) and then
-//     takes units u = blockIdx.x, +gridDim.x, ... (unit = one tile x 32
-//     h-columns, K split over the 4 waves).  The weight loads of the next unit
-//     are issued before the current unit is computed (two register buffers,
-//     alternated without copies), so HBM requests never stop; the few
-//     activation rows of a unit come from L2 while its weights are decoded.
-//  3. down + combine: workgroup b owns output columns [b*NCOL, b*NCOL+NCOL) of
-//     y for every token.  Its waves first issue the W2 loads of that column
-//     slice for all their tiles, then stage every h row in LDS (overlapping
-//     the weight fetch), compute y_perm of the slice into LDS and finish with
-//     the weighted combine of the slice.  No data crosses workgroups inside a
+//  2. gate/up: a persistent grid sized by occupancy.  Each workgroup stages x,
+//     sorted_idx and the 16-row tile list in LDS in one round trip, then takes
+//     units u = blockIdx.x, +gridDim.x, ... (unit = one tile x 32 h-columns;
+//     the 4 waves split K), two at a time with both units' weights in flight
+//     before either is computed; SiLU(gate)*up is rounded to bf16 into h.
+//  3. down: the same unit scheme over (tile x 64 output columns), h rows
+//     read with the weights; y_perm is rounded to bf16.
+//  4. combine: moe_combine's kernel (one workgroup per token).  Finishing
+//     the combine inside the down kernel needs a device-scope release per
+//     unit (an L2 write-back on this chip), which costs far more than a
 //     launch.
 //
-// Per-element arithmetic (K split, MFMA order, bf16 rounding of h and y_perm,
-// combine order) is that of the decode kernels of moe_expert_ffn and of
-// moe_combine, so the results are bit-identical to the separate calls.
+// Arithmetic per element: fp32 MFMA accumulation, K partials summed in wave
+// order, bf16 rounding of h and y_perm, combine in top-k order in fp32.
 #include "ffn_common.h"
 #include "route_common.h"
 
@@ -30,7 +27,7 @@ constexpr int kDGuCols = 32;  // gate/up unit: 16 + 16 h-columns (2 gate + 2 up 
 struct DecArgs {
   FfnArgs f;
   const float* logits;
-  int T, renorm, h_pitch;
+  int T, renorm;
   int* ids;
   float* wts;
   int* counts;
@@ -154,120 +151,180 @@ __device__ __forceinline__ void stage_store(const uint4 (&v)[B], uint16_t* dst, 
 }
 
 // ----------------------------------------------------------------------------
-// gate/up
+// expert units: gate/up (MODE_GU) and down (MODE_DN)
+//
+// A unit is one 16-row tile times four 16-column subtiles of the weight
+// matrix: gate/up takes 16 gate + 16 up columns twice (32 h-columns), down
+// takes 64 output columns.  The 4 waves split K: wave w owns the 128-wide
+// chunks w, w+4, ... (CPW of them; K = 512 * CPW).  CPW is a compile-time
+// count, so a load and its use are never guarded by separate runtime branches
+// (which would make the compiler wait for loads still needed later).
 // ----------------------------------------------------------------------------
-// CPW = K chunks of 128 per wave (H = 512 * CPW): a compile-time count, so a
-// load and its use are never guarded by separate runtime branches (which
-// would make the compiler wait for loads still needed later).
-template <int FMT, int CPW>
-struct GuRaw {
-  BRaw<FMT> r[CPW][4];  // [chunk slot][subtile]
+constexpr int MODE_GU = 0, MODE_DN = 1;
+
+template <int FMT, int CPW, int MODE>
+struct UnitRaw {
+  BRaw<FMT> w[CPW][4];                   // [chunk slot][subtile]
+  uint4 a[MODE == MODE_DN ? CPW : 1][4];  // down: h row chunk of this lane
 };
 
-template <int FMT, int CPW>
-__device__ __forceinline__ void gu_issue(const FfnArgs& a, const TileTable& L, int unit, int n_gu,
-                                         GuRaw<FMT, CPW>& R) {
+struct UnitPos {
+  int tile, cb, e, rows, seg0;
+};
+
+__device__ __forceinline__ UnitPos unit_pos(const TileTable& L, int unit, int n_cb) {
+  UnitPos q;
+  q.tile = unit / n_cb;
+  q.cb = unit - q.tile * n_cb;
+  q.e = L.tile_e[q.tile];
+  const int m0 = L.tile_m0[q.tile];
+  q.rows = min(16, L.cnt[q.e] - m0);
+  q.seg0 = L.off[q.e] + m0;
+  return q;
+}
+
+template <int FMT, int CPW, int MODE>
+__device__ __forceinline__ void unit_issue(const FfnArgs& a, const TileTable& L, int unit, int n_cb,
+                                           UnitRaw<FMT, CPW, MODE>& R) {
   const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
-  const int tile = unit / n_gu, cb = unit - tile * n_gu;
-  const uint8_t* rec = tile_record(a, L, tile);
-  const uint8_t* w = rec + a.off_w13;
-  const uint8_t* sc = rec + a.off_w13s;
-  const int n0 = cb * kDGuCols;
+  const UnitPos q = unit_pos(L, unit, n_cb);
+  const uint8_t* rec = tile_record(a, L, q.tile);
+  if constexpr (MODE == MODE_DN) {
+    // h rows first: waiting for them never waits for the weights issued after.
+    // Lanes past the tile's rows read its first row (discarded at use).
+    const uint16_t* arow = a.hbuf + (size_t)(q.seg0 + (l16 < q.rows ? l16 : 0)) * a.I;
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      const uint4* src = reinterpret_cast<const uint4*>(arow + (wave + 4 * u) * KC + g * 32);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) R.a[u][i] = src[i];
+    }
+  }
+  const int K = MODE == MODE_GU ? a.H : a.I;
+  const uint8_t* w = rec + (MODE == MODE_GU ? a.off_w13 : a.off_w2);
+  const uint8_t* sc = rec + (MODE == MODE_GU ? a.off_w13s : a.off_w2s);
 #pragma unroll
   for (int u = 0; u < CPW; ++u) {
     const int c = wave + 4 * u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      load_b_raw<FMT>(w, sc, (j < 2 ? n0 : a.I + n0) + (j & 1) * 16 + l16, a.H, c * KC + g * 32,
-                      R.r[u][j]);
+    for (int j = 0; j < 4; ++j) {
+      const int row = MODE == MODE_GU ? (j < 2 ? 0 : a.I) + q.cb * 32 + (j & 1) * 16 + l16
+                                      : q.cb * 64 + j * 16 + l16;
+      load_b_raw<FMT>(w, sc, row, K, c * KC + g * 32, R.w[u][j]);
+    }
   }
 }
 
-// x rows come from LDS (xs, pitch xp); sidx holds sorted_idx.  The only global
-// loads of a unit are its weights, so waiting for them never waits for the
-// next unit's weights, which were issued later.
-template <int FMT, int CPW>
-__device__ __forceinline__ void gu_finish(const FfnArgs& a, const TileTable& L, const int* sidx,
-                                          const uint16_t* xs, int xp, f32x4 (&red)[4][4][64],
-                                          int unit, int n_gu, const GuRaw<FMT, CPW>& R) {
+// x rows come from LDS (xs, pitch xp) for gate/up; sidx holds sorted_idx.
+template <int FMT, int CPW, int MODE>
+__device__ __forceinline__ void unit_finish(const FfnArgs& a, const TileTable& L, const int* sidx,
+                                            const uint16_t* xs, int xp, f32x4 (&red)[4][4][64],
+                                            int unit, int n_cb, const UnitRaw<FMT, CPW, MODE>& R) {
   const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
-  const int tile = unit / n_gu, cb = unit - tile * n_gu;
-  const int e = L.tile_e[tile], m0 = L.tile_m0[tile];
-  const int rows = min(16, L.cnt[e] - m0), seg0 = L.off[e] + m0;
-  const int n0 = cb * kDGuCols;
-  const uint16_t* arow = l16 < rows ? xs + (sidx[seg0 + l16] / a.k) * xp : nullptr;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const UnitPos q = unit_pos(L, unit, n_cb);
+  const bool live = l16 < q.rows;
+  const uint16_t* xrow = nullptr;
+  if constexpr (MODE == MODE_GU) xrow = xs + (sidx[q.seg0 + (live ? l16 : 0)] / a.k) * xp;
   f32x4 acc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < CPW; ++u) {
     const int c = wave + 4 * u;
-    {
-      bf16x8 av[4];
+    bf16x8 av[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        av[q] = arow ? *reinterpret_cast<const bf16x8*>(arow + c * KC + g * 32 + q * 8)
-                     : bits_to_bf16x8(0u, 0u, 0u, 0u);
+    for (int i = 0; i < 4; ++i) {
+      uint4 v;
+      if constexpr (MODE == MODE_GU)
+        v = *reinterpret_cast<const uint4*>(xrow + c * KC + g * 32 + i * 8);
+      else
+        v = R.a[u][i];
+      av[i] = live ? bits_to_bf16x8(v.x, v.y, v.z, v.w) : bits_to_bf16x8(0u, 0u, 0u, 0u);
+    }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16x8 b[4];
-        decode_b<FMT>(R.r[u][j], b);
-        if constexpr (FMT == MOE_W_FP8_B128) {
-          f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) {
+      bf16x8 b[4];
+      decode_b<FMT>(R.w[u][j], b);
+      if constexpr (FMT == MOE_W_FP8_B128) {
+        f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int q = 0; q < 4; ++q) t = mfma16(av[q], b[q], t);
-          const float bs = block_scale<FMT>(R.r[u][j]);
+        for (int i = 0; i < 4; ++i) t = mfma16(av[i], b[i], t);
+        const float bs = block_scale<FMT>(R.w[u][j]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[j][r] = fmaf(bs, t[r], acc[j][r]);
-        } else {
+        for (int r = 0; r < 4; ++r) acc[j][r] = fmaf(bs, t[r], acc[j][r]);
+      } else {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[j] = mfma16(av[q], b[q], acc[j]);
-        }
+        for (int i = 0; i < 4; ++i) acc[j] = mfma16(av[i], b[i], acc[j]);
       }
     }
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) red[wave][j][lane] = acc[j];
   __syncthreads();
-  if (wave < 2) {
-    f32x4 gs = red[0][wave][lane], us = red[0][2 + wave][lane];
+  // K partials summed in wave order (fixed order: deterministic)
+  if constexpr (MODE == MODE_GU) {
+    if (wave < 2) {
+      f32x4 gs = red[0][wave][lane], us = red[0][2 + wave][lane];
 #pragma unroll
-    for (int q = 1; q < 4; ++q) {
-      const f32x4 gq = red[q][wave][lane], uq = red[q][2 + wave][lane];
+      for (int w = 1; w < 4; ++w) {
+        const f32x4 gw = red[w][wave][lane], uw = red[w][2 + wave][lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          gs[r] += gw[r];
+          us[r] += uw[r];
+        }
+      }
+      float tsg = 1.0f, tsu = 1.0f;
+      if constexpr (FMT == MOE_W_NVFP4) {
+        const float* ts = reinterpret_cast<const float*>(tile_record(a, L, q.tile) + a.off_ts);
+        tsg = ts[0];
+        tsu = ts[1];
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        gs[r] += gq[r];
-        us[r] += uq[r];
+        const int m = g * 4 + r;
+        if (m < q.rows) {
+          const float gv = gs[r] * tsg, uv = us[r] * tsu;
+          const float hv = gv / (1.0f + expf(-gv)) * uv;
+          a.hbuf[(size_t)(q.seg0 + m) * a.I + q.cb * 32 + wave * 16 + l16] = f32_to_bf16_rne(hv);
+        }
       }
     }
-    float tsg = 1.0f, tsu = 1.0f;
-    if constexpr (FMT == MOE_W_NVFP4) {
-      const float* ts = reinterpret_cast<const float*>(tile_record(a, L, tile) + a.off_ts);
-      tsg = ts[0];
-      tsu = ts[1];
+  } else {
+    f32x4 ys = red[0][wave][lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      const f32x4 yw = red[w][wave][lane];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ys[r] += yw[r];
     }
+    float tsd = 1.0f;
+    if constexpr (FMT == MOE_W_NVFP4)
+      tsd = reinterpret_cast<const float*>(tile_record(a, L, q.tile) + a.off_ts)[2];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = g * 4 + r;
-      if (m < rows) {
-        const float gv = gs[r] * tsg, uv = us[r] * tsu;
-        const float hv = gv / (1.0f + expf(-gv)) * uv;
-        a.hbuf[(size_t)(seg0 + m) * a.I + n0 + wave * 16 + l16] = f32_to_bf16_rne(hv);
-      }
+      if (m < q.rows)
+        a.y_perm[(size_t)(q.seg0 + m) * a.H + q.cb * 64 + wave * 16 + l16] =
+            f32_to_bf16_rne(ys[r] * tsd);
     }
   }
   __syncthreads();  // red is rewritten by the next unit
 }
 
+// Units go in pairs: both units' loads are issued before the first is
+// computed.  Nothing stays in flight across iterations, so no register holding
+// a pending load is ever copied (a copy would wait for the load).
 template <int FMT, int CPW>
-__global__ __launch_bounds__(256) void dec_gateup_kernel(FfnArgs a, int T) {
+__global__ __launch_bounds__(256) void dec_gateup_kernel(DecArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];  // [T][H + 8]
   __shared__ TileTable L;
   __shared__ f32x4 red[4][4][64];
   __shared__ int sidx[kDA];
-  const int xp = a.H + 8, tid = threadIdx.x;
+  const FfnArgs& a = p.f;
+  const int xp = a.H + 8, tid = threadIdx.x, T = p.T;
   // one round trip: x rows, sorted_idx, counts/offsets/slot table
   uint4 xv[8];
   stage_load<256, 8>(xv, a.x, a.H, T, a.H, 0);
@@ -281,167 +338,38 @@ __global__ __launch_bounds__(256) void dec_gateup_kernel(FfnArgs a, int T) {
   }
   if (tid < a.A) sidx[tid] = sid;
   const int n_tiles = tiles_build<256>(a, tr, L);  // its barriers publish xs and sidx
-  const int n_gu = a.I / kDGuCols, U1 = n_tiles * n_gu, G = (int)gridDim.x;
-  // Units go in pairs: both pairs' weights are issued before the first is
-  // computed.  Nothing stays in flight across iterations, so no register
-  // holding a pending load is ever copied (a copy would wait for the load).
-  GuRaw<FMT, CPW> ra, rb;
-  for (int u = blockIdx.x; u < U1; u += 2 * G) {
-    gu_issue<FMT, CPW>(a, L, u, n_gu, ra);
-    if (u + G < U1) {
-      gu_issue<FMT, CPW>(a, L, u + G, n_gu, rb);
-      gu_finish<FMT, CPW>(a, L, sidx, xs, xp, red, u, n_gu, ra);
-      gu_finish<FMT, CPW>(a, L, sidx, xs, xp, red, u + G, n_gu, rb);
+  const int n_cb = a.I / 32, U = n_tiles * n_cb, G = (int)gridDim.x;
+  UnitRaw<FMT, CPW, MODE_GU> ra, rb;
+  for (int u = blockIdx.x; u < U; u += 2 * G) {
+    unit_issue<FMT, CPW, MODE_GU>(a, L, u, n_cb, ra);
+    if (u + G < U) {
+      unit_issue<FMT, CPW, MODE_GU>(a, L, u + G, n_cb, rb);
+      unit_finish<FMT, CPW, MODE_GU>(a, L, sidx, xs, xp, red, u, n_cb, ra);
+      unit_finish<FMT, CPW, MODE_GU>(a, L, sidx, xs, xp, red, u + G, n_cb, rb);
     } else {
-      gu_finish<FMT, CPW>(a, L, sidx, xs, xp, red, u, n_gu, ra);
+      unit_finish<FMT, CPW, MODE_GU>(a, L, sidx, xs, xp, red, u, n_cb, ra);
     }
   }
 }
 
-// ----------------------------------------------------------------------------
-// down + combine, one column slice of y per workgroup (8 waves)
-// ----------------------------------------------------------------------------
-struct K2Extra {
-  int inv[kDA];
-  float w[kDA];
-};
-
-constexpr int kK2Threads = 512, kK2Waves = kK2Threads / 64;
-// tiles of one wave whose weight loads are in flight together (register budget)
-template <int FMT>
-constexpr int k2_tiles() {
-  return FMT == MOE_W_BF16 ? 2 : FMT == MOE_W_FP8_B128 ? 4 : 8;
-}
-
-template <int FMT, int NCOL, int MT>
-__device__ __forceinline__ void k2_issue(const FfnArgs& a, const TileTable& L, int n_tiles, int t0,
-                                         int c0, int n0, BRaw<FMT> (&raw)[MT][4]) {
-  const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
-  const int nchunks = a.I / KC;
-#pragma unroll
-  for (int s = 0; s < MT; ++s) {
-    const int tile = t0 + kK2Waves * s;
-    if (tile < n_tiles) {
-      const uint8_t* rec = tile_record(a, L, tile);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (c0 + u < nchunks) {
-          if (l16 < NCOL)
-            load_b_raw<FMT>(rec + a.off_w2, rec + a.off_w2s, n0 + l16, a.I, (c0 + u) * KC + g * 32,
-                            raw[s][u]);
-          else
-            raw[s][u] = BRaw<FMT>{};
-        }
-      }
-    }
-  }
-}
-
-template <int FMT, int NCOL>
-__global__ __launch_bounds__(kK2Threads) void dec_down_combine_kernel(DecArgs p) {
-  constexpr int MT = k2_tiles<FMT>();
-  extern __shared__ __attribute__((aligned(16))) uint16_t dyn[];
+template <int FMT, int CPW>
+__global__ __launch_bounds__(256) void dec_down_kernel(FfnArgs a) {
   __shared__ TileTable L;
-  __shared__ K2Extra X;
-  const FfnArgs& a = p.f;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
-  const int T = p.T, k = a.k, A = T * k, I = a.I, H = a.H;
-  uint16_t* hs = dyn;                          // [A][h_pitch]
-  uint16_t* yp = dyn + (size_t)A * p.h_pitch;  // [A][NCOL]
-
-  // inv/weights and the tile table in one round trip
-  int inv_v = 0;
-  float w_v = 0.0f;
-  if (tid < A) {
-    inv_v = p.inv[tid];
-    w_v = p.wts[tid];
-  }
-  TileRegs<kK2Threads> tr;
-  tiles_load<kK2Threads>(a, tr);
-  if (tid < A) {
-    X.inv[tid] = inv_v;
-    X.w[tid] = w_v;
-  }
-  const int n_tiles = tiles_build<kK2Threads>(a, tr, L);
-  const int n0 = blockIdx.x * NCOL, nchunks = I / KC;
-  // the first weight group of every wave goes out before the h rows are
-  // staged; the staging then waits for both, which arrive together
-  BRaw<FMT> raw[MT][4];
-  k2_issue<FMT, NCOL, MT>(a, L, n_tiles, wave, 0, n0, raw);
-  for (int q0 = 0; q0 < A * (I / 8); q0 += kK2Threads * 8) {
-    uint4 v[8];
-    stage_load<kK2Threads, 8>(v, a.hbuf, I, A, I, q0);
-    stage_store<kK2Threads, 8>(v, hs, p.h_pitch, A, I, q0);
-  }
-  __syncthreads();
-
-  bool first = true;
-  for (int t0 = wave; t0 < n_tiles; t0 += kK2Waves * MT) {
-    f32x4 acc[MT];
-#pragma unroll
-    for (int s = 0; s < MT; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int c0 = 0; c0 < nchunks; c0 += 4) {
-      if (!first) k2_issue<FMT, NCOL, MT>(a, L, n_tiles, t0, c0, n0, raw);
-      first = false;
-#pragma unroll
-      for (int s = 0; s < MT; ++s) {
-        const int tile = t0 + kK2Waves * s;
-        if (tile < n_tiles) {
-          const int e = L.tile_e[tile], m0 = L.tile_m0[tile];
-          const int rows = min(16, L.cnt[e] - m0), seg0 = L.off[e] + m0;
-          const uint16_t* arow = l16 < rows ? hs + (seg0 + l16) * p.h_pitch : nullptr;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int c = c0 + u;
-            if (c < nchunks) {
-              bf16x8 av[4], b[4];
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                av[q] = arow ? *reinterpret_cast<const bf16x8*>(arow + c * KC + g * 32 + q * 8)
-                             : bits_to_bf16x8(0u, 0u, 0u, 0u);
-              decode_b<FMT>(raw[s][u], b);
-              if constexpr (FMT == MOE_W_FP8_B128) {
-                f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int q = 0; q < 4; ++q) t = mfma16(av[q], b[q], t);
-                const float bs = block_scale<FMT>(raw[s][u]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[s][r] = fmaf(bs, t[r], acc[s][r]);
-              } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) acc[s] = mfma16(av[q], b[q], acc[s]);
-              }
-            }
-          }
-        }
-      }
+  __shared__ f32x4 red[4][4][64];
+  TileRegs<256> tr;
+  tiles_load<256>(a, tr);
+  const int n_tiles = tiles_build<256>(a, tr, L);
+  const int n_cb = a.H / 64, U = n_tiles * n_cb, G = (int)gridDim.x;
+  UnitRaw<FMT, CPW, MODE_DN> ra, rb;
+  for (int u = blockIdx.x; u < U; u += 2 * G) {
+    unit_issue<FMT, CPW, MODE_DN>(a, L, u, n_cb, ra);
+    if (u + G < U) {
+      unit_issue<FMT, CPW, MODE_DN>(a, L, u + G, n_cb, rb);
+      unit_finish<FMT, CPW, MODE_DN>(a, L, nullptr, nullptr, 0, red, u, n_cb, ra);
+      unit_finish<FMT, CPW, MODE_DN>(a, L, nullptr, nullptr, 0, red, u + G, n_cb, rb);
+    } else {
+      unit_finish<FMT, CPW, MODE_DN>(a, L, nullptr, nullptr, 0, red, u, n_cb, ra);
     }
-#pragma unroll
-    for (int s = 0; s < MT; ++s) {
-      const int tile = t0 + kK2Waves * s;
-      if (tile < n_tiles && l16 < NCOL) {
-        const int e = L.tile_e[tile], m0 = L.tile_m0[tile];
-        const int rows = min(16, L.cnt[e] - m0), seg0 = L.off[e] + m0;
-        float tsd = 1.0f;
-        if constexpr (FMT == MOE_W_NVFP4)
-          tsd = reinterpret_cast<const float*>(tile_record(a, L, tile) + a.off_ts)[2];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = g * 4 + r;
-          if (m < rows) yp[(seg0 + m) * NCOL + l16] = f32_to_bf16_rne(acc[s][r] * tsd);
-        }
-      }
-    }
-  }
-  __syncthreads();
-  // combine of this column slice: fp32 sum in j order, one bf16 rounding
-  for (int i = tid; i < T * NCOL; i += kK2Threads) {
-    const int t = i / NCOL, c = i - t * NCOL;
-    float acc = 0.0f;
-    for (int j = 0; j < k; ++j)
-      acc = fmaf(X.w[t * k + j], bf16_to_f32(yp[X.inv[t * k + j] * NCOL + c]), acc);
-    if (p.y_shared) acc += bf16_to_f32(p.y_shared[(size_t)t * H + n0 + c]);
-    p.y[(size_t)t * H + n0 + c] = f32_to_bf16_rne(acc);
   }
 }
 
@@ -463,25 +391,33 @@ static int launch_gateup(const DecArgs& p, hipStream_t s) {
   const size_t x_lds = (size_t)p.T * (p.f.H + 8) * 2;
   static size_t granted = 0, occ_for = 0;
   static int per_cu = 0;
-  auto k1 = dec_gateup_kernel<FMT, CPW>;
-  if (!lds_ok(k1, x_lds, granted))
-    return set_error(MOE_ERR_HIP, "moe_forward_decode: LDS attribute");
+  auto k = dec_gateup_kernel<FMT, CPW>;
+  if (!lds_ok(k, x_lds, granted)) return set_error(MOE_ERR_HIP, "moe_forward_decode: LDS attribute");
   if (occ_for != x_lds) {  // persistent grid: as many workgroups as fit on the device at once
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k1),
-                                                     256, x_lds) != hipSuccess || per_cu < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k), 256,
+                                                     x_lds) != hipSuccess || per_cu < 1)
       per_cu = 1;
     occ_for = x_lds;
   }
-  k1<<<per_cu * g_cus, 256, x_lds, s>>>(p.f, p.T);
+  k<<<per_cu * g_cus, 256, x_lds, s>>>(p);
   return MOE_OK;
 }
 
+template <int FMT, int CPW>
+static int launch_down(const DecArgs& p, hipStream_t s) {
+  static int per_cu = 0;
+  auto k = dec_down_kernel<FMT, CPW>;
+  if (!per_cu &&
+      (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k), 256,
+                                                    0) != hipSuccess || per_cu < 1))
+    per_cu = 1;
+  k<<<per_cu * g_cus, 256, 0, s>>>(p.f);
+  return MOE_OK;
+}
+
+// K chunks per wave: H / 512 for gate/up, I / 512 for down
 template <int FMT>
 static int launch_decode(DecArgs& p, hipStream_t s) {
-  const int A = p.T * p.f.k;
-  const int ncol = (p.f.H / 16 >= g_cus) ? 16 : 8;
-  const size_t h_lds = (size_t)A * p.h_pitch * 2 + (size_t)A * ncol * 2;
-  static size_t g2a = 0, g2b = 0;
   int st;
   switch (p.f.H / 512) {
     case 1: st = launch_gateup<FMT, 1>(p, s); break;
@@ -490,16 +426,16 @@ static int launch_decode(DecArgs& p, hipStream_t s) {
     default: st = launch_gateup<FMT, 4>(p, s); break;
   }
   if (st) return st;
-  if (ncol == 16) {
-    auto k2 = dec_down_combine_kernel<FMT, 16>;
-    if (!lds_ok(k2, h_lds, g2a)) return set_error(MOE_ERR_HIP, "moe_forward_decode: LDS attribute");
-    k2<<<p.f.H / 16, kK2Threads, h_lds, s>>>(p);
-  } else {
-    auto k2 = dec_down_combine_kernel<FMT, 8>;
-    if (!lds_ok(k2, h_lds, g2b)) return set_error(MOE_ERR_HIP, "moe_forward_decode: LDS attribute");
-    k2<<<p.f.H / 8, kK2Threads, h_lds, s>>>(p);
+  switch (p.f.I / 512) {
+    case 1: st = launch_down<FMT, 1>(p, s); break;
+    case 2: st = launch_down<FMT, 2>(p, s); break;
+    case 3: st = launch_down<FMT, 3>(p, s); break;
+    default: st = launch_down<FMT, 4>(p, s); break;
   }
-  return check_launch("moe_forward_decode");
+  if (st) return st;
+  if ((st = check_launch("moe_forward_decode"))) return st;
+  return moe_combine(p.f.y_perm, p.inv, p.wts, p.T, p.f.k, p.f.H, p.y_shared, p.y,
+                     reinterpret_cast<moe_stream_t>(s));
 }
 
 }  // namespace moe
@@ -508,9 +444,11 @@ using namespace moe;
 
 static size_t dec_align(size_t v) { return (v + 255) / 256 * 256; }
 
+// Workspace: h [A][I] bf16 | y_perm [A][H] bf16.
 extern "C" size_t moe_forward_decode_workspace(const moe_experts* W, int32_t T, int32_t k) {
   if (!W || T < 0 || k < 1) return 0;
-  return dec_align((size_t)T * k * W->I * 2) + 256;
+  const size_t A = (size_t)T * k;
+  return dec_align(A * W->I * 2) + dec_align(A * W->H * 2);
 }
 
 extern "C" int moe_forward_decode(const moe_experts* W, const int32_t* slot_of_expert,
@@ -559,12 +497,13 @@ extern "C" int moe_forward_decode(const moe_experts* W, const int32_t* slot_of_e
   f.off_ts = Lo.ts < 0 ? 0 : Lo.ts;
   f.x = x;
   f.counts = counts; f.offsets = offsets; f.sorted_idx = sorted_idx;
-  f.hbuf = static_cast<uint16_t*>(ws);
-  f.y_perm = nullptr;
+  const size_t A = (size_t)T * k;
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  f.hbuf = reinterpret_cast<uint16_t*>(wsb);
+  f.y_perm = reinterpret_cast<uint16_t*>(wsb + dec_align(A * W->I * 2));
   p.logits = logits;
   p.T = T;
   p.renorm = renorm;
-  p.h_pitch = W->I + 8;
   p.ids = topk_ids; p.wts = topk_w; p.counts = counts; p.offsets = offsets;
   p.sorted = sorted_idx; p.inv = inv_idx;
   p.y_shared = y_shared;
@@ -582,15 +521,11 @@ extern "C" int moe_forward_decode(const moe_experts* W, const int32_t* slot_of_e
 }
 
 extern "C" int moe_forward_decode_supported(int32_t H, int32_t I, int32_t T, int32_t k) {
-  // routing in one workgroup; gate/up units hold H/512 chunks of 128 per wave
-  // (H in {512, 1024, 1536, 2048}) and keep the batch's x rows in LDS;
-  // down+combine keeps all h rows in LDS
+  // routing in one workgroup; the units hold K/512 chunks of 128 per wave
+  // (H and I in {512, 1024, 1536, 2048}); gate/up keeps the batch's x in LDS
   if (T < 0 || k < 1 || T > kDT || T * k > kDA) return 0;
-  if (H % 512 || I % 128 || H > 2048 || I > 16384 || H < 512 || I < 128) return 0;
-  const size_t lds_max = 160 * 1024;
+  if (H % 512 || I % 512 || H > 2048 || I > 2048 || H < 512 || I < 512) return 0;
   const size_t gu_lds = (size_t)T * (H + 8) * 2 + sizeof(TileTable) + sizeof(f32x4) * 4 * 4 * 64 +
                         sizeof(int) * kDA;
-  const size_t dn_lds = (size_t)T * k * (I + 8) * 2 + (size_t)T * k * 16 * 2 + sizeof(TileTable) +
-                        sizeof(K2Extra);
-  return gu_lds <= lds_max && dn_lds <= lds_max;
+  return gu_lds <= 160 * 1024;
 }

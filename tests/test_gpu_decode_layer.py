@@ -1,8 +1,11 @@
-"""GPU tests of the two-launch decode layer (moe_forward_decode).
+"""GPU tests of the three-launch decode layer (moe_forward_decode).
 
-* bit-identical to the separate calls (route_permute + decode FFN + combine)
-  in every weight format, and within tolerance of the oracle;
-* repeated calls with varying batch sizes on one workspace;
+* routing outputs (ids, weights, counts, offsets, sorted_idx, inv_idx) are
+  bit-identical to the separate calls, y is within tolerance of the oracle
+  and of the separate-call path, in every weight format;
+* every supported K chunking (H and I of 512 .. 2048);
+* repeated calls with varying batch sizes on one workspace (the per-call
+  column tickets start from zero every call) and bit-repeatable results;
 * slot-table indirection;
 * replays of a captured graph, checked against eager results every time.
 """
@@ -25,14 +28,18 @@ import moe_expert_ffn_router_amd as moe  # noqa: E402
 
 DEV = torch.device("cuda")
 
-DEC = {f: synth.Workload(f"dec_{f}", T=8, H=512, E=64, I=256, k=8, fmt=f, seed=70 + i)
+DEC = {f: synth.Workload(f"dec_{f}", T=8, H=512, E=64, I=512, k=8, fmt=f, seed=70 + i)
        for i, f in enumerate(synth.FORMATS)}
-OUTS = ("ids", "w", "counts", "offsets", "sorted_idx", "inv_idx", "y")
+ROUTING = ("ids", "w", "counts", "offsets", "sorted_idx", "inv_idx")
 
 
 def _layer(case):
     wl = case.wl
     return moe.MoELayer(wl.fmt, wl.E, wl.H, wl.I, wl.k, wl.T, case.stride)
+
+
+def _grab(layer):
+    return {n: getattr(layer, n).clone() for n in ROUTING + ("y",)}
 
 
 def _separate(layer, W, logits, x):
@@ -41,38 +48,55 @@ def _separate(layer, W, logits, x):
     layer.expert_ffn(W, x, T, variant="decode")
     layer.combine(T, False)
     torch.cuda.synchronize()
-    return {n: getattr(layer, n).clone() for n in OUTS}
+    return _grab(layer)
 
 
 def _decode(layer, W, logits, x, slot=None):
     layer.forward_decode(logits, x, W, slot)
     torch.cuda.synchronize()
-    return {n: getattr(layer, n).clone() for n in OUTS}
+    return _grab(layer)
 
 
-def _same(r1, r2, T, k, E):
+def _same_routing(r1, r2, T, k, E):
     A = T * k
     sl = {"ids": A, "w": A, "counts": E, "offsets": E + 1, "sorted_idx": A, "inv_idx": A}
     for n, m in sl.items():
         assert torch.equal(r1[n][:m], r2[n][:m]), n
+
+
+def _same_bits(r1, r2, T):
     assert torch.equal(r1["y"][:T].view(torch.int16), r2["y"][:T].view(torch.int16)), "y"
 
 
-@pytest.mark.parametrize("fmt", synth.FORMATS)
-def test_decode_layer_bit_identical_to_separate_calls(fmt):
-    wl = DEC[fmt]
-    flush(f"[decode-layer] {fmt}")
+def _check_case(wl, seed_note=""):
     case = Case(wl)
     layer = _layer(case)
     assert layer.decode_ws is not None
     W = layer.weights(case.records)
     sep = _separate(layer, W, case.logits, case.x)
     dec = _decode(layer, W, case.logits, case.x)
-    _same(sep, dec, wl.T, wl.k, wl.E)
+    _same_routing(sep, dec, wl.T, wl.k, wl.E)
     ref = OL.forward(case.logits_np, case.x_np, wl.k, case.oracle_experts())
     err = rel_err(bf16_to_np(dec["y"][:wl.T]), ref["y"])
-    flush(f"   rel err vs oracle {err:.2e}")
+    dif = rel_err(bf16_to_np(dec["y"][:wl.T]), bf16_to_np(sep["y"][:wl.T]))
+    flush(f"   {seed_note}rel err vs oracle {err:.2e}, vs separate calls {dif:.2e}")
     assert err <= TOL
+    assert dif <= 1e-2
+    again = _decode(layer, W, case.logits, case.x)
+    _same_bits(dec, again, wl.T)
+
+
+@pytest.mark.parametrize("fmt", synth.FORMATS)
+def test_decode_layer_matches_oracle_and_separate_calls(fmt):
+    flush(f"[decode-layer] {fmt}")
+    _check_case(DEC[fmt])
+
+
+@pytest.mark.parametrize("H,I", [(1024, 1536), (2048, 2048), (1536, 1024)])
+def test_decode_layer_chunkings(H, I):
+    wl = synth.Workload(f"dec_chunk_{H}_{I}", T=6, H=H, E=32, I=I, k=4, fmt="mxfp4", seed=H + I)
+    flush(f"[decode-layer] H={H} I={I}")
+    _check_case(wl, f"H={H} I={I}: ")
 
 
 def test_decode_layer_full_workload_and_varying_batch():
@@ -81,16 +105,25 @@ def test_decode_layer_full_workload_and_varying_batch():
     case = Case(wl, gen_device="cuda")
     layer = _layer(case)
     W = layer.weights(case.records)
-    ref = OL.forward(case.logits_np, case.x_np, wl.k, case.oracle_experts())
+    ex = case.oracle_experts()
+    ref = OL.forward(case.logits_np, case.x_np, wl.k, ex)
     dec = _decode(layer, W, case.logits, case.x)
     err = rel_err(bf16_to_np(dec["y"][:wl.T]), ref["y"])
     flush(f"   full batch rel err vs oracle {err:.2e}")
     assert err <= TOL
     for b, T in enumerate([8, 1, 5, 8, 3, 2]):
-        lg = torch.from_numpy(synth.make_logits(wl, 100 + b)).to(DEV)[:T].contiguous()
-        x = torch.from_numpy(synth.make_x(wl, 100 + b).view(np.int16)).to(DEV).view(torch.bfloat16)
-        x = x[:T].contiguous()
-        _same(_separate(layer, W, lg, x), _decode(layer, W, lg, x), T, wl.k, wl.E)
+        lg_np = synth.make_logits(wl, 100 + b)[:T]
+        x_np = synth.make_x(wl, 100 + b)[:T]
+        lg = torch.from_numpy(np.ascontiguousarray(lg_np)).to(DEV)
+        x = torch.from_numpy(np.ascontiguousarray(x_np).view(np.int16)).to(DEV).view(torch.bfloat16)
+        sep = _separate(layer, W, lg, x)
+        d1 = _decode(layer, W, lg, x)
+        d2 = _decode(layer, W, lg, x)
+        _same_routing(sep, d1, T, wl.k, wl.E)
+        _same_bits(d1, d2, T)
+        r = OL.forward(lg_np, x_np, wl.k, ex)
+        err = rel_err(bf16_to_np(d1["y"][:T]), r["y"])
+        assert err <= TOL, (T, err)
 
 
 def test_decode_layer_slot_table():
@@ -104,7 +137,8 @@ def test_decode_layer_slot_table():
     slot = torch.from_numpy(perm.astype(np.int32)).to(DEV)
     direct = _decode(layer, layer.weights(case.records), case.logits, case.x)
     via = _decode(layer, layer.weights(pool), case.logits, case.x, slot=slot)
-    _same(direct, via, wl.T, wl.k, wl.E)
+    _same_routing(direct, via, wl.T, wl.k, wl.E)
+    _same_bits(direct, via, wl.T)
 
 
 def test_decode_layer_graph_replays_match_eager():
@@ -139,5 +173,7 @@ def test_decode_layer_graph_replays_match_eager():
 
 def test_decode_layer_limits():
     assert moe.moe_forward_decode_supported(2048, 512, 8, 8)
+    assert moe.moe_forward_decode_supported(512, 2048, 64, 4)
     assert not moe.moe_forward_decode_supported(2048, 512, 65, 1)
+    assert not moe.moe_forward_decode_supported(2048, 256, 8, 8)
     assert not moe.moe_forward_decode_supported(7168, 2048, 8, 8)
