@@ -183,44 +183,55 @@ __device__ __forceinline__ UnitPos unit_pos(const TileTable& L, int unit, int n_
   return q;
 }
 
+// Loads of chunk slot j (K chunk wave + 4j) of a unit.
 template <int FMT, int CPW, int MODE>
-__device__ __forceinline__ void unit_issue(const FfnArgs& a, const TileTable& L, int unit, int n_cb,
-                                           UnitRaw<FMT, CPW, MODE>& R) {
+__device__ __forceinline__ void unit_issue_chunk(const FfnArgs& a, const TileTable& L,
+                                                 const int* sidx, int unit, int n_cb, int j,
+                                                 UnitRaw<FMT, CPW, MODE>& R) {
   const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
   const UnitPos q = unit_pos(L, unit, n_cb);
   const uint8_t* rec = tile_record(a, L, q.tile);
+  const int c = wave + 4 * j;
   if constexpr (MODE == MODE_DN) {
-    // h rows first: waiting for them never waits for the weights issued after.
+    // h rows (stored by assignment; sidx maps sorted position -> assignment)
+    // first: waiting for them never waits for the weights issued after.
     // Lanes past the tile's rows read its first row (discarded at use).
-    const uint16_t* arow = a.hbuf + (size_t)(q.seg0 + (l16 < q.rows ? l16 : 0)) * a.I;
+    const uint16_t* arow = a.hbuf + (size_t)sidx[q.seg0 + (l16 < q.rows ? l16 : 0)] * a.I;
+    const uint4* src = reinterpret_cast<const uint4*>(arow + c * KC + g * 32);
 #pragma unroll
-    for (int u = 0; u < CPW; ++u) {
-      const uint4* src = reinterpret_cast<const uint4*>(arow + (wave + 4 * u) * KC + g * 32);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) R.a[u][i] = src[i];
-    }
+    for (int i = 0; i < 4; ++i) R.a[j][i] = src[i];
   }
   const int K = MODE == MODE_GU ? a.H : a.I;
   const uint8_t* w = rec + (MODE == MODE_GU ? a.off_w13 : a.off_w2);
   const uint8_t* sc = rec + (MODE == MODE_GU ? a.off_w13s : a.off_w2s);
 #pragma unroll
-  for (int u = 0; u < CPW; ++u) {
-    const int c = wave + 4 * u;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = MODE == MODE_GU ? (j < 2 ? 0 : a.I) + q.cb * 32 + (j & 1) * 16 + l16
-                                      : q.cb * 64 + j * 16 + l16;
-      load_b_raw<FMT>(w, sc, row, K, c * KC + g * 32, R.w[u][j]);
-    }
+  for (int s = 0; s < 4; ++s) {
+    const int row = MODE == MODE_GU ? (s < 2 ? 0 : a.I) + q.cb * 32 + (s & 1) * 16 + l16
+                                    : q.cb * 64 + s * 16 + l16;
+    load_b_raw<FMT>(w, sc, row, K, c * KC + g * 32, R.w[j][s]);
   }
 }
 
-// x rows come from LDS (xs, pitch xp) for gate/up; sidx holds sorted_idx.
 template <int FMT, int CPW, int MODE>
+__device__ __forceinline__ void unit_issue(const FfnArgs& a, const TileTable& L, const int* sidx,
+                                           int unit, int n_cb, UnitRaw<FMT, CPW, MODE>& R) {
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) unit_issue_chunk<FMT, CPW, MODE>(a, L, sidx, unit, n_cb, j, R);
+}
+
+struct NoIssue {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
+// x rows come from LDS (xs, pitch xp) for gate/up; sidx holds sorted_idx.
+// pre(j) runs before chunk slot j is computed (it issues the next unit's
+// loads slot by slot, so computing starts as soon as this unit's data is in).
+template <int FMT, int CPW, int MODE, typename Pre = NoIssue>
 __device__ __forceinline__ void unit_finish(const FfnArgs& a, const TileTable& L, const int* sidx,
                                             const uint16_t* xs, int xp, f32x4 (&red)[4][4][64],
-                                            int unit, int n_cb, const UnitRaw<FMT, CPW, MODE>& R) {
+                                            int unit, int n_cb, const UnitRaw<FMT, CPW, MODE>& R,
+                                            Pre pre = Pre()) {
   const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const UnitPos q = unit_pos(L, unit, n_cb);
@@ -232,6 +243,7 @@ __device__ __forceinline__ void unit_finish(const FfnArgs& a, const TileTable& L
   for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < CPW; ++u) {
+    pre(u);
     const int c = wave + 4 * u;
     bf16x8 av[4];
 #pragma unroll
@@ -288,7 +300,8 @@ __device__ __forceinline__ void unit_finish(const FfnArgs& a, const TileTable& L
         if (m < q.rows) {
           const float gv = gs[r] * tsg, uv = us[r] * tsu;
           const float hv = gv / (1.0f + expf(-gv)) * uv;
-          a.hbuf[(size_t)(q.seg0 + m) * a.I + q.cb * 32 + wave * 16 + l16] = f32_to_bf16_rne(hv);
+          a.hbuf[(size_t)sidx[q.seg0 + m] * a.I + q.cb * 32 + wave * 16 + l16] =
+              f32_to_bf16_rne(hv);
         }
       }
     }
@@ -314,9 +327,10 @@ __device__ __forceinline__ void unit_finish(const FfnArgs& a, const TileTable& L
   __syncthreads();  // red is rewritten by the next unit
 }
 
-// Units go in pairs: both units' loads are issued before the first is
-// computed.  Nothing stays in flight across iterations, so no register holding
-// a pending load is ever copied (a copy would wait for the load).
+// Units go in pairs: the second unit's loads are issued chunk slot by chunk
+// slot while the first is computed.  Nothing stays in flight across
+// iterations, so no register holding a pending load is ever copied (a copy
+// would wait for the load).
 template <int FMT, int CPW>
 __global__ __launch_bounds__(256) void dec_gateup_kernel(DecArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];  // [T][H + 8]
@@ -341,10 +355,11 @@ __global__ __launch_bounds__(256) void dec_gateup_kernel(DecArgs p) {
   const int n_cb = a.I / 32, U = n_tiles * n_cb, G = (int)gridDim.x;
   UnitRaw<FMT, CPW, MODE_GU> ra, rb;
   for (int u = blockIdx.x; u < U; u += 2 * G) {
-    unit_issue<FMT, CPW, MODE_GU>(a, L, u, n_cb, ra);
+    unit_issue<FMT, CPW, MODE_GU>(a, L, sidx, u, n_cb, ra);
     if (u + G < U) {
-      unit_issue<FMT, CPW, MODE_GU>(a, L, u + G, n_cb, rb);
-      unit_finish<FMT, CPW, MODE_GU>(a, L, sidx, xs, xp, red, u, n_cb, ra);
+      unit_finish<FMT, CPW, MODE_GU>(a, L, sidx, xs, xp, red, u, n_cb, ra, [&](int j) {
+        unit_issue_chunk<FMT, CPW, MODE_GU>(a, L, sidx, u + G, n_cb, j, rb);
+      });
       unit_finish<FMT, CPW, MODE_GU>(a, L, sidx, xs, xp, red, u + G, n_cb, rb);
     } else {
       unit_finish<FMT, CPW, MODE_GU>(a, L, sidx, xs, xp, red, u, n_cb, ra);
@@ -356,20 +371,140 @@ template <int FMT, int CPW>
 __global__ __launch_bounds__(256) void dec_down_kernel(FfnArgs a) {
   __shared__ TileTable L;
   __shared__ f32x4 red[4][4][64];
+  __shared__ int sidx[kDA];
+  const int tid = threadIdx.x;
+  const int sid = tid < a.A ? a.sorted_idx[tid] : 0;
   TileRegs<256> tr;
   tiles_load<256>(a, tr);
+  if (tid < a.A) sidx[tid] = sid;
   const int n_tiles = tiles_build<256>(a, tr, L);
   const int n_cb = a.H / 64, U = n_tiles * n_cb, G = (int)gridDim.x;
   UnitRaw<FMT, CPW, MODE_DN> ra, rb;
   for (int u = blockIdx.x; u < U; u += 2 * G) {
-    unit_issue<FMT, CPW, MODE_DN>(a, L, u, n_cb, ra);
+    unit_issue<FMT, CPW, MODE_DN>(a, L, sidx, u, n_cb, ra);
     if (u + G < U) {
-      unit_issue<FMT, CPW, MODE_DN>(a, L, u + G, n_cb, rb);
-      unit_finish<FMT, CPW, MODE_DN>(a, L, nullptr, nullptr, 0, red, u, n_cb, ra);
+      unit_finish<FMT, CPW, MODE_DN>(a, L, nullptr, nullptr, 0, red, u, n_cb, ra, [&](int j) {
+        unit_issue_chunk<FMT, CPW, MODE_DN>(a, L, sidx, u + G, n_cb, j, rb);
+      });
       unit_finish<FMT, CPW, MODE_DN>(a, L, nullptr, nullptr, 0, red, u + G, n_cb, rb);
     } else {
       unit_finish<FMT, CPW, MODE_DN>(a, L, nullptr, nullptr, 0, red, u, n_cb, ra);
     }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// token-major down + combine (small T): workgroup (t, cb) computes y[t] for
+// output columns [32*cb, 32*cb + 32).  Wave w takes the token's experts
+// j = w, w+4, ... (NJ of them; past k it repeats the last expert and the
+// result is unused, so no load is guarded by a branch), all of K, in groups
+// of 4 chunks of 128.  The expert's h row is row 0 of the MFMA A operand (the
+// other 15 rows are zero).  Each expert's output is rounded to bf16 (the
+// y_perm value), then the workgroup sums them in top-k order in fp32 with the
+// routing weights, adds the shared expert and rounds once.
+// ----------------------------------------------------------------------------
+constexpr int kTokCols = 32;
+
+template <int FMT, int NJ>
+__global__ __launch_bounds__(256) void dec_down_tok_kernel(DecArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t hs[];  // [k][I + 8]
+  __shared__ float yp[kMaxK][kTokCols];
+  __shared__ int eid[kMaxK];
+  __shared__ float ew[kMaxK];
+  const FfnArgs& a = p.f;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int k = a.k, I = a.I, H = a.H, hp = I + 8;
+  const int n_cb = H / kTokCols, t = blockIdx.x / n_cb, cb = blockIdx.x - t * n_cb;
+  // one round trip: the token's k h rows (stored by assignment), ids, weights
+  uint4 hv[8];
+  stage_load<256, 8>(hv, a.hbuf + (size_t)t * k * I, I, k, I, 0);
+  int id_v = 0;
+  float w_v = 0.0f;
+  if (tid < k) {
+    id_v = p.ids[t * k + tid];
+    w_v = p.wts[t * k + tid];
+  }
+  stage_store<256, 8>(hv, hs, hp, k, I, 0);
+  for (int q0 = 256 * 8; q0 < k * (I / 8); q0 += 256 * 8) {
+    stage_load<256, 8>(hv, a.hbuf + (size_t)t * k * I, I, k, I, q0);
+    stage_store<256, 8>(hv, hs, hp, k, I, q0);
+  }
+  if (tid < k) {
+    eid[tid] = a.slot_of ? a.slot_of[id_v] : id_v;
+    ew[tid] = w_v;
+  }
+  __syncthreads();
+  const uint8_t* rec[NJ];
+  int jj[NJ];
+#pragma unroll
+  for (int i = 0; i < NJ; ++i) {
+    jj[i] = min(wave + 4 * i, k - 1);
+    rec[i] = a.base + (size_t)eid[jj[i]] * a.stride;
+  }
+  f32x4 acc[NJ][2];
+#pragma unroll
+  for (int i = 0; i < NJ; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nchunks = I / KC;
+  for (int c0 = 0; c0 < nchunks; c0 += 4) {
+    BRaw<FMT> raw[NJ][2][4];
+#pragma unroll
+    for (int i = 0; i < NJ; ++i)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          load_b_raw<FMT>(rec[i] + a.off_w2, rec[i] + a.off_w2s, cb * kTokCols + sub * 16 + l16, I,
+                          (c0 + u) * KC + g * 32, raw[i][sub][u]);
+#pragma unroll
+    for (int i = 0; i < NJ; ++i) {
+      const uint16_t* hrow = hs + jj[i] * hp;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        bf16x8 av[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint4 v = *reinterpret_cast<const uint4*>(hrow + (c0 + u) * KC + g * 32 + q * 8);
+          av[q] = l16 == 0 ? bits_to_bf16x8(v.x, v.y, v.z, v.w) : bits_to_bf16x8(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          bf16x8 b[4];
+          decode_b<FMT>(raw[i][sub][u], b);
+          if constexpr (FMT == MOE_W_FP8_B128) {
+            f32x4 tt = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) tt = mfma16(av[q], b[q], tt);
+            const float bs = block_scale<FMT>(raw[i][sub][u]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][sub][r] = fmaf(bs, tt[r], acc[i][sub][r]);
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[i][sub] = mfma16(av[q], b[q], acc[i][sub]);
+          }
+        }
+      }
+    }
+  }
+  // row 0 of each expert's 16x16 result sits in lanes 0..15, element 0
+#pragma unroll
+  for (int i = 0; i < NJ; ++i) {
+    const int j = wave + 4 * i;
+    if (j < k && g == 0) {
+      float tsd = 1.0f;
+      if constexpr (FMT == MOE_W_NVFP4) tsd = reinterpret_cast<const float*>(rec[i] + a.off_ts)[2];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+        yp[j][sub * 16 + l16] = bf16_to_f32(f32_to_bf16_rne(acc[i][sub][0] * tsd));
+    }
+  }
+  __syncthreads();
+  if (tid < kTokCols) {
+    const int col = cb * kTokCols + tid;
+    float y = 0.0f;
+    for (int j = 0; j < k; ++j) y = fmaf(ew[j], yp[j][tid], y);
+    if (p.y_shared) y += bf16_to_f32(p.y_shared[(size_t)t * H + col]);
+    p.y[(size_t)t * H + col] = f32_to_bf16_rne(y);
   }
 }
 
@@ -415,7 +550,21 @@ static int launch_down(const DecArgs& p, hipStream_t s) {
   return MOE_OK;
 }
 
-// K chunks per wave: H / 512 for gate/up, I / 512 for down
+template <int FMT, int NJ>
+static int launch_down_tok(const DecArgs& p, hipStream_t s) {
+  const size_t h_lds = (size_t)p.f.k * (p.f.I + 8) * 2;
+  static size_t granted = 0;
+  auto k = dec_down_tok_kernel<FMT, NJ>;
+  if (!lds_ok(k, h_lds, granted)) return set_error(MOE_ERR_HIP, "moe_forward_decode: LDS attribute");
+  k<<<p.T * (p.f.H / kTokCols), 256, h_lds, s>>>(p);
+  return MOE_OK;
+}
+
+// Token-major down (no permuted copy of y, no combine launch) while the
+// batch is small enough that few experts are shared between its tokens.
+constexpr int kTokMaxT = 16;
+
+// K chunks per wave: H / 512 for gate/up, I / 512 for the tile-major down
 template <int FMT>
 static int launch_decode(DecArgs& p, hipStream_t s) {
   int st;
@@ -426,6 +575,16 @@ static int launch_decode(DecArgs& p, hipStream_t s) {
     default: st = launch_gateup<FMT, 4>(p, s); break;
   }
   if (st) return st;
+  if (p.T <= kTokMaxT) {
+    switch ((p.f.k + 3) / 4) {
+      case 1: st = launch_down_tok<FMT, 1>(p, s); break;
+      case 2: st = launch_down_tok<FMT, 2>(p, s); break;
+      case 3: st = launch_down_tok<FMT, 3>(p, s); break;
+      default: st = launch_down_tok<FMT, 4>(p, s); break;
+    }
+    if (st) return st;
+    return check_launch("moe_forward_decode");
+  }
   switch (p.f.I / 512) {
     case 1: st = launch_down<FMT, 1>(p, s); break;
     case 2: st = launch_down<FMT, 2>(p, s); break;
@@ -527,5 +686,5 @@ extern "C" int moe_forward_decode_supported(int32_t H, int32_t I, int32_t T, int
   if (H % 512 || I % 512 || H > 2048 || I > 2048 || H < 512 || I < 512) return 0;
   const size_t gu_lds = (size_t)T * (H + 8) * 2 + sizeof(TileTable) + sizeof(f32x4) * 4 * 4 * 64 +
                         sizeof(int) * kDA;
-  return gu_lds <= 160 * 1024;
+  return gu_lds <= 160 * 1024;  // the token-major down's h rows (k <= 16) always fit
 }

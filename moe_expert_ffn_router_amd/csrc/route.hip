@@ -33,20 +33,26 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 constexpr int kSmallA = 256;
 constexpr int kSmallT = 64;
 
-// Route + permute for T <= 64, T*k <= 256 in one workgroup of 16 waves.  The
-// stable rank of assignment a among equal experts is counted directly over
-// the earlier assignments (at most 255 LDS reads, broadcast to the wave).
+// Route + permute for T <= 64, T*k <= 256 in one workgroup of 16 waves.
+// Stable rank of assignment a among equal experts: within its wave, the lanes
+// holding the same expert are found with one ballot per expert-id bit (their
+// AND is the match mask) and counted below the lane; earlier waves contribute
+// through per-wave histograms (the lowest lane of each match group adds the
+// group's size), summed in wave order.  No atomics: deterministic.
+constexpr int kSmallW = kSmallA / 64;
+
 template <int VPL>
 __global__ __launch_bounds__(1024) void route_permute_small_kernel(
     const float* __restrict__ logits, int T, int E, int k, int renorm, int* __restrict__ ids,
     float* __restrict__ wts, int* __restrict__ counts, int* __restrict__ offsets,
     int* __restrict__ sorted_idx, int* __restrict__ inv_idx) {
   __shared__ int sid[kSmallA];
+  __shared__ int whist[kSmallW][kMaxE];
   __shared__ int hist[kMaxE];
   __shared__ int wave_tot[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int A = T * k;
-  if (tid < E) hist[tid] = 0;
+  for (int i = tid; i < kSmallW * E; i += 1024) whist[i / E][i % E] = 0;
   for (int t = wave; t < T; t += 16) {
     int id;
     float w;
@@ -59,13 +65,31 @@ __global__ __launch_bounds__(1024) void route_permute_small_kernel(
   }
   __syncthreads();
   int e = 0, rank = 0;
-  if (tid < A) {
-    e = sid[tid];
-    for (int q = 0; q < tid; ++q) rank += (sid[q] == e);
-    atomicAdd(&hist[e], 1);  // integer count: order-independent
+  if (wave < kSmallW) {  // waves 0..3 own assignments 64*wave + lane
+    const bool live = tid < A;
+    e = live ? sid[tid] : -1;
+    uint64_t m = __ballot(live);
+#pragma unroll
+    for (int b = 0; b < 10; ++b) {  // E <= 1024: 10 id bits
+      const uint64_t on = __ballot(live && ((e >> b) & 1));
+      m &= ((e >> b) & 1) ? on : ~on;
+    }
+    if (!live) m = 0;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    rank = __popcll(m & below);
+    if (live && rank == 0) whist[wave][e] = __popcll(m);
   }
   __syncthreads();
-  if (tid < E) counts[tid] = hist[tid];
+  for (int i = tid; i < E; i += 1024) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < kSmallW; ++w) c += whist[w][i];
+    hist[i] = c;
+    counts[i] = c;
+  }
+  if (tid < A)
+    for (int w = 0; w < wave; ++w) rank += whist[w][e];
+  __syncthreads();
   const int total = block_exclusive_scan_1024(hist, E, wave_tot);
   if (tid < E) offsets[tid] = hist[tid];
   if (tid == 0) offsets[E] = total;

@@ -1,11 +1,13 @@
-"""GPU tests of the three-launch decode layer (moe_forward_decode).
+"""GPU tests of the decode layer (moe_forward_decode).
 
 * routing outputs (ids, weights, counts, offsets, sorted_idx, inv_idx) are
   bit-identical to the separate calls, y is within tolerance of the oracle
   and of the separate-call path, in every weight format;
-* every supported K chunking (H and I of 512 .. 2048);
-* repeated calls with varying batch sizes on one workspace (the per-call
-  column tickets start from zero every call) and bit-repeatable results;
+* every supported K chunking (H and I of 512 .. 2048), both down-projection
+  forms (token-major for small T, tile-major + combine above it) and k not a
+  multiple of the 4 waves;
+* repeated calls with varying batch sizes on one workspace and
+  bit-repeatable results;
 * slot-table indirection;
 * replays of a captured graph, checked against eager results every time.
 """
@@ -92,11 +94,13 @@ def test_decode_layer_matches_oracle_and_separate_calls(fmt):
     _check_case(DEC[fmt])
 
 
-@pytest.mark.parametrize("H,I", [(1024, 1536), (2048, 2048), (1536, 1024)])
-def test_decode_layer_chunkings(H, I):
-    wl = synth.Workload(f"dec_chunk_{H}_{I}", T=6, H=H, E=32, I=I, k=4, fmt="mxfp4", seed=H + I)
-    flush(f"[decode-layer] H={H} I={I}")
-    _check_case(wl, f"H={H} I={I}: ")
+@pytest.mark.parametrize("H,I,T,k", [(1024, 1536, 6, 4), (2048, 2048, 6, 4), (1536, 1024, 6, 4),
+                                     (512, 512, 16, 13), (512, 1024, 32, 4), (2048, 512, 24, 8)])
+def test_decode_layer_chunkings(H, I, T, k):
+    """Every K chunking; T <= 16 takes the token-major down, larger T the tile-major one."""
+    wl = synth.Workload(f"dec_chunk_{H}_{I}", T=T, H=H, E=32, I=I, k=k, fmt="mxfp4", seed=H + I + T)
+    flush(f"[decode-layer] H={H} I={I} T={T} k={k}")
+    _check_case(wl, f"H={H} I={I} T={T} k={k}: ")
 
 
 def test_decode_layer_full_workload_and_varying_batch():
