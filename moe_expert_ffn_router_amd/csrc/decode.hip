@@ -22,6 +22,7 @@
 namespace moe {
 
 constexpr int kDT = 64, kDA = 256, kDTiles = 256;
+constexpr int kTokMaxT = 16, kTokMaxH = 2048;  // token-major path: T <= 16, H <= 2048
 constexpr int kDGuCols = 32;  // gate/up unit: 16 + 16 h-columns (2 gate + 2 up subtiles)
 
 struct DecArgs {
@@ -394,6 +395,191 @@ __global__ __launch_bounds__(256) void dec_down_kernel(FfnArgs a) {
 }
 
 // ----------------------------------------------------------------------------
+// token-major gate/up (small T): the grid is a multiple of T and workgroup b
+// serves token t = b % T only, so it routes that one token itself (wave 0:
+// one round trip for the logits row, then the top-k) and needs nothing from
+// any other workgroup.  Its units u = b, b + G, ... are (t, expert slot j,
+// 32 h-columns cb) with u = t + T*(j + k*cb); an expert's weights are read
+// once per token that picked it.  The token's x row is row 0 of the MFMA A
+// operand (the other 15 rows are zero); the 4 waves split K as in the tile
+// units and sum their partials in wave order.  h is stored by assignment
+// (t*k + j).  Workgroup t (< T) also writes the token's ids and weights.
+// ----------------------------------------------------------------------------
+template <int FMT, int CPW>
+struct TokRaw {
+  BRaw<FMT> w[CPW][4];
+};
+
+__device__ __forceinline__ void tok_unit(int u, int T, int k, int& j, int& cb) {
+  const int r = u / T;
+  j = r % k;
+  cb = r / k;
+}
+
+template <int FMT, int CPW>
+__device__ __forceinline__ void tok_issue_chunk(const FfnArgs& a, const int* eslot, int T, int u,
+                                                int c_slot, TokRaw<FMT, CPW>& R) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int j, cb;
+  tok_unit(u, T, a.k, j, cb);
+  const uint8_t* rec = a.base + (size_t)eslot[j] * a.stride;
+  const int c = wave + 4 * c_slot;
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    load_b_raw<FMT>(rec + a.off_w13, rec + a.off_w13s, (s < 2 ? 0 : a.I) + cb * 32 + (s & 1) * 16 + l16,
+                    a.H, c * KC + g * 32, R.w[c_slot][s]);
+}
+
+template <int FMT, int CPW, typename Pre = NoIssue>
+__device__ __forceinline__ void tok_finish(const FfnArgs& a, const int* eslot, const uint16_t* xs,
+                                           f32x4 (&red)[4][4][64], int T, int t, int u,
+                                           const TokRaw<FMT, CPW>& R, Pre pre = Pre()) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  f32x4 acc[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int cs = 0; cs < CPW; ++cs) {
+    pre(cs);
+    const int c = wave + 4 * cs;
+    bf16x8 av[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = *reinterpret_cast<const uint4*>(xs + c * KC + g * 32 + q * 8);
+      av[q] = l16 == 0 ? bits_to_bf16x8(v.x, v.y, v.z, v.w) : bits_to_bf16x8(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 b[4];
+      decode_b<FMT>(R.w[cs][s], b);
+      if constexpr (FMT == MOE_W_FP8_B128) {
+        f32x4 tt = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tt = mfma16(av[q], b[q], tt);
+        const float bs = block_scale<FMT>(R.w[cs][s]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[s][r] = fmaf(bs, tt[r], acc[s][r]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[s] = mfma16(av[q], b[q], acc[s]);
+      }
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) red[wave][s][lane] = acc[s];
+  __syncthreads();
+  if (wave < 2 && g == 0) {  // row 0: lanes 0..15, element 0
+    float gs = red[0][wave][lane][0], us = red[0][2 + wave][lane][0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      gs += red[w][wave][lane][0];
+      us += red[w][2 + wave][lane][0];
+    }
+    int j, cb;
+    tok_unit(u, T, a.k, j, cb);
+    float tsg = 1.0f, tsu = 1.0f;
+    if constexpr (FMT == MOE_W_NVFP4) {
+      const float* ts =
+          reinterpret_cast<const float*>(a.base + (size_t)eslot[j] * a.stride + a.off_ts);
+      tsg = ts[0];
+      tsu = ts[1];
+    }
+    const float gv = gs * tsg, uv = us * tsu;
+    const float hv = gv / (1.0f + expf(-gv)) * uv;
+    a.hbuf[(size_t)(t * a.k + j) * a.I + cb * 32 + wave * 16 + l16] = f32_to_bf16_rne(hv);
+  }
+  __syncthreads();  // red is rewritten by the next unit
+}
+
+template <int FMT, int CPW, int VPL>
+__global__ __launch_bounds__(256) void dec_gateup_tok_kernel(DecArgs p) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[kTokMaxH];
+  __shared__ f32x4 red[4][4][64];
+  __shared__ int eslot[kMaxK];
+  const FfnArgs& a = p.f;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int T = p.T, k = a.k, E = a.E, t = blockIdx.x % T;
+  // one round trip: the token's x row and (wave 0) its logits row
+  uint4 xv = uint4{0u, 0u, 0u, 0u};
+  if (tid < a.H / 8) xv = reinterpret_cast<const uint4*>(a.x + (size_t)t * a.H)[tid];
+  float lv[VPL];
+  if (wave == 0) route_load<VPL>(p.logits + (size_t)t * E, E, lane, lv);
+  if (tid < a.H / 8) reinterpret_cast<uint4*>(xs)[tid] = xv;
+  if (wave == 0) {
+    int id;
+    float w;
+    route_select<VPL>(lv, E, k, p.renorm, lane, id, w);
+    if (lane < k) {
+      eslot[lane] = a.slot_of ? a.slot_of[id] : id;
+      if ((int)blockIdx.x == t) {
+        p.ids[t * k + lane] = id;
+        p.wts[t * k + lane] = w;
+      }
+    }
+  }
+  __syncthreads();
+  const int U = T * k * (a.I / 32), G = (int)gridDim.x;
+  TokRaw<FMT, CPW> ra, rb;
+  for (int u = blockIdx.x; u < U; u += 2 * G) {
+#pragma unroll
+    for (int cs = 0; cs < CPW; ++cs) tok_issue_chunk<FMT, CPW>(a, eslot, T, u, cs, ra);
+    if (u + G < U) {
+      tok_finish<FMT, CPW>(a, eslot, xs, red, T, t, u, ra,
+                           [&](int cs) { tok_issue_chunk<FMT, CPW>(a, eslot, T, u + G, cs, rb); });
+      tok_finish<FMT, CPW>(a, eslot, xs, red, T, t, u + G, rb);
+    } else {
+      tok_finish<FMT, CPW>(a, eslot, xs, red, T, t, u, ra);
+    }
+  }
+}
+
+// The permutation outputs of a token-major call (counts, offsets, sorted_idx,
+// inv_idx) from the routing ids, by one workgroup: stable rank inside each
+// wave's 64 assignments from per-bit ballot match masks, earlier waves through
+// per-wave histograms, then an exclusive scan of the counts.  Same results as
+// route_permute_small_kernel.
+__device__ __forceinline__ void permute_block(const DecArgs& p, int* lds) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = p.f.E, A = p.f.A;
+  int* whist = lds;             // [4][E]
+  int* hist = lds + 4 * E;      // [E]
+  int* wave_tot = hist + kMaxE;  // [16]
+  for (int i = tid; i < 4 * E; i += 256) whist[i] = 0;
+  const bool live = tid < A;
+  const int e = live ? p.ids[tid] : -1;
+  __syncthreads();
+  uint64_t m = __ballot(live);
+#pragma unroll
+  for (int b = 0; b < 10; ++b) {  // E <= 1024: 10 id bits
+    const uint64_t on = __ballot(live && ((e >> b) & 1));
+    m &= ((e >> b) & 1) ? on : ~on;
+  }
+  if (!live) m = 0;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int rank = __popcll(m & below);
+  if (live && rank == 0) whist[wave * E + e] = __popcll(m);
+  __syncthreads();
+  for (int i = tid; i < E; i += 256) {
+    const int c = whist[i] + whist[E + i] + whist[2 * E + i] + whist[3 * E + i];
+    hist[i] = c;
+    p.counts[i] = c;
+  }
+  if (live)
+    for (int w = 0; w < wave; ++w) rank += whist[w * E + e];
+  __syncthreads();
+  const int total = block_exclusive_scan<256>(hist, E, wave_tot);
+  for (int i = tid; i < E; i += 256) p.offsets[i] = hist[i];
+  if (tid == 0) p.offsets[E] = total;
+  if (live) {
+    const int pos = hist[e] + rank;
+    p.sorted[pos] = tid;
+    p.inv[tid] = pos;
+  }
+}
+
+// ----------------------------------------------------------------------------
 // token-major down + combine (small T): workgroup (t, cb) computes y[t] for
 // output columns [32*cb, 32*cb + 32).  Wave w takes the token's experts
 // j = w, w+4, ... (NJ of them; past k it repeats the last expert and the
@@ -416,6 +602,10 @@ __global__ __launch_bounds__(256) void dec_down_tok_kernel(DecArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int k = a.k, I = a.I, H = a.H, hp = I + 8;
   const int n_cb = H / kTokCols, t = blockIdx.x / n_cb, cb = blockIdx.x - t * n_cb;
+  if (t == p.T) {  // the one extra workgroup: permutation outputs
+    permute_block(p, reinterpret_cast<int*>(hs));
+    return;
+  }
   // one round trip: the token's k h rows (stored by assignment), ids, weights
   uint4 hv[8];
   stage_load<256, 8>(hv, a.hbuf + (size_t)t * k * I, I, k, I, 0);
@@ -538,6 +728,20 @@ static int launch_gateup(const DecArgs& p, hipStream_t s) {
   return MOE_OK;
 }
 
+template <int FMT, int CPW, int VPL>
+static int launch_gateup_tok(const DecArgs& p, hipStream_t s) {
+  static int per_cu = 0;
+  auto k = dec_gateup_tok_kernel<FMT, CPW, VPL>;
+  if (!per_cu &&
+      (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k), 256,
+                                                    0) != hipSuccess || per_cu < 1))
+    per_cu = 1;
+  // a multiple of T, so that every workgroup serves one token
+  const int G = p.T * ((per_cu * g_cus) / p.T > 0 ? (per_cu * g_cus) / p.T : 1);
+  k<<<G, 256, 0, s>>>(p);
+  return MOE_OK;
+}
+
 template <int FMT, int CPW>
 static int launch_down(const DecArgs& p, hipStream_t s) {
   static int per_cu = 0;
@@ -550,32 +754,40 @@ static int launch_down(const DecArgs& p, hipStream_t s) {
   return MOE_OK;
 }
 
+// One workgroup per (token, 32 columns) plus one for the permutation outputs.
 template <int FMT, int NJ>
 static int launch_down_tok(const DecArgs& p, hipStream_t s) {
   const size_t h_lds = (size_t)p.f.k * (p.f.I + 8) * 2;
+  const size_t perm_lds = ((size_t)5 * p.f.E + kMaxE + 16) * 4;
+  const size_t lds = h_lds > perm_lds ? h_lds : perm_lds;
   static size_t granted = 0;
   auto k = dec_down_tok_kernel<FMT, NJ>;
-  if (!lds_ok(k, h_lds, granted)) return set_error(MOE_ERR_HIP, "moe_forward_decode: LDS attribute");
-  k<<<p.T * (p.f.H / kTokCols), 256, h_lds, s>>>(p);
+  if (!lds_ok(k, lds, granted)) return set_error(MOE_ERR_HIP, "moe_forward_decode: LDS attribute");
+  k<<<p.T * (p.f.H / kTokCols) + 1, 256, lds, s>>>(p);
   return MOE_OK;
 }
 
-// Token-major down (no permuted copy of y, no combine launch) while the
-// batch is small enough that few experts are shared between its tokens.
-constexpr int kTokMaxT = 16;
+// Small batches (T <= 16, H <= 2048) take the token-major path: two launches,
+// no permutation on the critical path (few experts are shared by its tokens).
+static bool token_major(int T, int H) { return T <= kTokMaxT && H <= kTokMaxH; }
+
+template <int FMT, int CPW>
+static int launch_gateup_tok_vpl(const DecArgs& p, hipStream_t s) {
+  return p.f.E <= 256 ? launch_gateup_tok<FMT, CPW, 4>(p, s) : launch_gateup_tok<FMT, CPW, 16>(p, s);
+}
 
 // K chunks per wave: H / 512 for gate/up, I / 512 for the tile-major down
 template <int FMT>
 static int launch_decode(DecArgs& p, hipStream_t s) {
   int st;
-  switch (p.f.H / 512) {
-    case 1: st = launch_gateup<FMT, 1>(p, s); break;
-    case 2: st = launch_gateup<FMT, 2>(p, s); break;
-    case 3: st = launch_gateup<FMT, 3>(p, s); break;
-    default: st = launch_gateup<FMT, 4>(p, s); break;
-  }
-  if (st) return st;
-  if (p.T <= kTokMaxT) {
+  if (token_major(p.T, p.f.H)) {
+    switch (p.f.H / 512) {
+      case 1: st = launch_gateup_tok_vpl<FMT, 1>(p, s); break;
+      case 2: st = launch_gateup_tok_vpl<FMT, 2>(p, s); break;
+      case 3: st = launch_gateup_tok_vpl<FMT, 3>(p, s); break;
+      default: st = launch_gateup_tok_vpl<FMT, 4>(p, s); break;
+    }
+    if (st) return st;
     switch ((p.f.k + 3) / 4) {
       case 1: st = launch_down_tok<FMT, 1>(p, s); break;
       case 2: st = launch_down_tok<FMT, 2>(p, s); break;
@@ -585,6 +797,17 @@ static int launch_decode(DecArgs& p, hipStream_t s) {
     if (st) return st;
     return check_launch("moe_forward_decode");
   }
+  const int rp = moe_route_permute(p.logits, p.T, p.f.E, p.f.k, p.renorm, p.ids, p.wts, p.counts,
+                                   p.offsets, p.sorted, p.inv, nullptr, 0,
+                                   reinterpret_cast<moe_stream_t>(s));
+  if (rp) return rp;
+  switch (p.f.H / 512) {
+    case 1: st = launch_gateup<FMT, 1>(p, s); break;
+    case 2: st = launch_gateup<FMT, 2>(p, s); break;
+    case 3: st = launch_gateup<FMT, 3>(p, s); break;
+    default: st = launch_gateup<FMT, 4>(p, s); break;
+  }
+  if (st) return st;
   switch (p.f.I / 512) {
     case 1: st = launch_down<FMT, 1>(p, s); break;
     case 2: st = launch_down<FMT, 2>(p, s); break;
@@ -668,9 +891,7 @@ extern "C" int moe_forward_decode(const moe_experts* W, const int32_t* slot_of_e
   p.y_shared = y_shared;
   p.y = y;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  int st = moe_route_permute(logits, T, W->E, k, renorm, topk_ids, topk_w, counts, offsets,
-                             sorted_idx, inv_idx, nullptr, 0, stream);
-  if (st) return st;
+
   switch (W->fmt) {
     case MOE_W_BF16: return launch_decode<MOE_W_BF16>(p, s);
     case MOE_W_MXFP4: return launch_decode<MOE_W_MXFP4>(p, s);

@@ -146,6 +146,26 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_readlane(v, 63);
 }
 
+// One step of a 64-bit wave maximum: DPP moves both halves, one u64 compare.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint64_t max64_step(uint64_t x) {
+  const int lo = (int)(uint32_t)x, hi = (int)(uint32_t)(x >> 32);
+  const uint64_t o = ((uint64_t)(uint32_t)dpp_i32<CTRL, ROW_MASK>(hi, hi) << 32) |
+                     (uint32_t)dpp_i32<CTRL, ROW_MASK>(lo, lo);
+  return o > x ? o : x;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+  x = max64_step<0xB1>(x);
+  x = max64_step<0x4E>(x);
+  x = max64_step<0x141>(x);
+  x = max64_step<0x140>(x);
+  x = max64_step<0x142, 0xA>(x);
+  x = max64_step<0x143, 0xC>(x);
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 63) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 63);
+}
+
 // Sum over the wave in a fixed order (identical result in every lane).
 __device__ __forceinline__ float wave_sum_f32(float x) {
   int v = __float_as_int(x);

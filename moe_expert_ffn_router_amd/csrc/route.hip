@@ -1,12 +1,12 @@
 // Router: top-k experts per token with renormalised softmax weights.
 //
 // One wavefront per token.  Lane l holds logits l, l+64, ... of its token as
-// order-preserving 32-bit keys (-0.0 mapped to +0.0).  Each of the k rounds
-// takes the lane-local maximum, a DPP wave maximum, and then the lowest expert
-// index holding that key (ballot over the lane's slots in index order: index
-// e = lane + 64*slot, so the first slot with a hit and its lowest lane give
-// the lowest index).  The owner clears the winner; lane j < k keeps round j's
-// winner and finally computes exp(l_j - l_0) / sum over the k selected.
+// order-preserving 32-bit keys (-0.0 mapped to +0.0) packed with their
+// complemented expert index.  Each of the k rounds takes the lane-local and
+// then the DPP wave maximum of the packed values, which is the largest key
+// and, among equal keys, the lowest index.  The owner clears the winner; lane
+// j < k keeps round j's winner and finally computes exp(l_j - l_0) / sum over
+// the k selected.
 //
 // Decode-sized batches (T <= 64, T*k <= 256) also have a fused kernel that
 // routes and permutes in one workgroup (one launch instead of two).
