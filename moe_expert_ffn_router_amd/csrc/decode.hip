@@ -431,9 +431,13 @@ __device__ __forceinline__ void tok_issue_chunk(const FfnArgs& a, const int* esl
                     a.H, c * KC + g * 32, R.w[c_slot][s]);
 }
 
+// MXFP4 takes the block-scaled MFMA: x as E4M3 hi + lo (mh, ml, ms: A order,
+// E8M0 per 32) against the packed weights and their scale bytes, no decode.
 template <int FMT, int CPW, typename Pre = NoIssue>
 __device__ __forceinline__ void tok_finish(const FfnArgs& a, const int* eslot, const uint16_t* xs,
-                                           f32x4 (&red)[4][4][64], int T, int t, int u,
+                                           const uint8_t* mh, const uint8_t* ml, const uint8_t* ms,
+                                           const uint8_t* mz, f32x4 (&red)[4][4][64], int T, int t,
+                                           int u,
                                            const TokRaw<FMT, CPW>& R, Pre pre = Pre()) {
   const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -444,6 +448,22 @@ __device__ __forceinline__ void tok_finish(const FfnArgs& a, const int* eslot, c
   for (int cs = 0; cs < CPW; ++cs) {
     pre(cs);
     const int c = wave + 4 * cs;
+    if constexpr (FMT == MOE_W_MXFP4) {
+      // row 0 is the token; lanes of rows 1..15 read a zero block (scale 1)
+      const int off = l16 == 0 ? c * KC + g * 32 : -1;
+      const i32x8 ah = *reinterpret_cast<const i32x8*>(off < 0 ? mz : mh + off);
+      const i32x8 al = *reinterpret_cast<const i32x8*>(off < 0 ? mz : ml + off);
+      const int sa = off < 0 ? 127 : ms[c * 4 + g];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint4 q = R.w[cs][s].q[0];
+        const i32x4 b = {(int)q.x, (int)q.y, (int)q.z, (int)q.w};
+        acc[s] = mfma_mx(ah, b, sa, (int)R.w[cs][s].s, acc[s]);
+        acc[s] = mfma_mx(al, b, sa, (int)R.w[cs][s].s, acc[s]);
+        pin(acc[s]);
+      }
+      continue;
+    }
     bf16x8 av[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -495,18 +515,27 @@ __device__ __forceinline__ void tok_finish(const FfnArgs& a, const int* eslot, c
 
 template <int FMT, int CPW, int VPL>
 __global__ __launch_bounds__(256) void dec_gateup_tok_kernel(DecArgs p) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs[kTokMaxH];
+  constexpr bool MX = FMT == MOE_W_MXFP4;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[MX ? 8 : kTokMaxH];
+  __shared__ __attribute__((aligned(32))) uint8_t mx[MX ? 2 * kTokMaxH + kTokMaxH / 32 + 32 : 64];
   __shared__ f32x4 red[4][4][64];
   __shared__ int eslot[kMaxK];
   const FfnArgs& a = p.f;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = p.T, k = a.k, E = a.E, t = blockIdx.x % T;
-  // one round trip: the token's x row and (wave 0) its logits row
-  uint4 xv = uint4{0u, 0u, 0u, 0u};
-  if (tid < a.H / 8) xv = reinterpret_cast<const uint4*>(a.x + (size_t)t * a.H)[tid];
+  uint8_t *mh = mx, *ml = mx + kTokMaxH, *ms = mx + 2 * kTokMaxH;
+  uint8_t* mz = ms + kTokMaxH / 32;  // 32 zero bytes: A rows 1..15
+  if (tid < 8) reinterpret_cast<uint32_t*>(mz)[tid] = 0u;
+  // one round trip: (wave 0) the token's logits row and its x row
   float lv[VPL];
   if (wave == 0) route_load<VPL>(p.logits + (size_t)t * E, E, lane, lv);
-  if (tid < a.H / 8) reinterpret_cast<uint4*>(xs)[tid] = xv;
+  if constexpr (MX) {
+    prep_a_mx<256>(a.x + (size_t)t * a.H, 1, a.H, a.H, mh, ml, ms);
+  } else {
+    uint4 xv = uint4{0u, 0u, 0u, 0u};
+    if (tid < a.H / 8) xv = reinterpret_cast<const uint4*>(a.x + (size_t)t * a.H)[tid];
+    if (tid < a.H / 8) reinterpret_cast<uint4*>(xs)[tid] = xv;
+  }
   if (wave == 0) {
     int id;
     float w;
@@ -526,11 +555,11 @@ __global__ __launch_bounds__(256) void dec_gateup_tok_kernel(DecArgs p) {
 #pragma unroll
     for (int cs = 0; cs < CPW; ++cs) tok_issue_chunk<FMT, CPW>(a, eslot, T, u, cs, ra);
     if (u + G < U) {
-      tok_finish<FMT, CPW>(a, eslot, xs, red, T, t, u, ra,
+      tok_finish<FMT, CPW>(a, eslot, xs, mh, ml, ms, mz, red, T, t, u, ra,
                            [&](int cs) { tok_issue_chunk<FMT, CPW>(a, eslot, T, u + G, cs, rb); });
-      tok_finish<FMT, CPW>(a, eslot, xs, red, T, t, u + G, rb);
+      tok_finish<FMT, CPW>(a, eslot, xs, mh, ml, ms, mz, red, T, t, u + G, rb);
     } else {
-      tok_finish<FMT, CPW>(a, eslot, xs, red, T, t, u, ra);
+      tok_finish<FMT, CPW>(a, eslot, xs, mh, ml, ms, mz, red, T, t, u, ra);
     }
   }
 }
@@ -593,7 +622,7 @@ constexpr int kTokCols = 32;
 
 template <int FMT, int NJ>
 __global__ __launch_bounds__(256) void dec_down_tok_kernel(DecArgs p) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t hs[];  // [k][I + 8]
+  extern __shared__ __attribute__((aligned(32))) uint16_t hs[];  // [k][I + 8]
   __shared__ float yp[kMaxK][kTokCols];
   __shared__ int eid[kMaxK];
   __shared__ float ew[kMaxK];
@@ -606,19 +635,29 @@ __global__ __launch_bounds__(256) void dec_down_tok_kernel(DecArgs p) {
     permute_block(p, reinterpret_cast<int*>(hs));
     return;
   }
-  // one round trip: the token's k h rows (stored by assignment), ids, weights
-  uint4 hv[8];
-  stage_load<256, 8>(hv, a.hbuf + (size_t)t * k * I, I, k, I, 0);
+  constexpr bool MX = FMT == MOE_W_MXFP4;
+  uint8_t* mh = reinterpret_cast<uint8_t*>(hs);  // MXFP4: hi [k][I] | lo [k][I] | scales [k][I/32]
+  uint8_t* ml = mh + (size_t)k * I;
+  uint8_t* ms = ml + (size_t)k * I;
+  uint8_t* mz = ms + (size_t)k * (I / 32);  // 32 zero bytes: A rows 1..15
+  if (MX && tid < 8) reinterpret_cast<uint32_t*>(mz)[tid] = 0u;
+  // one round trip: ids, weights and the token's k h rows (stored by assignment)
   int id_v = 0;
   float w_v = 0.0f;
   if (tid < k) {
     id_v = p.ids[t * k + tid];
     w_v = p.wts[t * k + tid];
   }
-  stage_store<256, 8>(hv, hs, hp, k, I, 0);
-  for (int q0 = 256 * 8; q0 < k * (I / 8); q0 += 256 * 8) {
-    stage_load<256, 8>(hv, a.hbuf + (size_t)t * k * I, I, k, I, q0);
-    stage_store<256, 8>(hv, hs, hp, k, I, q0);
+  if constexpr (MX) {
+    prep_a_mx<256>(a.hbuf + (size_t)t * k * I, k, I, I, mh, ml, ms);
+  } else {
+    uint4 hv[8];
+    stage_load<256, 8>(hv, a.hbuf + (size_t)t * k * I, I, k, I, 0);
+    stage_store<256, 8>(hv, hs, hp, k, I, 0);
+    for (int q0 = 256 * 8; q0 < k * (I / 8); q0 += 256 * 8) {
+      stage_load<256, 8>(hv, a.hbuf + (size_t)t * k * I, I, k, I, q0);
+      stage_store<256, 8>(hv, hs, hp, k, I, q0);
+    }
   }
   if (tid < k) {
     eid[tid] = a.slot_of ? a.slot_of[id_v] : id_v;
@@ -648,6 +687,26 @@ __global__ __launch_bounds__(256) void dec_down_tok_kernel(DecArgs p) {
                           (c0 + u) * KC + g * 32, raw[i][sub][u]);
 #pragma unroll
     for (int i = 0; i < NJ; ++i) {
+      if constexpr (MX) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = c0 + u;
+          // row 0 is the expert's h row; lanes of rows 1..15 read a zero block
+          const int off = l16 == 0 ? jj[i] * I + c * KC + g * 32 : -1;
+          const i32x8 ah = *reinterpret_cast<const i32x8*>(off < 0 ? mz : mh + off);
+          const i32x8 al = *reinterpret_cast<const i32x8*>(off < 0 ? mz : ml + off);
+          const int sa = off < 0 ? 127 : ms[jj[i] * (I / 32) + c * 4 + g];
+#pragma unroll
+          for (int sub = 0; sub < 2; ++sub) {
+            const uint4 q = raw[i][sub][u].q[0];
+            const i32x4 b = {(int)q.x, (int)q.y, (int)q.z, (int)q.w};
+            acc[i][sub] = mfma_mx(ah, b, sa, (int)raw[i][sub][u].s, acc[i][sub]);
+            acc[i][sub] = mfma_mx(al, b, sa, (int)raw[i][sub][u].s, acc[i][sub]);
+            pin(acc[i][sub]);
+          }
+        }
+        continue;
+      }
       const uint16_t* hrow = hs + jj[i] * hp;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -757,7 +816,8 @@ static int launch_down(const DecArgs& p, hipStream_t s) {
 // One workgroup per (token, 32 columns) plus one for the permutation outputs.
 template <int FMT, int NJ>
 static int launch_down_tok(const DecArgs& p, hipStream_t s) {
-  const size_t h_lds = (size_t)p.f.k * (p.f.I + 8) * 2;
+  const size_t h_lds = FMT == MOE_W_MXFP4 ? (size_t)p.f.k * (2 * p.f.I + p.f.I / 32) + 32
+                                           : (size_t)p.f.k * (p.f.I + 8) * 2;
   const size_t perm_lds = ((size_t)5 * p.f.E + kMaxE + 16) * 4;
   const size_t lds = h_lds > perm_lds ? h_lds : perm_lds;
   static size_t granted = 0;

@@ -29,6 +29,106 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 
 // ---------------------------------------------------------------------------
+// Block-scaled MFMA (CDNA4 v_mfma_scale_f32_16x16x128_f8f6f4), A in E4M3 and
+// B in E2M1, one E8M0 scale per 32 consecutive K of each row (A) and column
+// (B).  Operand layouts (checked on the device against a CPU model):
+//  * E2M1 B: lane (g, i) holds column i, K [32g, 32g+32) of the 128-chunk,
+//    low nibble first (the weights' memory order); its scale register holds
+//    that block's E8M0 byte (byte 0 is used).
+//  * E4M3 A: lane (g, i) holds row i, K [16g, 16g+16) in bytes 0..15 and
+//    K [64+16g, 64+16g+16) in bytes 16..31; the scale for row i's 32-block s
+//    comes from lane (s, i).
+//  * C: lane (g, i) element r is C[4g + r][i], as for the other 16x16 shapes.
+// ---------------------------------------------------------------------------
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+
+__device__ __forceinline__ f32x4 mfma_mx(i32x8 a, i32x4 b, int sa, int sb, f32x4 c) {
+  const i32x8 bb = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bb, c, 0, 4, 0, sa, 0, sb);
+}
+
+// Pins an accumulator at this point of the program: an MFMA chain whose result
+// is only read at the end would otherwise be sunk there as a whole, keeping
+// every chunk's operands live at once.
+__device__ __forceinline__ void pin(f32x4& acc) { asm volatile("" : "+v"(acc)); }
+
+// Byte offset of element r of a row in the E4M3 A order (rows of K bytes).
+__device__ __forceinline__ int a_order(int r) {
+  const int rr = r & 127;
+  return (r & ~127) + ((rr & 63) >> 4) * 32 + (rr >> 6) * 16 + (rr & 15);
+}
+
+// Four floats -> E4M3 bytes of their RNE values (hw) and of the residuals (lw).
+__device__ __forceinline__ void e4m3_hi_lo(float a0, float a1, float a2, float a3, int& hw,
+                                           int& lw) {
+  hw = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+  hw = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, hw, true);
+  const float r0 = a0 - __builtin_amdgcn_cvt_f32_fp8(hw, 0);
+  const float r1 = a1 - __builtin_amdgcn_cvt_f32_fp8(hw, 1);
+  const float r2 = a2 - __builtin_amdgcn_cvt_f32_fp8(hw, 2);
+  const float r3 = a3 - __builtin_amdgcn_cvt_f32_fp8(hw, 3);
+  lw = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
+  lw = __builtin_amdgcn_cvt_pk_fp8_f32(r2, r3, lw, true);
+}
+
+// bf16 rows [rows][K] (row pitch src_pitch elements) -> E4M3 hi and lo bytes
+// in A order ([rows][K] each) and one E8M0 scale per 32 consecutive K
+// ([rows][K/32]), by all NT threads.  The block scale 2^e puts the block's
+// largest magnitude in [128, 256); hi = RNE_e4m3(x / 2^e) and lo =
+// RNE_e4m3(x / 2^e - hi), so hi + lo carries the bf16 value (its 8
+// significant bits: hi takes 4, the residual at most 4 more).
+template <int NT>
+__device__ __forceinline__ void prep_a_mx(const uint16_t* __restrict__ src, int rows, int K,
+                                          int src_pitch, uint8_t* hi, uint8_t* lo, uint8_t* sc) {
+  const int per_row = K / 8, n = rows * per_row, tid = threadIdx.x;
+  for (int i0 = 0; i0 < n; i0 += NT * 4) {
+    uint4 v[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int i = i0 + b * NT + tid;
+      v[b] = uint4{0u, 0u, 0u, 0u};
+      if (i < n) {
+        const int row = i / per_row, r = (i - row * per_row) * 8;
+        v[b] = *reinterpret_cast<const uint4*>(src + (size_t)row * src_pitch + r);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int i = i0 + b * NT + tid;
+      const uint32_t w[4] = {v[b].x, v[b].y, v[b].z, v[b].w};
+      float f[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f[2 * q] = __uint_as_float(w[q] << 16);
+        f[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+      }
+      uint32_t am = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t m = __float_as_uint(f[q]) & 0x7fffffffu;
+        am = m > am ? m : am;
+      }
+      // the 4 threads of a 32-block are lanes 4j..4j+3 of one quad
+      am = max(am, (uint32_t)dpp_i32<0xB1>((int)am, (int)am));
+      am = max(am, (uint32_t)dpp_i32<0x4E>((int)am, (int)am));
+      int e = am ? (int)(am >> 23) - 127 - 7 : 0;
+      e = e < -127 ? -127 : e;
+      const float inv = __uint_as_float((uint32_t)(127 - e) << 23);
+      int h0, h1, l0, l1;
+      e4m3_hi_lo(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv, h0, l0);
+      e4m3_hi_lo(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv, h1, l1);
+      if (i < n) {
+        const int row = i / per_row, r = (i - row * per_row) * 8;
+        const size_t o = (size_t)row * K + a_order(r);
+        *reinterpret_cast<uint2*>(hi + o) = uint2{(uint32_t)h0, (uint32_t)h1};
+        *reinterpret_cast<uint2*>(lo + o) = uint2{(uint32_t)l0, (uint32_t)l1};
+        if ((r & 31) == 0) sc[(size_t)row * (K / 32) + r / 32] = (uint8_t)(127 + e);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // weight loads: raw bytes first (so many can be in flight), decode later
 // ---------------------------------------------------------------------------
 template <int FMT>
