@@ -427,6 +427,189 @@ __global__ __launch_bounds__(256) void ffn_down_tile_kernel(FfnArgs a) {
   ffn_tile_body<FMT, false, kPreMSUB, 2>(a);
 }
 
+// ----------------------------------------------------------------------------
+// Prefill grouped GEMM, pipelined.  A block owns BM = 16*MSUB rows of one
+// expert tile and 256 weight rows (4 waves x 4 subtiles of 16; gate/up pairs
+// them as 2 gate + 2 up subtiles per wave, so 128 h-columns per block).  K
+// goes in chunks of 128: the A chunk is staged in LDS (two buffers), the B
+// chunk stays raw in registers (two named buffers used alternately, so no
+// register holding a pending load is copied).  While chunk c is computed the
+// loads of chunk c+1 are in flight; one barrier per chunk.  K/128 must be
+// even (the last prefetch re-reads the last chunk).  Blocks are numbered so
+// that consecutive logical blocks (the column blocks of one tile, which read
+// the same A rows) land on one XCD: hardware block b runs on XCD b % 8.
+// ----------------------------------------------------------------------------
+template <int FMT, bool GATED, int MSUB>
+__device__ __forceinline__ void ffn_pipe_body(const FfnArgs& a) {
+  constexpr int BM = MSUB * 16, NSUB = 4, NH = GATED ? 2 : 4;
+  constexpr int NCOLB = GATED ? 128 : 256;  // output columns per block
+  const int N_out = GATED ? a.I : a.H;
+  const int K = GATED ? a.H : a.I, nch = K / KC;
+  const int nnb = N_out / NCOLB;
+  const int G = (int)gridDim.x, b = (int)blockIdx.x;
+  const int lid = (b & 7) * (G >> 3) + (b >> 3);  // G is a multiple of 8
+  const int tile = lid / nnb, nb = lid - tile * nnb;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
+
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * A_PITCH];
+  __shared__ int src_row[BM];
+  __shared__ TileInfo s_ti;
+  __shared__ int s_valid;
+  if (wave == 0) {
+    TileInfo ti;
+    const bool ok = find_tile<BM>(a.counts, a.offsets, a.E, tile, lane, ti);
+    if (lane == 0) {
+      s_valid = ok;
+      if (ok) s_ti = ti;
+    }
+  }
+  __syncthreads();
+  if (!s_valid) return;
+  const TileInfo ti = s_ti;
+  const int seg0 = ti.seg0, rows = ti.rows;
+  const uint8_t* rec = record_of(a, ti.e);
+  const uint8_t* w = rec + (GATED ? a.off_w13 : a.off_w2);
+  const uint8_t* sc = rec + (GATED ? a.off_w13s : a.off_w2s);
+  // rows past the tile read its first row: valid memory, outputs discarded
+  for (int r = tid; r < BM; r += 256) {
+    const int rr = r < rows ? r : 0;
+    src_row[r] = GATED ? a.sorted_idx[seg0 + rr] / a.k : seg0 + rr;
+  }
+  const int ncol0 = nb * NCOLB + wave * (NH * 16);
+  int brow[NSUB];
+#pragma unroll
+  for (int j = 0; j < NSUB; ++j) {
+    if constexpr (GATED)
+      brow[j] = (j < NH) ? ncol0 + j * 16 + l16 : a.I + ncol0 + (j - NH) * 16 + l16;
+    else
+      brow[j] = ncol0 + j * 16 + l16;
+  }
+  f32x4 acc[MSUB][NSUB];
+#pragma unroll
+  for (int i = 0; i < MSUB; ++i)
+#pragma unroll
+    for (int j = 0; j < NSUB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+
+  const uint16_t* Asrc = GATED ? a.x : a.hbuf;
+  uint4 av[MSUB];  // this thread's share of one A chunk: BM*16 uint4 over 256 threads
+  auto a_issue = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < MSUB; ++i) {
+      const int q = tid + 256 * i, r = q >> 4, col = (q & 15) * 8;
+      av[i] = *reinterpret_cast<const uint4*>(Asrc + (size_t)src_row[r] * K + c * KC + col);
+    }
+  };
+  auto a_store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < MSUB; ++i) {
+      const int q = tid + 256 * i, r = q >> 4, col = (q & 15) * 8;
+      *reinterpret_cast<uint4*>(&As[buf][r * A_PITCH + col]) = av[i];
+    }
+  };
+  auto b_issue = [&](int c, BRaw<FMT> (&r)[NSUB]) {
+#pragma unroll
+    for (int j = 0; j < NSUB; ++j) load_b_raw<FMT>(w, sc, brow[j], K, c * KC + g * 32, r[j]);
+  };
+  // A fragments of the chunk come to registers once; then each B subtile is
+  // decoded right before its MFMAs, so the decode of subtile j+1 can overlap
+  // the MFMAs of subtile j.
+  auto compute = [&](int buf, const BRaw<FMT> (&r)[NSUB]) {
+    const uint16_t* Ab = As[buf];
+    bf16x8 af[MSUB][4];
+#pragma unroll
+    for (int i = 0; i < MSUB; ++i)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        af[i][s] = *reinterpret_cast<const bf16x8*>(&Ab[(i * 16 + l16) * A_PITCH + g * 32 + s * 8]);
+#pragma unroll
+    for (int j = 0; j < NSUB; ++j) {
+      bf16x8 bv[4];
+      decode_b<FMT>(r[j], bv);
+      if constexpr (FMT == MOE_W_FP8_B128) {
+        const float bs = block_scale<FMT>(r[j]);
+#pragma unroll
+        for (int i = 0; i < MSUB; ++i) {
+          f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) t = mfma16(af[i][s], bv[s], t);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(bs, t[q], acc[i][j][q]);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int i = 0; i < MSUB; ++i) acc[i][j] = mfma16(af[i][s], bv[s], acc[i][j]);
+      }
+    }
+  };
+
+  BRaw<FMT> rx[NSUB], ry[NSUB];
+  a_issue(0);
+  b_issue(0, rx);
+  a_store(0);
+  __syncthreads();
+  for (int c = 0; c < nch; c += 2) {
+    a_issue(c + 1);
+    b_issue(c + 1, ry);
+    compute(0, rx);
+    a_store(1);
+    __syncthreads();
+    const int c2 = c + 2 < nch ? c + 2 : nch - 1;
+    a_issue(c2);
+    b_issue(c2, rx);
+    compute(1, ry);
+    a_store(0);  // the last iteration stores a re-read chunk nobody uses
+    __syncthreads();
+  }
+
+  if constexpr (GATED) {
+    float tsg = 1.0f, tsu = 1.0f;
+    if constexpr (FMT == MOE_W_NVFP4) {
+      const float* ts = reinterpret_cast<const float*>(rec + a.off_ts);
+      tsg = ts[0];
+      tsu = ts[1];
+    }
+#pragma unroll
+    for (int i = 0; i < MSUB; ++i)
+#pragma unroll
+      for (int j = 0; j < NH; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = i * 16 + g * 4 + r;
+          if (m < rows) {
+            const float gv = acc[i][j][r] * tsg, uv = acc[i][j + NH][r] * tsu;
+            const float hv = gv / (1.0f + expf(-gv)) * uv;
+            a.hbuf[(size_t)(seg0 + m) * a.I + ncol0 + j * 16 + l16] = f32_to_bf16_rne(hv);
+          }
+        }
+  } else {
+    float tsd = 1.0f;
+    if constexpr (FMT == MOE_W_NVFP4) tsd = reinterpret_cast<const float*>(rec + a.off_ts)[2];
+#pragma unroll
+    for (int i = 0; i < MSUB; ++i)
+#pragma unroll
+      for (int j = 0; j < NSUB; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = i * 16 + g * 4 + r;
+          if (m < rows)
+            a.y_perm[(size_t)(seg0 + m) * a.H + ncol0 + j * 16 + l16] =
+                f32_to_bf16_rne(acc[i][j][r] * tsd);
+        }
+  }
+}
+
+template <int FMT, int MSUB>
+__global__ __launch_bounds__(256) void ffn_gateup_pipe_kernel(FfnArgs a) {
+  ffn_pipe_body<FMT, true, MSUB>(a);
+}
+template <int FMT, int MSUB>
+__global__ __launch_bounds__(256) void ffn_down_pipe_kernel(FfnArgs a) {
+  ffn_pipe_body<FMT, false, MSUB>(a);
+}
+
 // Decode one expert record to fp32 with the same decoders as the GEMMs.
 template <int FMT>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ rec, FfnArgs a,
@@ -485,12 +668,27 @@ static void fill_args(FfnArgs& a, const moe_experts* W, const Layout& L) {
   a.off_ts = L.ts < 0 ? 0 : L.ts;
 }
 
+template <int MSUB, typename K1, typename K2>
+static void launch_pipe(const FfnArgs& a, K1 k1, K2 k2, hipStream_t s) {
+  const int64_t mt = max_tiles_for(a.A, a.E, MSUB * 16);
+  auto pad8 = [](int64_t n) { return (unsigned)((n + 7) / 8 * 8); };
+  k1<<<pad8(mt * (a.I / 128)), 256, 0, s>>>(a);
+  k2<<<pad8(mt * (a.H / 256)), 256, 0, s>>>(a);
+}
+
+// The pipelined prefill kernels need K/128 even for both GEMMs and the
+// column blocks to divide I (128) and H (256).
+static bool pipe_ok(const FfnArgs& a) { return a.H % 256 == 0 && a.I % 256 == 0; }
+
 template <int FMT>
 static void launch_ffn(const FfnArgs& a, bool decode, hipStream_t s) {
   if (decode) {
     const int64_t mt = max_tiles_for(a.A, a.E, 16);
     ffn_gateup_decode_kernel<FMT><<<(unsigned)(mt * (a.I / kGuCols)), 256, 0, s>>>(a);
     ffn_down_decode_kernel<FMT><<<(unsigned)(mt * (a.H / kDnCols)), 256, 0, s>>>(a);
+  } else if (pipe_ok(a)) {
+    // 64-row tiles: 128 rows per wave measured slower (one wave per SIMD)
+    launch_pipe<4>(a, ffn_gateup_pipe_kernel<FMT, 4>, ffn_down_pipe_kernel<FMT, 4>, s);
   } else {
     const int64_t mt = max_tiles_for(a.A, a.E, kPreMSUB * 16);
     ffn_gateup_tile_kernel<FMT><<<(unsigned)(mt * (a.I / 128)), 256, 0, s>>>(a);

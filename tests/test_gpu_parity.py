@@ -252,6 +252,30 @@ def test_layer_small_all_formats(fmt, variant):
     assert err <= TOL
 
 
+# Shapes the pipelined prefill GEMM takes (H and I multiples of 256): 128-row
+# tiles (tokens per expert >= 96 on average) and 64-row tiles, ragged tails,
+# several column blocks, every format.
+PIPE = [(f, T, E) for f in synth.FORMATS for (T, E) in ((300, 4), (170, 12))]
+
+
+@pytest.mark.parametrize("fmt,T,E", PIPE)
+def test_layer_prefill_pipe(fmt, T, E):
+    wl = synth.Workload(f"pipe_{fmt}_{T}", T=T, H=512, E=E, I=768, k=2, fmt=fmt,
+                        seed=90 + T + E, zipf=0.8)
+    flush(f"[layer-pipe] fmt={fmt} T={T} E={E} A/E={T * 2 / E:.0f}")
+    case = Case(wl)
+    layer, y = _run_layer(case, "prefill")
+    y = y.clone()
+    ref = OL.forward(case.logits_np, case.x_np, wl.k, case.oracle_experts())
+    assert np.array_equal(layer.sorted_idx[:wl.T * wl.k].cpu().numpy(), ref["sorted_idx"])
+    assert rel_err(bf16_to_np(layer.y_perm[:wl.T * wl.k]), ref["y_perm"]) <= TOL
+    err = rel_err(bf16_to_np(y), ref["y"])
+    _, y_dec = _run_layer(case, "decode")
+    dif = rel_err(bf16_to_np(y), bf16_to_np(y_dec))
+    flush(f"   rel err {err:.2e}, vs decode kernels {dif:.2e}")
+    assert err <= TOL and dif <= 1e-2
+
+
 @pytest.mark.parametrize("fmt", synth.FORMATS)
 def test_variants_agree_and_deterministic(fmt):
     wl = SMALL[fmt]
