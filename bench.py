@@ -48,7 +48,52 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--variant", default="auto")
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of graph replay")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 64 MiB device copy (for HBM counter calibration)")
     return ap.parse_args()
+
+
+KERNEL_SOURCES = ("decode.hip", "ffn.hip", "ffn_common.h", "moe_internal.h", "route.hip",
+                  "route_common.h", "permute.hip", "combine.hip")
+
+
+def source_hash() -> str:
+    """sha256 over the kernel sources: counter readings are valid only for these bytes."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "moe_expert_ffn_router_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per step from committed rocprofv3 FETCH_SIZE / WRITE_SIZE readings, scaled by
+    the copy-kernel calibration; None when the readings were taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("TRAFFIC "):
+            rec = json.loads(line[len("TRAFFIC "):])
+            if rec.get("source_hash") != source_hash():
+                return None
+            return int(sum(k["fetch_kib"] * 1024 * rec["fetch_scale"] +
+                           k["write_kib"] * 1024 * rec["write_scale"]
+                           for k in rec["kernels"].values()))
+    return None
+
+
+def calibrate_copy():
+    """A plain device copy of known size: the reference for the counters' scale."""
+    import torch
+    n = 64 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": n, "launches": 5}), flush=True)
 
 
 def main():
@@ -57,6 +102,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer has no "
               "multi-GPU path in this build.", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     import torch
 
     import moe_expert_ffn_router_amd as moe
@@ -182,7 +230,11 @@ def main():
         ffn_bytes += wl.T * wl.E * 4 + wl.T * wl.H * 2
         achieved = ffn_bytes / (ffn_ms / 1e3) / 1e9
         roof.update({"achieved": round(achieved, 1), "frac": round(achieved / HBM_PEAK_GBS, 4)})
-    roof.update({"kernel": ("moe_forward_decode (route+permute+gate/up, down+combine)" if whole
+    if whole and use_graph:
+        roof["traffic"] = measured_traffic(wl.name)
+    roof.update({"kernel": ("moe_forward_decode: token-major gate/up with routing + token-major "
+                            "down with combine (2 launches)" if whole and wl.T <= 16 else
+                            "moe_forward_decode (4 launches)" if whole
                             else "moe_expert_ffn (gate/up + down launches)"),
                  "ffn_ms": round(ffn_ms, 5),
                  "timing": ("HIP events around one replay of a graph of the %d launches"
