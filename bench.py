@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of graph replay")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 64 MiB device copy (for HBM counter calibration)")
+    ap.add_argument("--resident", action="store_true",
+                    help="cache workloads: keep every expert in HBM instead of the slot pool")
     return ap.parse_args()
 
 
@@ -111,6 +113,8 @@ def main():
     import synth
 
     wl = synth.WORKLOADS[args.workload]
+    if wl.pool_slots and not args.resident:
+        return bench_cached(args, wl)
     steps_d, warm_d, nb = DEFAULTS[wl.name]
     steps = args.steps if args.steps is not None else steps_d
     warmup = args.warmup if args.warmup is not None else warm_d
@@ -273,6 +277,149 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_cached(args, wl):
+    """The slot-pool workload: experts live in a pinned host bank, a pool of wl.pool_slots HBM
+    slots holds the ones in use, the LRU lookup runs on the host after each routing, misses are
+    copied on a side stream and the FFN reads the pool through the slot table.  One step =
+    route+permute, counts to the host, lookup, fills, expert FFN, combine (eager: the host
+    decision sits in the middle of every step).  Batches rotate over the domain-biased routing
+    distributions, so the pool churns."""
+    import torch
+
+    import moe_expert_ffn_router_amd as moe
+    import synth
+
+    steps_d, warm_d, _ = DEFAULTS[wl.name]
+    nb = wl.batches
+    steps = args.steps if args.steps is not None else steps_d
+    warmup = args.warmup if args.warmup is not None else warm_d
+    dev = torch.device("cuda")
+    lay = synth.record_layout(wl.fmt, wl.H, wl.I)
+    stride, payload = lay["stride"], lay["payload"]
+    E, S = wl.E, wl.pool_slots
+
+    t0 = time.time()
+    bank = torch.empty((E, stride), dtype=torch.uint8, pin_memory=True)
+    for e0 in range(0, E, 16):
+        ids = list(range(e0, min(E, e0 + 16)))
+        bank[e0:e0 + len(ids)].copy_(
+            synth.make_expert_records(wl.fmt, E, wl.H, wl.I, wl.seed, device=dev, experts=ids))
+    pool = torch.empty((S, stride), dtype=torch.uint8, device=dev)
+    table = torch.full((E,), -1, dtype=torch.int32, device=dev)
+    cache = moe.ExpertCache(1, E, S, stride, pool, bank, table)
+    layer = moe.MoELayer(wl.fmt, E, wl.H, wl.I, wl.k, wl.T, stride)
+    pool_W = moe.experts(wl.fmt, E, wl.H, wl.I, pool, stride)
+    logits = [torch.from_numpy(synth.make_logits(wl, b)).to(dev) for b in range(nb)]
+    xs = [torch.from_numpy(synth.make_x(wl, b).view(np.int16)).to(dev).view(torch.bfloat16)
+          for b in range(nb)]
+    side = torch.cuda.Stream()
+    setup_s = time.time() - t0
+
+    def step(i):
+        return layer.forward_cached(logits[i % nb], xs[i % nb], 0, cache, pool_W, table,
+                                    side=side)[1]
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    st0 = cache.stats()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    touched, misses = [], []
+    start.record()
+    for i in range(steps):
+        info = step(warmup + i)
+        touched.append(info["hits"] + info["misses"])
+        misses.append(info["misses"])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    st1 = cache.stats()
+    filled = st1["bytes_filled"] - st0["bytes_filled"]
+
+    # pinned host -> HBM copy rate of this box (the fill path's ceiling)
+    n_copy = min(64, S)
+    h2d = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    h2d[0].record(side)
+    with torch.cuda.stream(side):
+        pool[:n_copy].copy_(bank[:n_copy], non_blocking=True)
+    h2d[1].record(side)
+    torch.cuda.synchronize()
+    h2d_gbs = n_copy * stride / (h2d[0].elapsed_time(h2d[1]) / 1e3) / 1e9
+    # (the cache is not used after this point: the pool is rewritten below)
+
+    # hit path: the expert FFN on the pool with every expert of the last batch resident,
+    # replayed in a graph (slot table: touched expert -> its slot)
+    b = (warmup + steps - 1) % nb
+    layer.route_permute(logits[b])
+    ids_needed = torch.nonzero(layer.counts[:E] > 0).flatten().to(torch.int32)
+    ident = torch.full((E,), 0, dtype=torch.int32, device=dev)
+    ident[ids_needed.long()] = torch.arange(len(ids_needed), dtype=torch.int32, device=dev)
+    for j, e in enumerate(ids_needed.tolist()):
+        pool[j].copy_(bank[e], non_blocking=True)
+    torch.cuda.synchronize()
+    reps = 10
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            layer.expert_ffn(pool_W, xs[b], wl.T, ident)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ffn_ms = e0.elapsed_time(e1) / reps
+    A = wl.T * wl.k
+    n_t = len(ids_needed)
+    ffn_bytes = n_t * payload + wl.T * wl.H * 2 + 2 * A * wl.I * 2 + A * wl.H * 2
+    achieved = ffn_bytes / (ffn_ms / 1e3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "moe_expert_ffn on the slot pool (gate/up + down launches), hit path",
+            "ffn_ms": round(ffn_ms, 5),
+            "timing": f"HIP events around one replay of a graph of {reps} FFN launches",
+            "algorithmic_bytes_per_launch": int(ffn_bytes),
+            "algorithmic_flops_per_launch": int(2.0 * A * 3 * wl.H * wl.I),
+            "touched_experts": n_t}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, bank, None, args.cpu_seconds)
+
+    out = {
+        "metric": "MoE-layer tokens/s at 1 GPU; % HBM roofline (decode), % MFMA peak (prefill)",
+        "value": round(wl.T * steps / (total_ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(total_ms / steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": E, "I": wl.I, "k": wl.k,
+                   "weights": wl.fmt, "global_batch": wl.T, "pool_slots": S,
+                   "domains": wl.domains, "batches_rotated": nb,
+                   "boundary": "route+permute -> counts to host -> expert_cache_lookup -> "
+                               "expert_cache_fill (side stream, pinned bank) -> expert_ffn on "
+                               "the pool via the slot table -> combine; eager",
+                   "parallelism": "none (1 GPU)", "setup_s": round(setup_s, 1)},
+        "cache": {"touched_mean": round(float(np.mean(touched)), 1),
+                  "misses_mean": round(float(np.mean(misses)), 1),
+                  "hit_rate": round(1 - sum(misses) / max(1, sum(touched)), 4),
+                  "bytes_filled": int(filled),
+                  "fill_gb_per_step": round(filled / steps / 1e9, 3),
+                  "pinned_h2d_gbs": round(h2d_gbs, 1)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    cache.close()
 
 
 def cpu_baseline(wl, base_set, shared, budget_s):
