@@ -439,9 +439,10 @@ __global__ __launch_bounds__(256) void ffn_down_tile_kernel(FfnArgs a) {
 // that consecutive logical blocks (the column blocks of one tile, which read
 // the same A rows) land on one XCD: hardware block b runs on XCD b % 8.
 // ----------------------------------------------------------------------------
-template <int FMT, bool GATED, int MSUB>
+template <int FMT, bool GATED, int MSUB, int MH>
 __device__ __forceinline__ void ffn_pipe_body(const FfnArgs& a) {
-  constexpr int BM = MSUB * 16, NSUB = 4, NH = GATED ? 2 : 4;
+  // MH row groups of MSUB*16 rows; 4*MH waves: wave = (row group, column quarter)
+  constexpr int NT = 256 * MH, WM = MSUB * 16, BM = WM * MH, NSUB = 4, NH = GATED ? 2 : 4;
   constexpr int NCOLB = GATED ? 128 : 256;  // output columns per block
   const int N_out = GATED ? a.I : a.H;
   const int K = GATED ? a.H : a.I, nch = K / KC;
@@ -449,13 +450,14 @@ __device__ __forceinline__ void ffn_pipe_body(const FfnArgs& a) {
   const int G = (int)gridDim.x, b = (int)blockIdx.x;
   const int lid = (b & 7) * (G >> 3) + (b >> 3);  // G is a multiple of 8
   const int tile = lid / nnb, nb = lid - tile * nnb;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int wave = (tid >> 6) & 3, mh = tid >> 8;  // column quarter, row group
 
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * A_PITCH];
   __shared__ int src_row[BM];
   __shared__ TileInfo s_ti;
   __shared__ int s_valid;
-  if (wave == 0) {
+  if (tid < 64) {
     TileInfo ti;
     const bool ok = find_tile<BM>(a.counts, a.offsets, a.E, tile, lane, ti);
     if (lane == 0) {
@@ -471,7 +473,7 @@ __device__ __forceinline__ void ffn_pipe_body(const FfnArgs& a) {
   const uint8_t* w = rec + (GATED ? a.off_w13 : a.off_w2);
   const uint8_t* sc = rec + (GATED ? a.off_w13s : a.off_w2s);
   // rows past the tile read its first row: valid memory, outputs discarded
-  for (int r = tid; r < BM; r += 256) {
+  for (int r = tid; r < BM; r += NT) {
     const int rr = r < rows ? r : 0;
     src_row[r] = GATED ? a.sorted_idx[seg0 + rr] / a.k : seg0 + rr;
   }
@@ -492,18 +494,18 @@ __device__ __forceinline__ void ffn_pipe_body(const FfnArgs& a) {
   __syncthreads();
 
   const uint16_t* Asrc = GATED ? a.x : a.hbuf;
-  uint4 av[MSUB];  // this thread's share of one A chunk: BM*16 uint4 over 256 threads
+  uint4 av[MSUB];  // this thread's share of one A chunk: BM*16 uint4 over NT threads
   auto a_issue = [&](int c) {
 #pragma unroll
     for (int i = 0; i < MSUB; ++i) {
-      const int q = tid + 256 * i, r = q >> 4, col = (q & 15) * 8;
+      const int q = tid + NT * i, r = q >> 4, col = (q & 15) * 8;
       av[i] = *reinterpret_cast<const uint4*>(Asrc + (size_t)src_row[r] * K + c * KC + col);
     }
   };
   auto a_store = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < MSUB; ++i) {
-      const int q = tid + 256 * i, r = q >> 4, col = (q & 15) * 8;
+      const int q = tid + NT * i, r = q >> 4, col = (q & 15) * 8;
       *reinterpret_cast<uint4*>(&As[buf][r * A_PITCH + col]) = av[i];
     }
   };
@@ -515,7 +517,7 @@ __device__ __forceinline__ void ffn_pipe_body(const FfnArgs& a) {
   // decoded right before its MFMAs, so the decode of subtile j+1 can overlap
   // the MFMAs of subtile j.
   auto compute = [&](int buf, const BRaw<FMT> (&r)[NSUB]) {
-    const uint16_t* Ab = As[buf];
+    const uint16_t* Ab = As[buf] + mh * WM * A_PITCH;  // this wave's row group
     bf16x8 af[MSUB][4];
 #pragma unroll
     for (int i = 0; i < MSUB; ++i)
@@ -577,7 +579,7 @@ __device__ __forceinline__ void ffn_pipe_body(const FfnArgs& a) {
       for (int j = 0; j < NH; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int m = i * 16 + g * 4 + r;
+          const int m = mh * WM + i * 16 + g * 4 + r;
           if (m < rows) {
             const float gv = acc[i][j][r] * tsg, uv = acc[i][j + NH][r] * tsu;
             const float hv = gv / (1.0f + expf(-gv)) * uv;
@@ -593,7 +595,7 @@ __device__ __forceinline__ void ffn_pipe_body(const FfnArgs& a) {
       for (int j = 0; j < NSUB; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int m = i * 16 + g * 4 + r;
+          const int m = mh * WM + i * 16 + g * 4 + r;
           if (m < rows)
             a.y_perm[(size_t)(seg0 + m) * a.H + ncol0 + j * 16 + l16] =
                 f32_to_bf16_rne(acc[i][j][r] * tsd);
@@ -601,13 +603,13 @@ __device__ __forceinline__ void ffn_pipe_body(const FfnArgs& a) {
   }
 }
 
-template <int FMT, int MSUB>
-__global__ __launch_bounds__(256) void ffn_gateup_pipe_kernel(FfnArgs a) {
-  ffn_pipe_body<FMT, true, MSUB>(a);
+template <int FMT, int MSUB, int MH>
+__global__ __launch_bounds__(256 * MH) void ffn_gateup_pipe_kernel(FfnArgs a) {
+  ffn_pipe_body<FMT, true, MSUB, MH>(a);
 }
-template <int FMT, int MSUB>
-__global__ __launch_bounds__(256) void ffn_down_pipe_kernel(FfnArgs a) {
-  ffn_pipe_body<FMT, false, MSUB>(a);
+template <int FMT, int MSUB, int MH>
+__global__ __launch_bounds__(256 * MH) void ffn_down_pipe_kernel(FfnArgs a) {
+  ffn_pipe_body<FMT, false, MSUB, MH>(a);
 }
 
 // Decode one expert record to fp32 with the same decoders as the GEMMs.
@@ -668,12 +670,12 @@ static void fill_args(FfnArgs& a, const moe_experts* W, const Layout& L) {
   a.off_ts = L.ts < 0 ? 0 : L.ts;
 }
 
-template <int MSUB, typename K1, typename K2>
+template <int MSUB, int MH, typename K1, typename K2>
 static void launch_pipe(const FfnArgs& a, K1 k1, K2 k2, hipStream_t s) {
-  const int64_t mt = max_tiles_for(a.A, a.E, MSUB * 16);
+  const int64_t mt = max_tiles_for(a.A, a.E, MSUB * 16 * MH);
   auto pad8 = [](int64_t n) { return (unsigned)((n + 7) / 8 * 8); };
-  k1<<<pad8(mt * (a.I / 128)), 256, 0, s>>>(a);
-  k2<<<pad8(mt * (a.H / 256)), 256, 0, s>>>(a);
+  k1<<<pad8(mt * (a.I / 128)), 256 * MH, 0, s>>>(a);
+  k2<<<pad8(mt * (a.H / 256)), 256 * MH, 0, s>>>(a);
 }
 
 // The pipelined prefill kernels need K/128 even for both GEMMs and the
@@ -687,8 +689,9 @@ static void launch_ffn(const FfnArgs& a, bool decode, hipStream_t s) {
     ffn_gateup_decode_kernel<FMT><<<(unsigned)(mt * (a.I / kGuCols)), 256, 0, s>>>(a);
     ffn_down_decode_kernel<FMT><<<(unsigned)(mt * (a.H / kDnCols)), 256, 0, s>>>(a);
   } else if (pipe_ok(a)) {
-    // 64-row tiles: 128 rows per wave measured slower (one wave per SIMD)
-    launch_pipe<4>(a, ffn_gateup_pipe_kernel<FMT, 4>, ffn_down_pipe_kernel<FMT, 4>, s);
+    // 64 rows per wave (more needs too many registers for two waves per SIMD);
+    // a 128-row tile over 8 waves (MH = 2) measured slower than 64-row tiles
+    launch_pipe<4, 1>(a, ffn_gateup_pipe_kernel<FMT, 4, 1>, ffn_down_pipe_kernel<FMT, 4, 1>, s);
   } else {
     const int64_t mt = max_tiles_for(a.A, a.E, kPreMSUB * 16);
     ffn_gateup_tile_kernel<FMT><<<(unsigned)(mt * (a.I / 128)), 256, 0, s>>>(a);
