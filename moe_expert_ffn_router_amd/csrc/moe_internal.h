@@ -134,36 +134,31 @@ __device__ __forceinline__ int dpp_i32(int old, int v) {
   return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, BOUND_ZERO);
 }
 
+// Wave maximum / minimum: the DPP source operand's "old" value is the
+// operation's identity, so each step compiles to one v_max/v_min with a DPP
+// modifier (lanes without a source lane keep their value).
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
   int v = (int)x;
   auto mx = [](int a, int b) { return (int)((uint32_t)a > (uint32_t)b ? (uint32_t)a : (uint32_t)b); };
-  v = mx(v, dpp_i32<0xB1>(v, v));         // quad_perm [1,0,3,2]
-  v = mx(v, dpp_i32<0x4E>(v, v));         // quad_perm [2,3,0,1]
-  v = mx(v, dpp_i32<0x141>(v, v));        // row_half_mirror
-  v = mx(v, dpp_i32<0x140>(v, v));        // row_mirror
-  v = mx(v, dpp_i32<0x142, 0xA>(v, v));   // row_bcast15 into rows 1, 3
-  v = mx(v, dpp_i32<0x143, 0xC>(v, v));   // row_bcast31 into rows 2, 3
+  v = mx(v, dpp_i32<0xB1>(0, v));         // quad_perm [1,0,3,2]
+  v = mx(v, dpp_i32<0x4E>(0, v));         // quad_perm [2,3,0,1]
+  v = mx(v, dpp_i32<0x141>(0, v));        // row_half_mirror
+  v = mx(v, dpp_i32<0x140>(0, v));        // row_mirror
+  v = mx(v, dpp_i32<0x142, 0xA>(0, v));   // row_bcast15 into rows 1, 3
+  v = mx(v, dpp_i32<0x143, 0xC>(0, v));   // row_bcast31 into rows 2, 3
   return (uint32_t)__builtin_amdgcn_readlane(v, 63);
 }
 
-// One step of a 64-bit wave maximum: DPP moves both halves, one u64 compare.
-template <int CTRL, int ROW_MASK = 0xF>
-__device__ __forceinline__ uint64_t max64_step(uint64_t x) {
-  const int lo = (int)(uint32_t)x, hi = (int)(uint32_t)(x >> 32);
-  const uint64_t o = ((uint64_t)(uint32_t)dpp_i32<CTRL, ROW_MASK>(hi, hi) << 32) |
-                     (uint32_t)dpp_i32<CTRL, ROW_MASK>(lo, lo);
-  return o > x ? o : x;
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
-  x = max64_step<0xB1>(x);
-  x = max64_step<0x4E>(x);
-  x = max64_step<0x141>(x);
-  x = max64_step<0x140>(x);
-  x = max64_step<0x142, 0xA>(x);
-  x = max64_step<0x143, 0xC>(x);
-  return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 63) << 32) |
-         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 63);
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  int v = (int)x;
+  auto mn = [](int a, int b) { return (int)((uint32_t)a < (uint32_t)b ? (uint32_t)a : (uint32_t)b); };
+  v = mn(v, dpp_i32<0xB1>(-1, v));
+  v = mn(v, dpp_i32<0x4E>(-1, v));
+  v = mn(v, dpp_i32<0x141>(-1, v));
+  v = mn(v, dpp_i32<0x140>(-1, v));
+  v = mn(v, dpp_i32<0x142, 0xA>(-1, v));
+  v = mn(v, dpp_i32<0x143, 0xC>(-1, v));
+  return (uint32_t)__builtin_amdgcn_readlane(v, 63);
 }
 
 // Sum over the wave in a fixed order (identical result in every lane).

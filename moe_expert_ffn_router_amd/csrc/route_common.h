@@ -1,10 +1,12 @@
 // Per-token router top-k shared by the routing kernels: one wavefront routes
 // one token.  Lane l holds logits l, l+64, ... as order-preserving 32-bit keys
-// (-0.0 mapped to +0.0), each packed with its complemented index.  Each of
-// the k rounds takes the lane-local maximum and a DPP wave maximum of the
-// packed values: the largest key, lowest index first among equal keys.  The
-// owner clears the winner; lane j < k keeps round j's winner and finally the
-// softmax over the k selected logits (or the full-softmax value).
+// (-0.0 mapped to +0.0); each lane first sorts its own keys (largest first,
+// lower index first among equal keys).  Each of the k rounds is a 32-bit DPP
+// wave maximum over the lanes' heads; a ballot of the lanes whose head equals
+// it finds the owner (when several lanes tie, a wave minimum of their indices
+// picks the lowest index), and the owner pops its head.  Lane j < k keeps
+// round j's winner and finally the softmax over the k selected logits (or the
+// full-softmax value).
 #pragma once
 
 #include "moe_internal.h"
@@ -33,31 +35,54 @@ __device__ __forceinline__ void route_load(const float* __restrict__ row, int E,
 }
 
 // Top-k of loaded logits with the calling wave; lane j < k returns (id_j, w_j).
-// Each slot is packed as (key << 32 | ~index): one 64-bit wave maximum gives
-// the largest key and, among equal keys, the lowest index; the owning lane
-// clears it with selects (no branches).  Slots past E are 0, below any logit.
+// Slots past E hold key 0 and index 0xffffffff, below every logit.
 template <int VPL>
 __device__ __forceinline__ void route_select(const float (&val)[VPL], int E, int k, int renorm,
                                              int lane, int& my_id, float& my_w) {
+  // lane-local list, sorted by (key desc, index asc): the packed value
+  // (key << 32 | ~index) orders exactly that way
   uint64_t pk[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = lane + 64 * i;
     pk[i] = (e < E) ? ((uint64_t)order_key(val[i]) << 32) | (uint32_t)~e : 0ull;
   }
+#pragma unroll
+  for (int p = 0; p < VPL; ++p)
+#pragma unroll
+    for (int i = p & 1; i + 1 < VPL; i += 2) {
+      const uint64_t hi = pk[i] > pk[i + 1] ? pk[i] : pk[i + 1];
+      const uint64_t lo = pk[i] > pk[i + 1] ? pk[i + 1] : pk[i];
+      pk[i] = hi;
+      pk[i + 1] = lo;
+    }
+  uint32_t key[VPL], idx[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    key[i] = (uint32_t)(pk[i] >> 32);
+    idx[i] = ~(uint32_t)pk[i];
+  }
   my_id = 0;
   float my_val = 0.0f;
   for (int r = 0; r < k; ++r) {
-    uint64_t best = pk[0];
+    const uint32_t top = wave_max_u32(key[0]);
+    const uint64_t tied = __builtin_amdgcn_ballot_w64(key[0] == top);
+    uint32_t win;
+    if (__builtin_popcountll(tied) == 1)
+      win = (uint32_t)__builtin_amdgcn_readlane((int)idx[0], (int)__builtin_ctzll(tied));
+    else
+      win = wave_min_u32(key[0] == top ? idx[0] : 0xffffffffu);
+    const bool pop = lane == (int)(win & 63u);
 #pragma unroll
-    for (int i = 1; i < VPL; ++i) best = pk[i] > best ? pk[i] : best;
-    const uint64_t g = wave_max_u64(best);
-    const int win = (int)~(uint32_t)g;
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) pk[i] = (lane + 64 * i == win) ? 0ull : pk[i];
+    for (int i = 0; i + 1 < VPL; ++i) {
+      key[i] = pop ? key[i + 1] : key[i];
+      idx[i] = pop ? idx[i + 1] : idx[i];
+    }
+    key[VPL - 1] = pop ? 0u : key[VPL - 1];
+    idx[VPL - 1] = pop ? 0xffffffffu : idx[VPL - 1];
     if (lane == r) {
-      my_id = win;
-      my_val = key_value((uint32_t)(g >> 32));
+      my_id = (int)win;
+      my_val = key_value(top);
     }
   }
   const float v0 = __shfl(my_val, 0, 64);

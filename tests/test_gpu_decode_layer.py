@@ -130,6 +130,25 @@ def test_decode_layer_full_workload_and_varying_batch():
         assert err <= TOL, (T, err)
 
 
+def test_decode_layer_routing_ties():
+    """Logits with many exact ties: the token-major kernels route each token
+    themselves and must keep the lowest-index tie-break."""
+    wl = synth.Workload("dec_ties", T=8, H=512, E=256, I=512, k=8, fmt="mxfp4", seed=77)
+    flush("[decode-layer] ties")
+    case = Case(wl)
+    rng = np.random.default_rng(9)
+    lg_np = (rng.integers(-2, 3, size=(wl.T, wl.E)) * 0.5).astype(np.float32)
+    lg = torch.from_numpy(lg_np).to(DEV)
+    layer = _layer(case)
+    W = layer.weights(case.records)
+    sep = _separate(layer, W, lg, case.x)
+    dec = _decode(layer, W, lg, case.x)
+    _same_routing(sep, dec, wl.T, wl.k, wl.E)
+    ref = OL.forward(lg_np, case.x_np, wl.k, case.oracle_experts())
+    assert np.array_equal(dec["ids"][:wl.T * wl.k].cpu().numpy().reshape(wl.T, wl.k), ref["ids"])
+    assert rel_err(bf16_to_np(dec["y"][:wl.T]), ref["y"]) <= TOL
+
+
 def test_decode_layer_slot_table():
     wl = DEC["nvfp4"]
     case = Case(wl)
