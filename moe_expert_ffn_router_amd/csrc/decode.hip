@@ -23,7 +23,6 @@ namespace moe {
 
 constexpr int kDT = 64, kDA = 256, kDTiles = 256;
 constexpr int kTokMaxT = 16, kTokMaxH = 2048;  // token-major path: T <= 16, H <= 2048
-constexpr int kDGuCols = 32;  // gate/up unit: 16 + 16 h-columns (2 gate + 2 up subtiles)
 
 struct DecArgs {
   FfnArgs f;

@@ -612,6 +612,255 @@ __global__ __launch_bounds__(256 * MH) void ffn_down_pipe_kernel(FfnArgs a) {
   ffn_pipe_body<FMT, false, MSUB, MH>(a);
 }
 
+// ----------------------------------------------------------------------------
+// Prefill grouped GEMM on the block-scaled MFMA (MXFP4 and FP8 weights).
+// Same tiling and pipeline as ffn_pipe_body (64 rows x 256 weight rows per
+// block, K chunks of 128, A double-buffered in LDS, B raw in two register
+// buffers; blocks walk super-tiles of 8 m-tiles), but nothing is decoded: the A operand arrives split
+// into E4M3 hi + lo with E8M0 scales (quant_rows_kernel), and each 16x16x128
+// product is two v_mfma_scale_f32_16x16x128_f8f6f4 (hi, lo) on the raw weight
+// bytes — E2M1 with their E8M0 bytes, or E4M3 with scale 1 and the fp32 block
+// scale applied to the chunk's partial sums.
+//   LDS per buffer: hi and lo rows of 128 bytes at a 144-byte pitch (lane
+//   (g, i) reads 32 bytes of row i at 32g: 16 rows land on distinct banks),
+//   and 4 scale bytes per row.
+// ----------------------------------------------------------------------------
+constexpr int QP = KC + 16;  // LDS row pitch of the hi / lo bytes
+constexpr int kSuperM = 8;   // m-tiles per super-tile
+
+template <int FMT>
+struct QRaw {
+  uint4 q[FMT == MOE_W_FP8_B128 ? 2 : 1];
+  uint32_t s;  // MXFP4: E8M0 byte of the lane's 32-block
+  float bs;    // FP8: the 128x128 block scale
+};
+
+template <int FMT, bool GATED>
+__device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
+  static_assert(FMT == MOE_W_MXFP4 || FMT == MOE_W_FP8_B128, "block-scaled formats only");
+  // 4 waves; each owns 4 subtiles of 16 weight rows over all 64 rows
+  constexpr int MSUB = 4, NT = 256, BM = 64, NSUB = 4, NH = GATED ? 2 : 4;
+  constexpr int NCOLB = GATED ? 128 : 256;  // output columns per block
+  const int N_out = GATED ? a.I : a.H;
+  const int K = GATED ? a.H : a.I, nch = K / KC;
+  const int nnb = N_out / NCOLB;
+  const int G = (int)gridDim.x, b = (int)blockIdx.x;
+  const int lid = (b & 7) * (G >> 3) + (b >> 3);  // G is a multiple of 8
+  // super-tiles of kSuperM m-tiles x all column blocks, walked column block
+  // by column block: the blocks one XCD runs at a time share both the A rows
+  // of a few m-tiles and the weights of a few column blocks in its L2
+  const int grp = lid / (kSuperM * nnb), gi = lid - grp * (kSuperM * nnb);
+  const int tile = grp * kSuperM + gi % kSuperM, nb = gi / kSuperM;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
+
+  __shared__ __attribute__((aligned(16))) uint8_t Sh[2][BM * QP];
+  __shared__ __attribute__((aligned(16))) uint8_t Sl[2][BM * QP];
+  __shared__ __attribute__((aligned(16))) uint8_t Ss[2][BM * 4];
+  __shared__ int src_row[BM];
+  __shared__ TileInfo s_ti;
+  __shared__ int s_valid;
+  if (tid < 64) {
+    TileInfo ti;
+    const bool ok = find_tile<BM>(a.counts, a.offsets, a.E, tile, lane, ti);
+    if (lane == 0) {
+      s_valid = ok;
+      if (ok) s_ti = ti;
+    }
+  }
+  __syncthreads();
+  if (!s_valid) return;
+  // the tile is the same for the whole block: keep it in scalar registers
+  const int e = __builtin_amdgcn_readfirstlane(s_ti.e);
+  const int seg0 = __builtin_amdgcn_readfirstlane(s_ti.seg0);
+  const int rows = __builtin_amdgcn_readfirstlane(s_ti.rows);
+  const uint8_t* rec = record_of(a, e);
+  const uint8_t* w = rec + (GATED ? a.off_w13 : a.off_w2);
+  const uint8_t* sc = rec + (GATED ? a.off_w13s : a.off_w2s);
+  // rows past the tile read its first row: valid memory, outputs discarded
+  if (tid < BM) {
+    const int rr = tid < rows ? tid : 0;
+    src_row[tid] = GATED ? a.sorted_idx[seg0 + rr] / a.k : seg0 + rr;
+  }
+  const int ncol0 = nb * NCOLB + wave * (NH * 16);
+  // 32-bit byte offsets from the (scalar) weight and scale bases: a weight
+  // matrix has fewer than 2^32 bytes
+  uint32_t boff[NSUB], soff[NSUB];
+#pragma unroll
+  for (int j = 0; j < NSUB; ++j) {
+    int row;
+    if constexpr (GATED)
+      row = (j < NH) ? ncol0 + j * 16 + l16 : a.I + ncol0 + (j - NH) * 16 + l16;
+    else
+      row = ncol0 + j * 16 + l16;
+    if constexpr (FMT == MOE_W_MXFP4) {
+      boff[j] = (uint32_t)row * (uint32_t)(K / 2) + g * 16;
+      soff[j] = (uint32_t)row * (uint32_t)(K / 32) + g;
+    } else {
+      boff[j] = (uint32_t)row * (uint32_t)K + g * 16;
+      soff[j] = (uint32_t)((row / 128) * (K / 128));
+    }
+  }
+  f32x4 acc[MSUB][NSUB];
+#pragma unroll
+  for (int i = 0; i < MSUB; ++i)
+#pragma unroll
+    for (int j = 0; j < NSUB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+
+  // A chunk: BM rows x (128 hi + 128 lo bytes), two 16-byte pieces of each
+  // per thread, plus one scale dword per row (threads 0..BM-1).  Named
+  // registers (an array here was kept in scratch memory).  32-bit offsets:
+  // the split operands have fewer than 2^32 bytes (checked by the caller).
+  uint4 h0, h1, l0, l1;
+  uint32_t sv = 0;
+  const int KS = K / 32;
+  const int ar0 = tid >> 3, ar1 = (tid + NT) >> 3, acol = (tid & 7) * 16;
+  const uint32_t ao0 = (uint32_t)src_row[ar0] * (uint32_t)K + acol;
+  const uint32_t ao1 = (uint32_t)src_row[ar1] * (uint32_t)K + acol;
+  const uint32_t aos = (uint32_t)src_row[tid < BM ? tid : 0] * (uint32_t)KS;
+  auto a_issue = [&](int c) {
+    const uint32_t cc = (uint32_t)(c * KC);
+    h0 = *reinterpret_cast<const uint4*>(a.aq_hi + (ao0 + cc));
+    l0 = *reinterpret_cast<const uint4*>(a.aq_lo + (ao0 + cc));
+    h1 = *reinterpret_cast<const uint4*>(a.aq_hi + (ao1 + cc));
+    l1 = *reinterpret_cast<const uint4*>(a.aq_lo + (ao1 + cc));
+    if (tid < BM) sv = *reinterpret_cast<const uint32_t*>(a.aq_sc + (aos + (uint32_t)(c * 4)));
+  };
+  auto a_store = [&](int buf) {
+    *reinterpret_cast<uint4*>(&Sh[buf][ar0 * QP + acol]) = h0;
+    *reinterpret_cast<uint4*>(&Sl[buf][ar0 * QP + acol]) = l0;
+    *reinterpret_cast<uint4*>(&Sh[buf][ar1 * QP + acol]) = h1;
+    *reinterpret_cast<uint4*>(&Sl[buf][ar1 * QP + acol]) = l1;
+    if (tid < BM) *reinterpret_cast<uint32_t*>(&Ss[buf][tid * 4]) = sv;
+  };
+  auto b_issue = [&](int c, QRaw<FMT> (&r)[NSUB]) {
+#pragma unroll
+    for (int j = 0; j < NSUB; ++j) {
+      if constexpr (FMT == MOE_W_MXFP4) {
+        r[j].q[0] = *reinterpret_cast<const uint4*>(w + (boff[j] + (uint32_t)(c * (KC / 2))));
+        r[j].s = sc[soff[j] + (uint32_t)(c * 4)];
+      } else {
+        const uint8_t* p = w + (boff[j] + (uint32_t)(c * KC));
+        r[j].q[0] = *reinterpret_cast<const uint4*>(p);
+        r[j].q[1] = *reinterpret_cast<const uint4*>(p + 64);
+        r[j].bs = reinterpret_cast<const float*>(sc)[soff[j] + (uint32_t)c];
+      }
+    }
+  };
+  // one m-subtile's A fragments at a time (hi, lo: 16 registers), the next
+  // subtile's read from LDS while these are used, against the chunk's 4 raw
+  // B subtiles; accumulators pinned after each step
+  auto compute = [&](int buf, const QRaw<FMT> (&r)[NSUB]) {
+    auto frag = [&](int i, i32x8& h, i32x8& l, int& sa) {
+      const int o = (i * 16 + l16) * QP + g * 32;
+      h = *reinterpret_cast<const i32x8*>(&Sh[buf][o]);
+      l = *reinterpret_cast<const i32x8*>(&Sl[buf][o]);
+      sa = Ss[buf][(i * 16 + l16) * 4 + g];
+    };
+    i32x8 ah, al;
+    int sa;
+    frag(0, ah, al, sa);
+#pragma unroll
+    for (int i = 0; i < MSUB; ++i) {
+      i32x8 nh, nl;
+      int ns = 0;
+      if (i + 1 < MSUB) frag(i + 1, nh, nl, ns);
+#pragma unroll
+      for (int j = 0; j < NSUB; ++j) {
+        if constexpr (FMT == MOE_W_MXFP4) {
+          const i32x4 bq = {(int)r[j].q[0].x, (int)r[j].q[0].y, (int)r[j].q[0].z, (int)r[j].q[0].w};
+          acc[i][j] = mfma_mx(ah, bq, sa, (int)r[j].s, acc[i][j]);
+          acc[i][j] = mfma_mx(al, bq, sa, (int)r[j].s, acc[i][j]);
+          pin_a(acc[i][j]);
+        } else {
+          const i32x8 bq = {(int)r[j].q[0].x, (int)r[j].q[0].y, (int)r[j].q[0].z, (int)r[j].q[0].w,
+                            (int)r[j].q[1].x, (int)r[j].q[1].y, (int)r[j].q[1].z, (int)r[j].q[1].w};
+          f32x4 t = mfma_f8(ah, bq, sa, f32x4{0.f, 0.f, 0.f, 0.f});
+          t = mfma_f8(al, bq, sa, t);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[i][j][u] = fmaf(r[j].bs, t[u], acc[i][j][u]);
+          pin(acc[i][j]);  // the block-scale FMA reads it as a VALU operand
+        }
+      }
+      if (i + 1 < MSUB) {
+        ah = nh;
+        al = nl;
+        sa = ns;
+      }
+    }
+  };
+
+  // Chunk c is computed from LDS buffer c % 2 and register buffer rx / ry
+  // while the loads of chunk c+1 are in flight; after the compute its A share
+  // goes to the other LDS buffer; one barrier per chunk.  K/128 is even; the
+  // last prefetch re-reads the last chunk (valid memory, never used).
+  QRaw<FMT> rx[NSUB], ry[NSUB];
+  a_issue(0);
+  b_issue(0, rx);
+  a_store(0);
+  __syncthreads();
+  for (int c = 0; c < nch; c += 2) {
+    a_issue(c + 1);
+    b_issue(c + 1, ry);
+    compute(0, rx);
+    a_store(1);
+    __syncthreads();
+    const int c2 = c + 2 < nch ? c + 2 : nch - 1;
+    a_issue(c2);
+    b_issue(c2, rx);
+    compute(1, ry);
+    a_store(0);
+    __syncthreads();
+  }
+
+  if constexpr (GATED) {
+#pragma unroll
+    for (int i = 0; i < MSUB; ++i)
+#pragma unroll
+      for (int j = 0; j < NH; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = i * 16 + g * 4 + r;
+          if (m < rows) {
+            const float gv = acc[i][j][r], uv = acc[i][j + NH][r];
+            const float hv = gv / (1.0f + expf(-gv)) * uv;
+            a.hbuf[(size_t)(seg0 + m) * a.I + ncol0 + j * 16 + l16] = f32_to_bf16_rne(hv);
+          }
+        }
+  } else {
+#pragma unroll
+    for (int i = 0; i < MSUB; ++i)
+#pragma unroll
+      for (int j = 0; j < NSUB; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = i * 16 + g * 4 + r;
+          if (m < rows)
+            a.y_perm[(size_t)(seg0 + m) * a.H + ncol0 + j * 16 + l16] = f32_to_bf16_rne(acc[i][j][r]);
+        }
+  }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void ffn_gateup_mx_kernel(FfnArgs a) {
+  ffn_mx_pipe_body<FMT, true>(a);
+}
+template <int FMT>
+__global__ __launch_bounds__(256) void ffn_down_mx_kernel(FfnArgs a) {
+  ffn_mx_pipe_body<FMT, false>(a);
+}
+
+// bf16 rows [R][K] -> E4M3 hi / lo (A order) and E8M0 scales per 32 along K;
+// workgroup b converts rows [8b, 8b + 8).
+__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ src, int R,
+                                                         int K, uint8_t* hi, uint8_t* lo,
+                                                         uint8_t* sc) {
+  const int r0 = blockIdx.x * 8, n = min(8, R - r0);
+  if (n <= 0) return;
+  prep_a_mx<256>(src + (size_t)r0 * K, n, K, K, hi + (size_t)r0 * K, lo + (size_t)r0 * K,
+                 sc + (size_t)r0 * (K / 32));
+}
+
 // Decode one expert record to fp32 with the same decoders as the GEMMs.
 template <int FMT>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ rec, FfnArgs a,
@@ -668,6 +917,7 @@ static void fill_args(FfnArgs& a, const moe_experts* W, const Layout& L) {
   a.off_w13 = L.w13; a.off_w13s = L.w13s < 0 ? 0 : L.w13s;
   a.off_w2 = L.w2; a.off_w2s = L.w2s < 0 ? 0 : L.w2s;
   a.off_ts = L.ts < 0 ? 0 : L.ts;
+  a.aq_hi = a.aq_lo = a.aq_sc = nullptr;
 }
 
 template <int MSUB, int MH, typename K1, typename K2>
@@ -682,8 +932,56 @@ static void launch_pipe(const FfnArgs& a, K1 k1, K2 k2, hipStream_t s) {
 // column blocks to divide I (128) and H (256).
 static bool pipe_ok(const FfnArgs& a) { return a.H % 256 == 0 && a.I % 256 == 0; }
 
+static int64_t al256(int64_t n) { return (n + 255) / 256 * 256; }
+
+// Workspace of one moe_expert_ffn call: h (bf16 [A][I]), then for the
+// block-scaled prefill formats the split A operands of both GEMMs: h as
+// hi [A][I], lo [A][I], scales [A][I/32], then x as hi [T][H], lo, scales.
+struct FfnWs {
+  int64_t h, hq_hi, hq_lo, hq_sc, xq_hi, xq_lo, xq_sc, total;
+};
+static bool quantized_prefill_fmt(int fmt) { return fmt == MOE_W_MXFP4 || fmt == MOE_W_FP8_B128; }
+static FfnWs ffn_ws(int fmt, int64_t T, int64_t k, int H, int I) {
+  FfnWs w{};
+  const int64_t A = T * k;
+  int64_t p = 0;
+  w.h = p; p += al256(A * I * 2);
+  if (quantized_prefill_fmt(fmt)) {
+    w.hq_hi = p; p += al256(A * I);
+    w.hq_lo = p; p += al256(A * I);
+    w.hq_sc = p; p += al256(A * I / 32);
+    w.xq_hi = p; p += al256(T * H);
+    w.xq_lo = p; p += al256(T * H);
+    w.xq_sc = p; p += al256(T * H / 32);
+  }
+  w.total = p + 256;
+  return w;
+}
+
 template <int FMT>
 static void launch_ffn(const FfnArgs& a, bool decode, hipStream_t s) {
+  if constexpr (FMT == MOE_W_MXFP4 || FMT == MOE_W_FP8_B128) {
+    const int T = a.A / a.k;
+    // the kernels address the split operands with 32-bit offsets
+    const bool fits = (int64_t)T * a.H < (1ll << 32) && (int64_t)a.A * a.I < (1ll << 32);
+    if (!decode && pipe_ok(a) && fits) {
+      // split x once, gate/up, split h once, down
+      const FfnWs L = ffn_ws(FMT, T, a.k, a.H, a.I);
+      uint8_t* ws = reinterpret_cast<uint8_t*>(a.hbuf);
+      FfnArgs g = a;
+      g.aq_hi = ws + L.xq_hi; g.aq_lo = ws + L.xq_lo; g.aq_sc = ws + L.xq_sc;
+      FfnArgs d = a;
+      d.aq_hi = ws + L.hq_hi; d.aq_lo = ws + L.hq_lo; d.aq_sc = ws + L.hq_sc;
+      const int64_t mt = (max_tiles_for(a.A, a.E, 64) + kSuperM - 1) / kSuperM * kSuperM;
+      quant_rows_kernel<<<(unsigned)((T + 7) / 8), 256, 0, s>>>(
+          a.x, T, a.H, ws + L.xq_hi, ws + L.xq_lo, ws + L.xq_sc);
+      ffn_gateup_mx_kernel<FMT><<<(unsigned)(mt * (a.I / 128)), 256, 0, s>>>(g);
+      quant_rows_kernel<<<(unsigned)((a.A + 7) / 8), 256, 0, s>>>(
+          a.hbuf, a.A, a.I, ws + L.hq_hi, ws + L.hq_lo, ws + L.hq_sc);
+      ffn_down_mx_kernel<FMT><<<(unsigned)(mt * (a.H / 256)), 256, 0, s>>>(d);
+      return;
+    }
+  }
   if (decode) {
     const int64_t mt = max_tiles_for(a.A, a.E, 16);
     ffn_gateup_decode_kernel<FMT><<<(unsigned)(mt * (a.I / kGuCols)), 256, 0, s>>>(a);
@@ -703,11 +1001,10 @@ static void launch_ffn(const FfnArgs& a, bool decode, hipStream_t s) {
 
 using namespace moe;
 
-static size_t ws_h_bytes(int64_t A, int I) { return (size_t)((A * I * 2 + 255) / 256 * 256); }
 
 extern "C" size_t moe_expert_ffn_workspace(const moe_experts* W, int32_t T, int32_t k) {
   if (!W || T < 0 || k < 1 || W->E < 1) return 0;
-  return ws_h_bytes((int64_t)T * k, W->I) + 256;
+  return (size_t)ffn_ws(W->fmt, T, k, W->H, W->I).total;
 }
 
 extern "C" int moe_expert_ffn(const moe_experts* W, const int32_t* slot_of_expert,

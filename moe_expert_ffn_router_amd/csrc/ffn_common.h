@@ -22,6 +22,12 @@ struct FfnArgs {
   const int* sorted_idx;
   uint16_t* hbuf;
   uint16_t* y_perm;
+  // block-scaled prefill: the A operand (x rows for gate/up, h rows for down)
+  // split into E4M3 hi and lo bytes in A order ([rows][K] each) and one E8M0
+  // scale per 32 along K ([rows][K/32])
+  const uint8_t* aq_hi;
+  const uint8_t* aq_lo;
+  const uint8_t* aq_sc;
 };
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -47,10 +53,17 @@ __device__ __forceinline__ f32x4 mfma_mx(i32x8 a, i32x4 b, int sa, int sb, f32x4
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bb, c, 0, 4, 0, sa, 0, sb);
 }
 
+// Both operands E4M3 (same lane layout for B as for A); B's scale is 1.
+__device__ __forceinline__ f32x4 mfma_f8(i32x8 a, i32x8 b, int sa, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, 127);
+}
+
 // Pins an accumulator at this point of the program: an MFMA chain whose result
 // is only read at the end would otherwise be sunk there as a whole, keeping
 // every chunk's operands live at once.
 __device__ __forceinline__ void pin(f32x4& acc) { asm volatile("" : "+v"(acc)); }
+// The same, keeping the accumulator in accumulation registers (AGPRs).
+__device__ __forceinline__ void pin_a(f32x4& acc) { asm volatile("" : "+a"(acc)); }
 
 // Byte offset of element r of a row in the E4M3 A order (rows of K bytes).
 __device__ __forceinline__ int a_order(int r) {
