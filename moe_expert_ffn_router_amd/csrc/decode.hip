@@ -529,7 +529,8 @@ __global__ __launch_bounds__(256) void dec_gateup_tok_kernel(DecArgs p) {
   float lv[VPL];
   if (wave == 0) route_load<VPL>(p.logits + (size_t)t * E, E, lane, lv);
   if constexpr (MX) {
-    prep_a_mx<256>(a.x + (size_t)t * a.H, 1, a.H, a.H, mh, ml, ms);
+    // waves 1..3 split the x row while wave 0 routes
+    if (wave > 0) prep_a_mx<192>(a.x + (size_t)t * a.H, 1, a.H, a.H, mh, ml, ms, tid - 64);
   } else {
     uint4 xv = uint4{0u, 0u, 0u, 0u};
     if (tid < a.H / 8) xv = reinterpret_cast<const uint4*>(a.x + (size_t)t * a.H)[tid];
@@ -623,7 +624,6 @@ template <int FMT, int NJ>
 __global__ __launch_bounds__(256) void dec_down_tok_kernel(DecArgs p) {
   extern __shared__ __attribute__((aligned(32))) uint16_t hs[];  // [k][I + 8]
   __shared__ float yp[kMaxK][kTokCols];
-  __shared__ int eid[kMaxK];
   __shared__ float ew[kMaxK];
   const FfnArgs& a = p.f;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
@@ -640,42 +640,32 @@ __global__ __launch_bounds__(256) void dec_down_tok_kernel(DecArgs p) {
   uint8_t* ms = ml + (size_t)k * I;
   uint8_t* mz = ms + (size_t)k * (I / 32);  // 32 zero bytes: A rows 1..15
   if (MX && tid < 8) reinterpret_cast<uint32_t*>(mz)[tid] = 0u;
-  // one round trip: ids, weights and the token's k h rows (stored by assignment)
-  int id_v = 0;
+  // One round trip for the token's k h rows (stored by assignment; the first
+  // round of them in registers), its ids and weights.  Each wave reads the
+  // ids of its own experts and issues their first weight loads before the h
+  // rows are converted and staged, so the weight stream starts one round trip
+  // after launch; the h loads, issued first, complete first.
+  const uint16_t* hsrc = a.hbuf + (size_t)t * k * I;
+  const int nh = k * (I / 8);
+  uint4 hv[8];
+  if constexpr (MX)
+    prep_a_mx_load<256>(hsrc, k, I, I, 0, tid, *reinterpret_cast<uint4(*)[4]>(hv));
+  else
+    stage_load<256, 8>(hv, hsrc, I, k, I, 0);
   float w_v = 0.0f;
-  if (tid < k) {
-    id_v = p.ids[t * k + tid];
-    w_v = p.wts[t * k + tid];
-  }
-  if constexpr (MX) {
-    prep_a_mx<256>(a.hbuf + (size_t)t * k * I, k, I, I, mh, ml, ms);
-  } else {
-    uint4 hv[8];
-    stage_load<256, 8>(hv, a.hbuf + (size_t)t * k * I, I, k, I, 0);
-    stage_store<256, 8>(hv, hs, hp, k, I, 0);
-    for (int q0 = 256 * 8; q0 < k * (I / 8); q0 += 256 * 8) {
-      stage_load<256, 8>(hv, a.hbuf + (size_t)t * k * I, I, k, I, q0);
-      stage_store<256, 8>(hv, hs, hp, k, I, q0);
-    }
-  }
-  if (tid < k) {
-    eid[tid] = a.slot_of ? a.slot_of[id_v] : id_v;
-    ew[tid] = w_v;
-  }
-  __syncthreads();
+  if (tid < k) w_v = p.wts[t * k + tid];
   const uint8_t* rec[NJ];
   int jj[NJ];
 #pragma unroll
   for (int i = 0; i < NJ; ++i) {
     jj[i] = min(wave + 4 * i, k - 1);
-    rec[i] = a.base + (size_t)eid[jj[i]] * a.stride;
+    const int id = __builtin_amdgcn_readfirstlane(p.ids[t * k + jj[i]]);
+    const int slot = a.slot_of ? __builtin_amdgcn_readfirstlane(a.slot_of[id]) : id;
+    rec[i] = a.base + (size_t)slot * a.stride;
   }
-  f32x4 acc[NJ][2];
-#pragma unroll
-  for (int i = 0; i < NJ; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nchunks = I / KC;
-  for (int c0 = 0; c0 < nchunks; c0 += 4) {
-    BRaw<FMT> raw[NJ][2][4];
+  BRaw<FMT> raw[NJ][2][4];
+  auto issue = [&](int c0) {
 #pragma unroll
     for (int i = 0; i < NJ; ++i)
 #pragma unroll
@@ -684,6 +674,28 @@ __global__ __launch_bounds__(256) void dec_down_tok_kernel(DecArgs p) {
         for (int u = 0; u < 4; ++u)
           load_b_raw<FMT>(rec[i] + a.off_w2, rec[i] + a.off_w2s, cb * kTokCols + sub * 16 + l16, I,
                           (c0 + u) * KC + g * 32, raw[i][sub][u]);
+  };
+  issue(0);
+  if constexpr (MX) {
+    prep_a_mx_store<256>(*reinterpret_cast<const uint4(*)[4]>(hv), k, I, 0, tid, mh, ml, ms);
+    for (int i0 = 256 * 4; i0 < nh; i0 += 256 * 4) {  // k*I > 8192 only
+      uint4 v[4];
+      prep_a_mx_load<256>(hsrc, k, I, I, i0, tid, v);
+      prep_a_mx_store<256>(v, k, I, i0, tid, mh, ml, ms);
+    }
+  } else {
+    stage_store<256, 8>(hv, hs, hp, k, I, 0);
+    for (int q0 = 256 * 8; q0 < nh; q0 += 256 * 8) {
+      stage_load<256, 8>(hv, hsrc, I, k, I, q0);
+      stage_store<256, 8>(hv, hs, hp, k, I, q0);
+    }
+  }
+  if (tid < k) ew[tid] = w_v;
+  __syncthreads();
+  f32x4 acc[NJ][2];
+#pragma unroll
+  for (int i = 0; i < NJ; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0;;) {
 #pragma unroll
     for (int i = 0; i < NJ; ++i) {
       if constexpr (MX) {
@@ -733,6 +745,9 @@ __global__ __launch_bounds__(256) void dec_down_tok_kernel(DecArgs p) {
         }
       }
     }
+    c0 += 4;
+    if (c0 >= nchunks) break;
+    issue(c0);
   }
   // row 0 of each expert's 16x16 result sits in lanes 0..15, element 0
 #pragma unroll

@@ -86,58 +86,76 @@ __device__ __forceinline__ void e4m3_hi_lo(float a0, float a1, float a2, float a
 
 // bf16 rows [rows][K] (row pitch src_pitch elements) -> E4M3 hi and lo bytes
 // in A order ([rows][K] each) and one E8M0 scale per 32 consecutive K
-// ([rows][K/32]), by all NT threads.  The block scale 2^e puts the block's
-// largest magnitude in [128, 256); hi = RNE_e4m3(x / 2^e) and lo =
-// RNE_e4m3(x / 2^e - hi), so hi + lo carries the bf16 value (its 8
-// significant bits: hi takes 4, the residual at most 4 more).
+// ([rows][K/32]), by NT threads (thread index `tid`).  The block scale 2^e
+// puts the block's largest magnitude in [128, 256); hi = RNE_e4m3(x / 2^e)
+// and lo = RNE_e4m3(x / 2^e - hi), so hi + lo carries the bf16 value (its 8
+// significant bits: hi takes 4, the residual at most 4 more).  Work goes in
+// rounds of NT*4 16-byte pieces: prep_a_mx_load issues one round's loads,
+// prep_a_mx_store converts and stores them, so the loads of the first round
+// can be issued early and other loads issued behind them.
+template <int NT>
+__device__ __forceinline__ void prep_a_mx_load(const uint16_t* __restrict__ src, int rows, int K,
+                                               int src_pitch, int i0, int tid, uint4 (&v)[4]) {
+  const int per_row = K / 8, n = rows * per_row;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int i = i0 + b * NT + tid;
+    v[b] = uint4{0u, 0u, 0u, 0u};
+    if (i < n) {
+      const int row = i / per_row, r = (i - row * per_row) * 8;
+      v[b] = *reinterpret_cast<const uint4*>(src + (size_t)row * src_pitch + r);
+    }
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void prep_a_mx_store(const uint4 (&v)[4], int rows, int K, int i0,
+                                                int tid, uint8_t* hi, uint8_t* lo, uint8_t* sc) {
+  const int per_row = K / 8, n = rows * per_row;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int i = i0 + b * NT + tid;
+    const uint32_t w[4] = {v[b].x, v[b].y, v[b].z, v[b].w};
+    float f[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f[2 * q] = __uint_as_float(w[q] << 16);
+      f[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+    }
+    uint32_t am = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t m = __float_as_uint(f[q]) & 0x7fffffffu;
+      am = m > am ? m : am;
+    }
+    // the 4 threads of a 32-block are lanes 4j..4j+3 of one quad
+    am = max(am, (uint32_t)dpp_i32<0xB1>((int)am, (int)am));
+    am = max(am, (uint32_t)dpp_i32<0x4E>((int)am, (int)am));
+    int e = am ? (int)(am >> 23) - 127 - 7 : 0;
+    e = e < -127 ? -127 : e;
+    const float inv = __uint_as_float((uint32_t)(127 - e) << 23);
+    int h0, h1, l0, l1;
+    e4m3_hi_lo(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv, h0, l0);
+    e4m3_hi_lo(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv, h1, l1);
+    if (i < n) {
+      const int row = i / per_row, r = (i - row * per_row) * 8;
+      const size_t o = (size_t)row * K + a_order(r);
+      *reinterpret_cast<uint2*>(hi + o) = uint2{(uint32_t)h0, (uint32_t)h1};
+      *reinterpret_cast<uint2*>(lo + o) = uint2{(uint32_t)l0, (uint32_t)l1};
+      if ((r & 31) == 0) sc[(size_t)row * (K / 32) + r / 32] = (uint8_t)(127 + e);
+    }
+  }
+}
+
 template <int NT>
 __device__ __forceinline__ void prep_a_mx(const uint16_t* __restrict__ src, int rows, int K,
-                                          int src_pitch, uint8_t* hi, uint8_t* lo, uint8_t* sc) {
-  const int per_row = K / 8, n = rows * per_row, tid = threadIdx.x;
+                                          int src_pitch, uint8_t* hi, uint8_t* lo, uint8_t* sc,
+                                          int tid = threadIdx.x) {
+  const int n = rows * (K / 8);
   for (int i0 = 0; i0 < n; i0 += NT * 4) {
     uint4 v[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int i = i0 + b * NT + tid;
-      v[b] = uint4{0u, 0u, 0u, 0u};
-      if (i < n) {
-        const int row = i / per_row, r = (i - row * per_row) * 8;
-        v[b] = *reinterpret_cast<const uint4*>(src + (size_t)row * src_pitch + r);
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int i = i0 + b * NT + tid;
-      const uint32_t w[4] = {v[b].x, v[b].y, v[b].z, v[b].w};
-      float f[8];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        f[2 * q] = __uint_as_float(w[q] << 16);
-        f[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
-      }
-      uint32_t am = 0;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const uint32_t m = __float_as_uint(f[q]) & 0x7fffffffu;
-        am = m > am ? m : am;
-      }
-      // the 4 threads of a 32-block are lanes 4j..4j+3 of one quad
-      am = max(am, (uint32_t)dpp_i32<0xB1>((int)am, (int)am));
-      am = max(am, (uint32_t)dpp_i32<0x4E>((int)am, (int)am));
-      int e = am ? (int)(am >> 23) - 127 - 7 : 0;
-      e = e < -127 ? -127 : e;
-      const float inv = __uint_as_float((uint32_t)(127 - e) << 23);
-      int h0, h1, l0, l1;
-      e4m3_hi_lo(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv, h0, l0);
-      e4m3_hi_lo(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv, h1, l1);
-      if (i < n) {
-        const int row = i / per_row, r = (i - row * per_row) * 8;
-        const size_t o = (size_t)row * K + a_order(r);
-        *reinterpret_cast<uint2*>(hi + o) = uint2{(uint32_t)h0, (uint32_t)h1};
-        *reinterpret_cast<uint2*>(lo + o) = uint2{(uint32_t)l0, (uint32_t)l1};
-        if ((r & 31) == 0) sc[(size_t)row * (K / 32) + r / 32] = (uint8_t)(127 + e);
-      }
-    }
+    prep_a_mx_load<NT>(src, rows, K, src_pitch, i0, tid, v);
+    prep_a_mx_store<NT>(v, rows, K, i0, tid, hi, lo, sc);
   }
 }
 
