@@ -219,8 +219,11 @@ def main():
     t_mean = float(np.mean([touched[b] for b in step_batches]))
     ffn_bytes = t_mean * payload + wl.T * wl.H * 2 + 2 * A * wl.I * 2 + A * wl.H * 2
     ffn_flops = 2.0 * A * 3 * wl.H * wl.I
-    decode = wl.T * wl.k <= 2 * wl.E
-    if decode:
+    # binding roofline: the larger of the HBM floor and the MFMA floor
+    # (bf16 rate: the rate of the instructions the prefill kernels issue)
+    t_hbm = ffn_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = ffn_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    if t_hbm >= t_mfma:
         achieved = ffn_bytes / (ffn_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
