@@ -136,9 +136,14 @@ int moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t k, int3
  *   x_p      = x[sorted_idx[p] / k]                       (bf16 row, H)
  *   h_p      = SiLU(x_p W_gate[e]^T) * (x_p W_up[e]^T)    (I values)
  *   y_perm_p = h_p W_down[e]^T                            (H values, bf16)
- * with SiLU(z) = z / (1 + e^-z), fp32 accumulation, weights decoded exactly
- * (MXFP4, NVFP4 block part and FP8 values are exact in bf16; FP8 block scales
- * and NVFP4 tensor scales are applied to fp32 partial sums).  The activation
+ * with SiLU(z) = z / (1 + e^-z), fp32 accumulation, weights used exactly:
+ * MXFP4 and FP8 weights feed the block-scaled MFMA as stored (prefill) or
+ * decoded to bf16 (decode variants); NVFP4 and BF16 are decoded to bf16 (the
+ * NVFP4 block part is exact in bf16); FP8 block scales and NVFP4 tensor
+ * scales are applied to fp32 partial sums.  For the block-scaled MFMA the
+ * bf16 activations (x, then h) are split into E4M3 hi + lo with one E8M0
+ * scale per 32 (hi + lo equals the bf16 value except for magnitudes below
+ * 2^-9 of the block scale, i.e. ~2^-16 of the block's largest).  The activation
  * is not named on the pages; SwiGLU is the plainest reading for the MoE
  * families the guide lists.
  *   slot_of_expert  device int32 [E] or NULL (identity); only entries of
@@ -150,7 +155,8 @@ int moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t k, int3
  *   variant         0 = choose by size, 1 = small-batch (decode) kernels,
  *                   2 = tiled (prefill) kernels; all give the same result up
  *                   to fp32 summation order
- * ws: device, >= moe_expert_ffn_workspace(W, T, k).                         */
+ * ws: device, >= moe_expert_ffn_workspace(W, T, k): h bf16 [T*k][I], and
+ *     for MXFP4 / FP8 weights the split activations of both GEMMs.          */
 size_t moe_expert_ffn_workspace(const moe_experts* W, int32_t T, int32_t k);
 int moe_expert_ffn(const moe_experts* W, const int32_t* slot_of_expert, const uint16_t* x,
                    int32_t T, int32_t k, const int32_t* counts, const int32_t* offsets,
@@ -170,9 +176,13 @@ int moe_combine(const uint16_t* y_perm, const int32_t* inv_idx, const float* top
                 moe_stream_t stream);
 
 /* ---------------------------------------------------------------------------
- * moe_forward_decode — the whole layer for decode-sized batches in one call
- * (four launches: route + permute in one workgroup; gate/up and down as
- * persistent grids over 16-row expert tiles; combine).  Writes every output
+ * moe_forward_decode — the whole layer for decode-sized batches in one call.
+ * T <= 16 (H <= 2048): two launches, token-major — gate/up workgroups route
+ * their own token (one wave, from the logits) and store h by assignment; the
+ * down workgroups fold in the combine, and one extra workgroup writes the
+ * permutation outputs.  16 < T <= 64: four launches — route + permute in one
+ * workgroup, gate/up and down as persistent grids over 16-row expert tiles,
+ * combine.  Writes every output
  * of moe_route_permute + moe_expert_ffn + moe_combine: topk_ids / topk_w
  * [T][k], counts [E], offsets [E+1], sorted_idx / inv_idx [T*k] (identical
  * to moe_route_permute), y [T][H] (y_shared [T][H] nullable, added with
@@ -180,7 +190,7 @@ int moe_combine(const uint16_t* y_perm, const int32_t* inv_idx, const float* top
  * (the FFN kernels split K their own way; fixed order, so repeat calls give
  * the same bits).  The pages' "graph-compatible execution" (README feature
  * list; fork production configuration, --cuda-graph-max-bs) is served with
- * four graph nodes per layer.  Shapes outside
+ * two (or four) graph nodes per layer.  Shapes outside
  * moe_forward_decode_supported(H, I, T, k) return MOE_ERR_UNSUPPORTED (use
  * the separate calls): T <= 64, T*k <= 256, H and I in {512, 1024, 1536,
  * 2048}, T*(H+8)*2 bytes of x fitting in LDS beside the tile table.
