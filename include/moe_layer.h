@@ -142,8 +142,8 @@ int moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t k, int3
  * NVFP4 block part is exact in bf16); FP8 block scales and NVFP4 tensor
  * scales are applied to fp32 partial sums.  For the block-scaled MFMA the
  * bf16 activations (x, then h) are split into E4M3 hi + lo with one E8M0
- * scale per 32 (hi + lo equals the bf16 value except for magnitudes below
- * 2^-9 of the block scale, i.e. ~2^-16 of the block's largest).  The activation
+ * scale per 32; hi + lo differs from the bf16 value by at most 2^-10 times
+ * the block scale, i.e. less than 2^-17 of the block's largest magnitude.  The activation
  * is not named on the pages; SwiGLU is the plainest reading for the MoE
  * families the guide lists.
  *   slot_of_expert  device int32 [E] or NULL (identity); only entries of
