@@ -252,17 +252,21 @@ def test_layer_small_all_formats(fmt, variant):
     assert err <= TOL
 
 
-# Shapes the pipelined prefill GEMM takes (H and I multiples of 256): 128-row
-# tiles (tokens per expert >= 96 on average) and 64-row tiles, ragged tails,
-# several column blocks, every format.
-PIPE = [(f, T, E) for f in synth.FORMATS for (T, E) in ((300, 4), (170, 12))]
+# Shapes the pipelined prefill GEMMs take (H and I multiples of 256; MXFP4 and
+# FP8 through the block-scaled kernels, BF16 and NVFP4 through the bf16 ones):
+# 64-row tiles with ragged tails, several column blocks, every format; 1200
+# tokens over 16 experts give ~48 tiles, several super-tile groups of 8;
+# H = I = 256 is the shortest K loop (two chunks).
+PIPE = [(f, T, E, H, I) for f in synth.FORMATS
+        for (T, E, H, I) in ((300, 4, 512, 768), (170, 12, 512, 768), (1200, 16, 512, 768),
+                             (200, 4, 256, 256))]
 
 
-@pytest.mark.parametrize("fmt,T,E", PIPE)
-def test_layer_prefill_pipe(fmt, T, E):
-    wl = synth.Workload(f"pipe_{fmt}_{T}", T=T, H=512, E=E, I=768, k=2, fmt=fmt,
+@pytest.mark.parametrize("fmt,T,E,H,I", PIPE)
+def test_layer_prefill_pipe(fmt, T, E, H, I):
+    wl = synth.Workload(f"pipe_{fmt}_{T}", T=T, H=H, E=E, I=I, k=2, fmt=fmt,
                         seed=90 + T + E, zipf=0.8)
-    flush(f"[layer-pipe] fmt={fmt} T={T} E={E} A/E={T * 2 / E:.0f}")
+    flush(f"[layer-pipe] fmt={fmt} T={T} E={E} H={H} I={I} A/E={T * 2 / E:.0f}")
     case = Case(wl)
     layer, y = _run_layer(case, "prefill")
     y = y.clone()
