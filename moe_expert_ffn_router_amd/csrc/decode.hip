@@ -400,13 +400,18 @@ __global__ __launch_bounds__(256) void dec_down_kernel(FfnArgs a) {
 // any other workgroup.  Its units u = b, b + G, ... are (t, expert slot j,
 // 32 h-columns cb) with u = t + T*(j + k*cb); an expert's weights are read
 // once per token that picked it.  The token's x row is row 0 of the MFMA A
-// operand (the other 15 rows are zero); the 4 waves split K as in the tile
-// units and sum their partials in wave order.  h is stored by assignment
-// (t*k + j).  Workgroup t (< T) also writes the token's ids and weights.
+// operand (the other 15 rows are zero); wave w takes the contiguous K chunks
+// [w*CPW, w*CPW + CPW) and the 4 partial sums are added in wave order.  With
+// MXFP4 and four chunks per wave a lane's 16 scale bytes of a weight row
+// (4 chunks x 4 lane groups) come in one load, not one byte per chunk.  h is
+// stored by assignment (t*k + j).  Workgroup t (< T) also writes the token's
+// ids and weights.
 // ----------------------------------------------------------------------------
 template <int FMT, int CPW>
 struct TokRaw {
+  static constexpr bool S4 = FMT == MOE_W_MXFP4 && CPW == 4;  // scales as one uint4 per subtile
   BRaw<FMT> w[CPW][4];
+  uint4 s4[S4 ? 4 : 1];
 };
 
 __device__ __forceinline__ void tok_unit(int u, int T, int k, int& j, int& cb) {
@@ -423,11 +428,21 @@ __device__ __forceinline__ void tok_issue_chunk(const FfnArgs& a, const int* esl
   int j, cb;
   tok_unit(u, T, a.k, j, cb);
   const uint8_t* rec = a.base + (size_t)eslot[j] * a.stride;
-  const int c = wave + 4 * c_slot;
+  const int c = wave * CPW + c_slot;
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
-    load_b_raw<FMT>(rec + a.off_w13, rec + a.off_w13s, (s < 2 ? 0 : a.I) + cb * 32 + (s & 1) * 16 + l16,
-                    a.H, c * KC + g * 32, R.w[c_slot][s]);
+  for (int s = 0; s < 4; ++s) {
+    const int row = (s < 2 ? 0 : a.I) + cb * 32 + (s & 1) * 16 + l16;
+    if constexpr (TokRaw<FMT, CPW>::S4) {
+      R.w[c_slot][s].q[0] = *reinterpret_cast<const uint4*>(
+          rec + a.off_w13 + (((size_t)row * a.H + c * KC + g * 32) >> 1));
+      if (c_slot == 0)  // bytes [16*wave, 16*wave + 16) of the row's scales
+        R.s4[s] = *reinterpret_cast<const uint4*>(rec + a.off_w13s + (size_t)row * (a.H / 32) +
+                                                  wave * 16);
+    } else {
+      load_b_raw<FMT>(rec + a.off_w13, rec + a.off_w13s, row, a.H, c * KC + g * 32,
+                      R.w[c_slot][s]);
+    }
+  }
 }
 
 // MXFP4 takes the block-scaled MFMA: x as E4M3 hi + lo (mh, ml, ms: A order,
@@ -446,7 +461,7 @@ __device__ __forceinline__ void tok_finish(const FfnArgs& a, const int* eslot, c
 #pragma unroll
   for (int cs = 0; cs < CPW; ++cs) {
     pre(cs);
-    const int c = wave + 4 * cs;
+    const int c = wave * CPW + cs;
     if constexpr (FMT == MOE_W_MXFP4) {
       // row 0 is the token; lanes of rows 1..15 read a zero block (scale 1)
       const int off = l16 == 0 ? c * KC + g * 32 : -1;
@@ -457,8 +472,15 @@ __device__ __forceinline__ void tok_finish(const FfnArgs& a, const int* eslot, c
       for (int s = 0; s < 4; ++s) {
         const uint4 q = R.w[cs][s].q[0];
         const i32x4 b = {(int)q.x, (int)q.y, (int)q.z, (int)q.w};
-        acc[s] = mfma_mx(ah, b, sa, (int)R.w[cs][s].s, acc[s]);
-        acc[s] = mfma_mx(al, b, sa, (int)R.w[cs][s].s, acc[s]);
+        int sb;
+        if constexpr (TokRaw<FMT, CPW>::S4) {
+          const uint32_t d = cs == 0 ? R.s4[s].x : cs == 1 ? R.s4[s].y : cs == 2 ? R.s4[s].z : R.s4[s].w;
+          sb = (int)((d >> (8 * g)) & 0xffu);
+        } else {
+          sb = (int)R.w[cs][s].s;
+        }
+        acc[s] = mfma_mx(ah, b, sa, sb, acc[s]);
+        acc[s] = mfma_mx(al, b, sa, sb, acc[s]);
         pin(acc[s]);
       }
       continue;
