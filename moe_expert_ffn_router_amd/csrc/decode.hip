@@ -687,15 +687,28 @@ __global__ __launch_bounds__(256) void dec_down_tok_kernel(DecArgs p) {
   }
   const int nchunks = I / KC;
   BRaw<FMT> raw[NJ][2][4];
+  // MXFP4: a lane's scale bytes of the 4 chunks (4 lane groups each) are 16
+  // consecutive bytes of the row's scales, loaded at once
+  uint4 s4[MX ? NJ : 1][2];
   auto issue = [&](int c0) {
 #pragma unroll
     for (int i = 0; i < NJ; ++i)
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
+      for (int sub = 0; sub < 2; ++sub) {
+        const int row = cb * kTokCols + sub * 16 + l16;
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          load_b_raw<FMT>(rec[i] + a.off_w2, rec[i] + a.off_w2s, cb * kTokCols + sub * 16 + l16, I,
-                          (c0 + u) * KC + g * 32, raw[i][sub][u]);
+        for (int u = 0; u < 4; ++u) {
+          if constexpr (MX)
+            raw[i][sub][u].q[0] = *reinterpret_cast<const uint4*>(
+                rec[i] + a.off_w2 + (((size_t)row * I + (c0 + u) * KC + g * 32) >> 1));
+          else
+            load_b_raw<FMT>(rec[i] + a.off_w2, rec[i] + a.off_w2s, row, I, (c0 + u) * KC + g * 32,
+                            raw[i][sub][u]);
+        }
+        if constexpr (MX)
+          s4[i][sub] = *reinterpret_cast<const uint4*>(rec[i] + a.off_w2s + (size_t)row * (I / 32) +
+                                                       c0 * 4);
+      }
   };
   issue(0);
   if constexpr (MX) {
@@ -733,8 +746,11 @@ __global__ __launch_bounds__(256) void dec_down_tok_kernel(DecArgs p) {
           for (int sub = 0; sub < 2; ++sub) {
             const uint4 q = raw[i][sub][u].q[0];
             const i32x4 b = {(int)q.x, (int)q.y, (int)q.z, (int)q.w};
-            acc[i][sub] = mfma_mx(ah, b, sa, (int)raw[i][sub][u].s, acc[i][sub]);
-            acc[i][sub] = mfma_mx(al, b, sa, (int)raw[i][sub][u].s, acc[i][sub]);
+            const uint4 sv = s4[i][sub];
+            const uint32_t d = u == 0 ? sv.x : u == 1 ? sv.y : u == 2 ? sv.z : sv.w;
+            const int sb = (int)((d >> (8 * g)) & 0xffu);
+            acc[i][sub] = mfma_mx(ah, b, sa, sb, acc[i][sub]);
+            acc[i][sub] = mfma_mx(al, b, sa, sb, acc[i][sub]);
             pin(acc[i][sub]);
           }
         }
