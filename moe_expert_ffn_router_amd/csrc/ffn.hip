@@ -656,6 +656,10 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
   __shared__ __attribute__((aligned(16))) uint8_t Sh[2][BM * QP];
   __shared__ __attribute__((aligned(16))) uint8_t Sl[2][BM * QP];
   __shared__ __attribute__((aligned(16))) uint8_t Ss[2][BM * 4];
+  // MXFP4: the chunk's 4 E8M0 bytes of each of the block's 256 weight rows,
+  // staged with the A chunk (one dword load per thread instead of one byte
+  // load per lane and subtile)
+  __shared__ uint32_t Bs[2][FMT == MOE_W_MXFP4 ? 256 : 1];
   __shared__ int src_row[BM];
   __shared__ TileInfo s_ti;
   __shared__ int s_valid;
@@ -694,11 +698,24 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
       row = ncol0 + j * 16 + l16;
     if constexpr (FMT == MOE_W_MXFP4) {
       boff[j] = (uint32_t)row * (uint32_t)(K / 2) + g * 16;
-      soff[j] = (uint32_t)row * (uint32_t)(K / 32) + g;
+      soff[j] = 0;  // scales come through LDS (Bs)
     } else {
       boff[j] = (uint32_t)row * (uint32_t)K + g * 16;
       soff[j] = (uint32_t)((row / 128) * (K / 128));
     }
+  }
+  // the weight row whose scales thread tid stages: block-local row tid =
+  // (wave tid/64, subtile (tid/16)%4, lane row tid%16)
+  uint32_t bso = 0;
+  if constexpr (FMT == MOE_W_MXFP4) {
+    const int sw = tid >> 6, sj = (tid >> 4) & 3, sl = tid & 15;
+    const int c0 = nb * NCOLB + sw * (NH * 16);
+    int row;
+    if constexpr (GATED)
+      row = (sj < NH) ? c0 + sj * 16 + sl : a.I + c0 + (sj - NH) * 16 + sl;
+    else
+      row = c0 + sj * 16 + sl;
+    bso = (uint32_t)row * (uint32_t)(K / 32);
   }
   f32x4 acc[MSUB][NSUB];
 #pragma unroll
@@ -712,7 +729,7 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
   // registers (an array here was kept in scratch memory).  32-bit offsets:
   // the split operands have fewer than 2^32 bytes (checked by the caller).
   uint4 h0, h1, l0, l1;
-  uint32_t sv = 0;
+  uint32_t sv = 0, bsv = 0;
   const int KS = K / 32;
   const int ar0 = tid >> 3, ar1 = (tid + NT) >> 3, acol = (tid & 7) * 16;
   const uint32_t ao0 = (uint32_t)src_row[ar0] * (uint32_t)K + acol;
@@ -725,6 +742,8 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
     h1 = *reinterpret_cast<const uint4*>(a.aq_hi + (ao1 + cc));
     l1 = *reinterpret_cast<const uint4*>(a.aq_lo + (ao1 + cc));
     if (tid < BM) sv = *reinterpret_cast<const uint32_t*>(a.aq_sc + (aos + (uint32_t)(c * 4)));
+    if constexpr (FMT == MOE_W_MXFP4)
+      bsv = *reinterpret_cast<const uint32_t*>(sc + (bso + (uint32_t)(c * 4)));
   };
   auto a_store = [&](int buf) {
     *reinterpret_cast<uint4*>(&Sh[buf][ar0 * QP + acol]) = h0;
@@ -732,13 +751,13 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
     *reinterpret_cast<uint4*>(&Sh[buf][ar1 * QP + acol]) = h1;
     *reinterpret_cast<uint4*>(&Sl[buf][ar1 * QP + acol]) = l1;
     if (tid < BM) *reinterpret_cast<uint32_t*>(&Ss[buf][tid * 4]) = sv;
+    if constexpr (FMT == MOE_W_MXFP4) Bs[buf][tid] = bsv;
   };
   auto b_issue = [&](int c, QRaw<FMT> (&r)[NSUB]) {
 #pragma unroll
     for (int j = 0; j < NSUB; ++j) {
       if constexpr (FMT == MOE_W_MXFP4) {
         r[j].q[0] = *reinterpret_cast<const uint4*>(w + (boff[j] + (uint32_t)(c * (KC / 2))));
-        r[j].s = sc[soff[j] + (uint32_t)(c * 4)];
       } else {
         const uint8_t* p = w + (boff[j] + (uint32_t)(c * KC));
         r[j].q[0] = *reinterpret_cast<const uint4*>(p);
@@ -760,6 +779,12 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
     i32x8 ah, al;
     int sa;
     frag(0, ah, al, sa);
+    int sbv[NSUB];  // MXFP4: this lane's scale byte of each subtile
+    if constexpr (FMT == MOE_W_MXFP4) {
+#pragma unroll
+      for (int j = 0; j < NSUB; ++j)
+        sbv[j] = reinterpret_cast<const uint8_t*>(Bs[buf])[(wave * 64 + j * 16 + l16) * 4 + g];
+    }
 #pragma unroll
     for (int i = 0; i < MSUB; ++i) {
       i32x8 nh, nl;
@@ -769,8 +794,8 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
       for (int j = 0; j < NSUB; ++j) {
         if constexpr (FMT == MOE_W_MXFP4) {
           const i32x4 bq = {(int)r[j].q[0].x, (int)r[j].q[0].y, (int)r[j].q[0].z, (int)r[j].q[0].w};
-          acc[i][j] = mfma_mx(ah, bq, sa, (int)r[j].s, acc[i][j]);
-          acc[i][j] = mfma_mx(al, bq, sa, (int)r[j].s, acc[i][j]);
+          acc[i][j] = mfma_mx(ah, bq, sa, sbv[j], acc[i][j]);
+          acc[i][j] = mfma_mx(al, bq, sa, sbv[j], acc[i][j]);
           pin_a(acc[i][j]);
         } else {
           const i32x8 bq = {(int)r[j].q[0].x, (int)r[j].q[0].y, (int)r[j].q[0].z, (int)r[j].q[0].w,
