@@ -454,6 +454,11 @@ __device__ __forceinline__ void ffn_pipe_body(const FfnArgs& a) {
   const int wave = (tid >> 6) & 3, mh = tid >> 8;  // column quarter, row group
 
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * A_PITCH];
+  // NVFP4: the chunk's 8 E4M3 block-scale bytes of each of the block's 256
+  // weight rows, staged with the A chunk (one 8-byte load per thread instead
+  // of one 2-byte load per lane and subtile)
+  constexpr bool SNV = FMT == MOE_W_NVFP4 && MH == 1;
+  __shared__ uint2 Bs[2][SNV ? 256 : 1];
   __shared__ int src_row[BM];
   __shared__ TileInfo s_ti;
   __shared__ int s_valid;
@@ -486,6 +491,20 @@ __device__ __forceinline__ void ffn_pipe_body(const FfnArgs& a) {
     else
       brow[j] = ncol0 + j * 16 + l16;
   }
+  // the weight row whose scales thread tid stages: block-local row tid =
+  // (wave tid/64, subtile (tid/16)%4, lane row tid%16)
+  size_t bso = 0;
+  if constexpr (SNV) {
+    const int sw = tid >> 6, sj = (tid >> 4) & 3, sl = tid & 15;
+    const int c0 = nb * NCOLB + sw * (NH * 16);
+    int row;
+    if constexpr (GATED)
+      row = (sj < NH) ? c0 + sj * 16 + sl : a.I + c0 + (sj - NH) * 16 + sl;
+    else
+      row = c0 + sj * 16 + sl;
+    bso = (size_t)row * (K / 16);
+  }
+  uint2 bsv = uint2{0u, 0u};
   f32x4 acc[MSUB][NSUB];
 #pragma unroll
   for (int i = 0; i < MSUB; ++i)
@@ -501,6 +520,7 @@ __device__ __forceinline__ void ffn_pipe_body(const FfnArgs& a) {
       const int q = tid + NT * i, r = q >> 4, col = (q & 15) * 8;
       av[i] = *reinterpret_cast<const uint4*>(Asrc + (size_t)src_row[r] * K + c * KC + col);
     }
+    if constexpr (SNV) bsv = *reinterpret_cast<const uint2*>(sc + bso + (size_t)c * 8);
   };
   auto a_store = [&](int buf) {
 #pragma unroll
@@ -508,10 +528,16 @@ __device__ __forceinline__ void ffn_pipe_body(const FfnArgs& a) {
       const int q = tid + NT * i, r = q >> 4, col = (q & 15) * 8;
       *reinterpret_cast<uint4*>(&As[buf][r * A_PITCH + col]) = av[i];
     }
+    if constexpr (SNV) Bs[buf][tid] = bsv;
   };
   auto b_issue = [&](int c, BRaw<FMT> (&r)[NSUB]) {
 #pragma unroll
-    for (int j = 0; j < NSUB; ++j) load_b_raw<FMT>(w, sc, brow[j], K, c * KC + g * 32, r[j]);
+    for (int j = 0; j < NSUB; ++j) {
+      if constexpr (SNV)  // codes only; the scales come through LDS (Bs)
+        r[j].q[0] = *reinterpret_cast<const uint4*>(w + (((size_t)brow[j] * K + c * KC + g * 32) >> 1));
+      else
+        load_b_raw<FMT>(w, sc, brow[j], K, c * KC + g * 32, r[j]);
+    }
   };
   // A fragments of the chunk come to registers once; then each B subtile is
   // decoded right before its MFMAs, so the decode of subtile j+1 can overlap
@@ -527,7 +553,13 @@ __device__ __forceinline__ void ffn_pipe_body(const FfnArgs& a) {
 #pragma unroll
     for (int j = 0; j < NSUB; ++j) {
       bf16x8 bv[4];
-      decode_b<FMT>(r[j], bv);
+      if constexpr (SNV) {
+        BRaw<FMT> rj = r[j];
+        rj.s = reinterpret_cast<const uint16_t*>(&Bs[buf][wave * 64 + j * 16 + l16])[g];
+        decode_b<FMT>(rj, bv);
+      } else {
+        decode_b<FMT>(r[j], bv);
+      }
       if constexpr (FMT == MOE_W_FP8_B128) {
         const float bs = block_scale<FMT>(r[j]);
 #pragma unroll
