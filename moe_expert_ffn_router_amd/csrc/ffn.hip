@@ -692,6 +692,9 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
   // staged with the A chunk (one dword load per thread instead of one byte
   // load per lane and subtile)
   __shared__ uint32_t Bs[2][FMT == MOE_W_MXFP4 ? 256 : 1];
+  // FP8: the chunk's fp32 block scales of the block's two 128-row weight
+  // blocks (gate and up rows, or the two halves of 256 down rows)
+  __shared__ float Fs[2][2];
   __shared__ int src_row[BM];
   __shared__ TileInfo s_ti;
   __shared__ int s_valid;
@@ -720,7 +723,7 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
   const int ncol0 = nb * NCOLB + wave * (NH * 16);
   // 32-bit byte offsets from the (scalar) weight and scale bases: a weight
   // matrix has fewer than 2^32 bytes
-  uint32_t boff[NSUB], soff[NSUB];
+  uint32_t boff[NSUB];
 #pragma unroll
   for (int j = 0; j < NSUB; ++j) {
     int row;
@@ -728,13 +731,9 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
       row = (j < NH) ? ncol0 + j * 16 + l16 : a.I + ncol0 + (j - NH) * 16 + l16;
     else
       row = ncol0 + j * 16 + l16;
-    if constexpr (FMT == MOE_W_MXFP4) {
-      boff[j] = (uint32_t)row * (uint32_t)(K / 2) + g * 16;
-      soff[j] = 0;  // scales come through LDS (Bs)
-    } else {
-      boff[j] = (uint32_t)row * (uint32_t)K + g * 16;
-      soff[j] = (uint32_t)((row / 128) * (K / 128));
-    }
+    // (the scales come through LDS: Bs, Fs)
+    boff[j] = FMT == MOE_W_MXFP4 ? (uint32_t)row * (uint32_t)(K / 2) + g * 16
+                                 : (uint32_t)row * (uint32_t)K + g * 16;
   }
   // the weight row whose scales thread tid stages: block-local row tid =
   // (wave tid/64, subtile (tid/16)%4, lane row tid%16)
@@ -762,6 +761,10 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
   // the split operands have fewer than 2^32 bytes (checked by the caller).
   uint4 h0, h1, l0, l1;
   uint32_t sv = 0, bsv = 0;
+  float fsv = 0.0f;
+  int fsrow = 0;  // FP8: the 128-row block whose scale thread tid < 2 stages
+  if constexpr (FMT == MOE_W_FP8_B128)
+    fsrow = GATED ? (tid == 0 ? nb : a.I / 128 + nb) : nb * 2 + (tid & 1);
   const int KS = K / 32;
   const int ar0 = tid >> 3, ar1 = (tid + NT) >> 3, acol = (tid & 7) * 16;
   const uint32_t ao0 = (uint32_t)src_row[ar0] * (uint32_t)K + acol;
@@ -776,6 +779,8 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
     if (tid < BM) sv = *reinterpret_cast<const uint32_t*>(a.aq_sc + (aos + (uint32_t)(c * 4)));
     if constexpr (FMT == MOE_W_MXFP4)
       bsv = *reinterpret_cast<const uint32_t*>(sc + (bso + (uint32_t)(c * 4)));
+    if constexpr (FMT == MOE_W_FP8_B128)
+      if (tid < 2) fsv = reinterpret_cast<const float*>(sc)[(size_t)fsrow * (K / 128) + c];
   };
   auto a_store = [&](int buf) {
     *reinterpret_cast<uint4*>(&Sh[buf][ar0 * QP + acol]) = h0;
@@ -784,6 +789,8 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
     *reinterpret_cast<uint4*>(&Sl[buf][ar1 * QP + acol]) = l1;
     if (tid < BM) *reinterpret_cast<uint32_t*>(&Ss[buf][tid * 4]) = sv;
     if constexpr (FMT == MOE_W_MXFP4) Bs[buf][tid] = bsv;
+    if constexpr (FMT == MOE_W_FP8_B128)
+      if (tid < 2) Fs[buf][tid] = fsv;
   };
   auto b_issue = [&](int c, QRaw<FMT> (&r)[NSUB]) {
 #pragma unroll
@@ -794,7 +801,6 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
         const uint8_t* p = w + (boff[j] + (uint32_t)(c * KC));
         r[j].q[0] = *reinterpret_cast<const uint4*>(p);
         r[j].q[1] = *reinterpret_cast<const uint4*>(p + 64);
-        r[j].bs = reinterpret_cast<const float*>(sc)[soff[j] + (uint32_t)c];
       }
     }
   };
@@ -811,6 +817,11 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
     i32x8 ah, al;
     int sa;
     frag(0, ah, al, sa);
+    float fb0 = 0.0f, fb1 = 0.0f;  // FP8: the chunk's two block scales
+    if constexpr (FMT == MOE_W_FP8_B128) {
+      fb0 = Fs[buf][0];
+      fb1 = Fs[buf][1];
+    }
     int sbv[NSUB];  // MXFP4: this lane's scale byte of each subtile
     if constexpr (FMT == MOE_W_MXFP4) {
 #pragma unroll
@@ -834,8 +845,10 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
                             (int)r[j].q[1].x, (int)r[j].q[1].y, (int)r[j].q[1].z, (int)r[j].q[1].w};
           f32x4 t = mfma_f8(ah, bq, sa, f32x4{0.f, 0.f, 0.f, 0.f});
           t = mfma_f8(al, bq, sa, t);
+          // subtile j's 128-row block: gate / up, or the half of the down rows
+          const float bs = (GATED ? j < NH : wave < 2) ? fb0 : fb1;
 #pragma unroll
-          for (int u = 0; u < 4; ++u) acc[i][j][u] = fmaf(r[j].bs, t[u], acc[i][j][u]);
+          for (int u = 0; u < 4; ++u) acc[i][j][u] = fmaf(bs, t[u], acc[i][j][u]);
           pin(acc[i][j]);  // the block-scale FMA reads it as a VALU operand
         }
       }
