@@ -436,9 +436,13 @@ __global__ __launch_bounds__(256) void ffn_down_tile_kernel(FfnArgs a) {
 // register holding a pending load is copied).  While chunk c is computed the
 // loads of chunk c+1 are in flight; one barrier per chunk.  K/128 must be
 // even (the last prefetch re-reads the last chunk).  Blocks are numbered so
-// that consecutive logical blocks (the column blocks of one tile, which read
-// the same A rows) land on one XCD: hardware block b runs on XCD b % 8.
+// that consecutive logical blocks land on one XCD (hardware block b runs on
+// XCD b % 8), and logical blocks walk super-tiles of 8 m-tiles column block
+// by column block: the blocks an XCD runs at a time share the A rows of a few
+// m-tiles and the weights of a few column blocks in its L2.
 // ----------------------------------------------------------------------------
+constexpr int kSuperM = 8;  // m-tiles per super-tile (prefill block order)
+
 template <int FMT, bool GATED, int MSUB, int MH>
 __device__ __forceinline__ void ffn_pipe_body(const FfnArgs& a) {
   // MH row groups of MSUB*16 rows; 4*MH waves: wave = (row group, column quarter)
@@ -449,7 +453,10 @@ __device__ __forceinline__ void ffn_pipe_body(const FfnArgs& a) {
   const int nnb = N_out / NCOLB;
   const int G = (int)gridDim.x, b = (int)blockIdx.x;
   const int lid = (b & 7) * (G >> 3) + (b >> 3);  // G is a multiple of 8
-  const int tile = lid / nnb, nb = lid - tile * nnb;
+  // super-tiles of kSuperM m-tiles, walked column block by column block (as
+  // in the block-scaled kernels)
+  const int grp = lid / (kSuperM * nnb), gi = lid - grp * (kSuperM * nnb);
+  const int tile = grp * kSuperM + gi % kSuperM, nb = gi / kSuperM;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const int wave = (tid >> 6) & 3, mh = tid >> 8;  // column quarter, row group
 
@@ -658,7 +665,6 @@ __global__ __launch_bounds__(256 * MH) void ffn_down_pipe_kernel(FfnArgs a) {
 //   and 4 scale bytes per row.
 // ----------------------------------------------------------------------------
 constexpr int QP = KC + 16;  // LDS row pitch of the hi / lo bytes
-constexpr int kSuperM = 8;   // m-tiles per super-tile
 
 template <int FMT>
 struct QRaw {
@@ -992,10 +998,10 @@ static void fill_args(FfnArgs& a, const moe_experts* W, const Layout& L) {
 
 template <int MSUB, int MH, typename K1, typename K2>
 static void launch_pipe(const FfnArgs& a, K1 k1, K2 k2, hipStream_t s) {
-  const int64_t mt = max_tiles_for(a.A, a.E, MSUB * 16 * MH);
-  auto pad8 = [](int64_t n) { return (unsigned)((n + 7) / 8 * 8); };
-  k1<<<pad8(mt * (a.I / 128)), 256 * MH, 0, s>>>(a);
-  k2<<<pad8(mt * (a.H / 256)), 256 * MH, 0, s>>>(a);
+  // whole super-tiles: the grid is then a multiple of 8 as well
+  const int64_t mt = (max_tiles_for(a.A, a.E, MSUB * 16 * MH) + kSuperM - 1) / kSuperM * kSuperM;
+  k1<<<(unsigned)(mt * (a.I / 128)), 256 * MH, 0, s>>>(a);
+  k2<<<(unsigned)(mt * (a.H / 256)), 256 * MH, 0, s>>>(a);
 }
 
 // The pipelined prefill kernels need K/128 even for both GEMMs and the
