@@ -655,22 +655,25 @@ __global__ __launch_bounds__(256 * MH) void ffn_down_pipe_kernel(FfnArgs a) {
 // Prefill grouped GEMM on the block-scaled MFMA (MXFP4 and FP8 weights).
 // Same tiling and pipeline as ffn_pipe_body (64 rows x 256 weight rows per
 // block, K chunks of 128, A double-buffered in LDS, B raw in two register
-// buffers; blocks walk super-tiles of 8 m-tiles), but nothing is decoded: the A operand arrives split
-// into E4M3 hi + lo with E8M0 scales (quant_rows_kernel), and each 16x16x128
-// product is two v_mfma_scale_f32_16x16x128_f8f6f4 (hi, lo) on the raw weight
-// bytes — E2M1 with their E8M0 bytes, or E4M3 with scale 1 and the fp32 block
-// scale applied to the chunk's partial sums.
+// buffers; blocks walk super-tiles of 8 m-tiles), but nothing is decoded: the
+// A operand arrives split into E4M3 hi + lo with E8M0 scales
+// (quant_rows_kernel), and each 16x16x128 product is two
+// v_mfma_scale_f32_16x16x128_f8f6f4 (hi, lo) on the raw weight bytes — E2M1
+// with their E8M0 bytes, or E4M3 with scale 1 and the fp32 block scale
+// applied to the chunk's partial sums.
 //   LDS per buffer: hi and lo rows of 128 bytes at a 144-byte pitch (lane
 //   (g, i) reads 32 bytes of row i at 32g: 16 rows land on distinct banks),
-//   and 4 scale bytes per row.
+//   4 A-scale bytes per row, and the chunk's weight scales (MXFP4: 4 E8M0
+//   bytes per weight row; FP8: the two fp32 block scales), staged with A.
 // ----------------------------------------------------------------------------
 constexpr int QP = KC + 16;  // LDS row pitch of the hi / lo bytes
 
+// A lane's raw weight bytes of one chunk in the MFMA's B order: E2M1, K
+// [32g, 32g+32) (16 bytes); E4M3, K [16g, 16g+16) and [64+16g, 64+16g+16)
+// (2 x 16 bytes).  Their scales are staged through LDS.
 template <int FMT>
 struct QRaw {
   uint4 q[FMT == MOE_W_FP8_B128 ? 2 : 1];
-  uint32_t s;  // MXFP4: E8M0 byte of the lane's 32-block
-  float bs;    // FP8: the 128x128 block scale
 };
 
 template <int FMT, bool GATED>
