@@ -62,15 +62,13 @@ __device__ __forceinline__ void route_select(const float (&val)[VPL], int E, int
     key[i] = (uint32_t)(pk[i] >> 32);
     idx[i] = ~(uint32_t)pk[i];
   }
-  my_id = 0;
-  float my_val = 0.0f;
+  // round r's winner and its key go to lane r; keys become values after the loop
+  int id_r = 0, key_r = 0;
   for (int r = 0; r < k; ++r) {
     const uint32_t top = wave_max_u32(key[0]);
     const uint64_t tied = __builtin_amdgcn_ballot_w64(key[0] == top);
-    uint32_t win;
-    if (__builtin_popcountll(tied) == 1)
-      win = (uint32_t)__builtin_amdgcn_readlane((int)idx[0], (int)__builtin_ctzll(tied));
-    else
+    uint32_t win = (uint32_t)__builtin_amdgcn_readlane((int)idx[0], (int)__builtin_ctzll(tied));
+    if (__builtin_expect(__builtin_popcountll(tied) != 1, 0))  // equal keys in several lanes
       win = wave_min_u32(key[0] == top ? idx[0] : 0xffffffffu);
     const bool pop = lane == (int)(win & 63u);
 #pragma unroll
@@ -80,11 +78,11 @@ __device__ __forceinline__ void route_select(const float (&val)[VPL], int E, int
     }
     key[VPL - 1] = pop ? 0u : key[VPL - 1];
     idx[VPL - 1] = pop ? 0xffffffffu : idx[VPL - 1];
-    if (lane == r) {
-      my_id = (int)win;
-      my_val = key_value(top);
-    }
+    id_r = lane == r ? (int)win : id_r;
+    key_r = lane == r ? (int)top : key_r;
   }
+  my_id = id_r;
+  const float my_val = key_value((uint32_t)key_r);
   const float v0 = __shfl(my_val, 0, 64);
   const float z = (lane < k) ? expf(my_val - v0) : 0.0f;
   float denom;
