@@ -52,6 +52,8 @@ def parse():
                     help="only run a plain 64 MiB device copy (for HBM counter calibration)")
     ap.add_argument("--resident", action="store_true",
                     help="cache workloads: keep every expert in HBM instead of the slot pool")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="override the workload's batch size T (e.g. a decode batch-size sweep)")
     return ap.parse_args()
 
 
@@ -113,6 +115,8 @@ def main():
     import synth
 
     wl = synth.WORKLOADS[args.workload]
+    if args.tokens is not None:
+        wl = wl.scaled(T=args.tokens)
     if wl.pool_slots and not args.resident:
         return bench_cached(args, wl)
     steps_d, warm_d, nb = DEFAULTS[wl.name]
