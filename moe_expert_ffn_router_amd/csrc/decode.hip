@@ -155,17 +155,21 @@ __device__ __forceinline__ void stage_store(const uint4 (&v)[B], uint16_t* dst, 
 //
 // A unit is one 16-row tile times four 16-column subtiles of the weight
 // matrix: gate/up takes 16 gate + 16 up columns twice (32 h-columns), down
-// takes 64 output columns.  The 4 waves split K: wave w owns the 128-wide
-// chunks w, w+4, ... (CPW of them; K = 512 * CPW).  CPW is a compile-time
-// count, so a load and its use are never guarded by separate runtime branches
-// (which would make the compiler wait for loads still needed later).
+// takes 64 output columns.  The 4 waves split K: wave w owns the contiguous
+// 128-wide chunks [w*CPW, w*CPW + CPW) (K = 512 * CPW).  CPW is a
+// compile-time count, so a load and its use are never guarded by separate
+// runtime branches (which would make the compiler wait for loads still needed
+// later).  With MXFP4 and four chunks per wave a lane's scale bytes of a
+// weight row (4 chunks x 4 lane groups) come in one 16-byte load.
 // ----------------------------------------------------------------------------
 constexpr int MODE_GU = 0, MODE_DN = 1;
 
 template <int FMT, int CPW, int MODE>
 struct UnitRaw {
+  static constexpr bool S4 = FMT == MOE_W_MXFP4 && CPW == 4;  // scales as one uint4 per subtile
   BRaw<FMT> w[CPW][4];                   // [chunk slot][subtile]
   uint4 a[MODE == MODE_DN ? CPW : 1][4];  // down: h row chunk of this lane
+  uint4 s4[S4 ? 4 : 1];
 };
 
 struct UnitPos {
@@ -183,7 +187,7 @@ __device__ __forceinline__ UnitPos unit_pos(const TileTable& L, int unit, int n_
   return q;
 }
 
-// Loads of chunk slot j (K chunk wave + 4j) of a unit.
+// Loads of chunk slot j (K chunk wave*CPW + j) of a unit.
 template <int FMT, int CPW, int MODE>
 __device__ __forceinline__ void unit_issue_chunk(const FfnArgs& a, const TileTable& L,
                                                  const int* sidx, int unit, int n_cb, int j,
@@ -192,7 +196,7 @@ __device__ __forceinline__ void unit_issue_chunk(const FfnArgs& a, const TileTab
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
   const UnitPos q = unit_pos(L, unit, n_cb);
   const uint8_t* rec = tile_record(a, L, q.tile);
-  const int c = wave + 4 * j;
+  const int c = wave * CPW + j;
   if constexpr (MODE == MODE_DN) {
     // h rows (stored by assignment; sidx maps sorted position -> assignment)
     // first: waiting for them never waits for the weights issued after.
@@ -209,7 +213,13 @@ __device__ __forceinline__ void unit_issue_chunk(const FfnArgs& a, const TileTab
   for (int s = 0; s < 4; ++s) {
     const int row = MODE == MODE_GU ? (s < 2 ? 0 : a.I) + q.cb * 32 + (s & 1) * 16 + l16
                                     : q.cb * 64 + s * 16 + l16;
-    load_b_raw<FMT>(w, sc, row, K, c * KC + g * 32, R.w[j][s]);
+    if constexpr (UnitRaw<FMT, CPW, MODE>::S4) {
+      R.w[j][s].q[0] = *reinterpret_cast<const uint4*>(w + (((size_t)row * K + c * KC + g * 32) >> 1));
+      if (j == 0)  // bytes [16*wave, 16*wave + 16) of the row's scales
+        R.s4[s] = *reinterpret_cast<const uint4*>(sc + (size_t)row * (K / 32) + wave * 16);
+    } else {
+      load_b_raw<FMT>(w, sc, row, K, c * KC + g * 32, R.w[j][s]);
+    }
   }
 }
 
@@ -244,7 +254,7 @@ __device__ __forceinline__ void unit_finish(const FfnArgs& a, const TileTable& L
 #pragma unroll
   for (int u = 0; u < CPW; ++u) {
     pre(u);
-    const int c = wave + 4 * u;
+    const int c = wave * CPW + u;
     bf16x8 av[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -258,7 +268,15 @@ __device__ __forceinline__ void unit_finish(const FfnArgs& a, const TileTable& L
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       bf16x8 b[4];
-      decode_b<FMT>(R.w[u][j], b);
+      if constexpr (UnitRaw<FMT, CPW, MODE>::S4) {
+        BRaw<FMT> r = R.w[u][j];
+        const uint4 sv = R.s4[j];
+        const uint32_t d = u == 0 ? sv.x : u == 1 ? sv.y : u == 2 ? sv.z : sv.w;
+        r.s = (d >> (8 * g)) & 0xffu;
+        decode_b<FMT>(r, b);
+      } else {
+        decode_b<FMT>(R.w[u][j], b);
+      }
       if constexpr (FMT == MOE_W_FP8_B128) {
         f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
