@@ -18,7 +18,7 @@ feature list; guide, "how quantizations land" and "CPU layer split"), and keep
 them in a global LRU slot cache keyed by (layer, expert) with the most recent
 active step as recency (guide, "expert bank & LRU slot cache").  The pages give
 no formula for routing, activation or combine; each reading taken here is the
-plainest one and is listed in the design doc.
+plainest one and is stated in the module that takes it.
 
 Parity status per function is stated in each module's header.
 """

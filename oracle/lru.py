@@ -6,7 +6,7 @@ for every (layer, expert), the most recent step in which it was active; misses
 are fetched from a pinned host bank over PCIe (section "MoE strategies",
 offload).  Its "minimum cache constraint" section says too small a cache is
 refused outright.  The pages fix no tie-breaks; the plainest deterministic
-reading, recorded in DESIGN.md, is:
+reading, taken here, is:
 
   state   owner[s] = (layer, expert) or empty, recency[s], a step clock that
           advances once per (layer-)step

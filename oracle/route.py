@@ -3,7 +3,7 @@
 The pages state that each token of an MoE layer activates only a few experts
 (FreeToken supported-models guide, section "MoE strategies"; the aitujian
 feature article speaks of "activated experts") but give no router formula.
-Plainest reading, recorded in the design doc:
+Plainest reading, taken here:
 
   * experts are ordered by (logit descending, expert index ascending), with
     -0.0 equal to +0.0; the first k are the token's experts, in that order;
