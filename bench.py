@@ -104,7 +104,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer has no "
-              "multi-GPU path in this build.", file=sys.stderr)
+              "multi-GPU path (experts and tokens are not sharded).", file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
