@@ -576,24 +576,32 @@ __global__ __launch_bounds__(256) void dec_gateup_tok_kernel(DecArgs p) {
     if (tid < a.H / 8) xv = reinterpret_cast<const uint4*>(a.x + (size_t)t * a.H)[tid];
     if (tid < a.H / 8) reinterpret_cast<uint4*>(xs)[tid] = xv;
   }
+  // Wave 0 runs only the rounds that this workgroup's units need (their
+  // assignment slots j <= jneed) before the weight loads start; workgroup
+  // t < T, which also writes the token's ids and weights, finishes the other
+  // rounds and the softmax while its first loads are in flight.
+  const int U = T * k * (a.I / 32), G = (int)gridDim.x, b = (int)blockIdx.x;
+  int jneed = 0;
+  for (int u = b; u < U; u += G) jneed = max(jneed, (u / T) % k);
+  TopK<VPL> st;
   if (wave == 0) {
-    int id;
-    float w;
-    route_select<VPL>(lv, E, k, p.renorm, lane, id, w);
-    if (lane < k) {
-      eslot[lane] = a.slot_of ? a.slot_of[id] : id;
-      if ((int)blockIdx.x == t) {
-        p.ids[t * k + lane] = id;
+    topk_begin<VPL>(lv, E, lane, st);
+    for (int r = 0; r <= jneed; ++r) topk_round<VPL>(st, r, lane);
+    if (lane <= jneed) eslot[lane] = a.slot_of ? a.slot_of[st.id_r] : st.id_r;
+  }
+  __syncthreads();
+  TokRaw<FMT, CPW> ra, rb;
+  for (int u = b; u < U; u += 2 * G) {
+#pragma unroll
+    for (int cs = 0; cs < CPW; ++cs) tok_issue_chunk<FMT, CPW>(a, eslot, T, u, cs, ra);
+    if (b < T && u == b && wave == 0) {  // b == t
+      for (int r = jneed + 1; r < k; ++r) topk_round<VPL>(st, r, lane);
+      const float w = topk_weight<VPL>(st, lv, E, k, p.renorm, lane);
+      if (lane < k) {
+        p.ids[t * k + lane] = st.id_r;
         p.wts[t * k + lane] = w;
       }
     }
-  }
-  __syncthreads();
-  const int U = T * k * (a.I / 32), G = (int)gridDim.x;
-  TokRaw<FMT, CPW> ra, rb;
-  for (int u = blockIdx.x; u < U; u += 2 * G) {
-#pragma unroll
-    for (int cs = 0; cs < CPW; ++cs) tok_issue_chunk<FMT, CPW>(a, eslot, T, u, cs, ra);
     if (u + G < U) {
       tok_finish<FMT, CPW>(a, eslot, xs, mh, ml, ms, mz, red, T, t, u, ra,
                            [&](int cs) { tok_issue_chunk<FMT, CPW>(a, eslot, T, u + G, cs, rb); });

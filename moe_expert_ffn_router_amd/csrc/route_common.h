@@ -34,13 +34,19 @@ __device__ __forceinline__ void route_load(const float* __restrict__ row, int E,
   }
 }
 
-// Top-k of loaded logits with the calling wave; lane j < k returns (id_j, w_j).
-// Slots past E hold key 0 and index 0xffffffff, below every logit.
+// Lane-local state of one token's top-k selection: the lane's remaining keys
+// and indices, largest first, and round r's winner (index, key) held by lane r.
 template <int VPL>
-__device__ __forceinline__ void route_select(const float (&val)[VPL], int E, int k, int renorm,
-                                             int lane, int& my_id, float& my_w) {
-  // lane-local list, sorted by (key desc, index asc): the packed value
-  // (key << 32 | ~index) orders exactly that way
+struct TopK {
+  uint32_t key[VPL], idx[VPL];
+  int id_r, key_r;
+};
+
+// Sort the lane's own logits by (key desc, index asc): the packed value
+// (key << 32 | ~index) orders exactly that way.  Slots past E hold key 0 and
+// index 0xffffffff, below every logit.
+template <int VPL>
+__device__ __forceinline__ void topk_begin(const float (&val)[VPL], int E, int lane, TopK<VPL>& s) {
   uint64_t pk[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
@@ -56,46 +62,66 @@ __device__ __forceinline__ void route_select(const float (&val)[VPL], int E, int
       pk[i] = hi;
       pk[i + 1] = lo;
     }
-  uint32_t key[VPL], idx[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
-    key[i] = (uint32_t)(pk[i] >> 32);
-    idx[i] = ~(uint32_t)pk[i];
+    s.key[i] = (uint32_t)(pk[i] >> 32);
+    s.idx[i] = ~(uint32_t)pk[i];
   }
-  // round r's winner and its key go to lane r; keys become values after the loop
-  int id_r = 0, key_r = 0;
-  for (int r = 0; r < k; ++r) {
-    const uint32_t top = wave_max_u32(key[0]);
-    const uint64_t tied = __builtin_amdgcn_ballot_w64(key[0] == top);
-    uint32_t win = (uint32_t)__builtin_amdgcn_readlane((int)idx[0], (int)__builtin_ctzll(tied));
-    if (__builtin_expect(__builtin_popcountll(tied) != 1, 0))  // equal keys in several lanes
-      win = wave_min_u32(key[0] == top ? idx[0] : 0xffffffffu);
-    const bool pop = lane == (int)(win & 63u);
+  s.id_r = 0;
+  s.key_r = 0;
+}
+
+// Round r: the largest remaining key over the wave (lowest index among equal
+// keys) is popped from its lane and kept by lane r.
+template <int VPL>
+__device__ __forceinline__ void topk_round(TopK<VPL>& s, int r, int lane) {
+  const uint32_t top = wave_max_u32(s.key[0]);
+  const uint64_t tied = __builtin_amdgcn_ballot_w64(s.key[0] == top);
+  uint32_t win = (uint32_t)__builtin_amdgcn_readlane((int)s.idx[0], (int)__builtin_ctzll(tied));
+  if (__builtin_expect(__builtin_popcountll(tied) != 1, 0))  // equal keys in several lanes
+    win = wave_min_u32(s.key[0] == top ? s.idx[0] : 0xffffffffu);
+  const bool pop = lane == (int)(win & 63u);
 #pragma unroll
-    for (int i = 0; i + 1 < VPL; ++i) {
-      key[i] = pop ? key[i + 1] : key[i];
-      idx[i] = pop ? idx[i + 1] : idx[i];
-    }
-    key[VPL - 1] = pop ? 0u : key[VPL - 1];
-    idx[VPL - 1] = pop ? 0xffffffffu : idx[VPL - 1];
-    id_r = lane == r ? (int)win : id_r;
-    key_r = lane == r ? (int)top : key_r;
+  for (int i = 0; i + 1 < VPL; ++i) {
+    s.key[i] = pop ? s.key[i + 1] : s.key[i];
+    s.idx[i] = pop ? s.idx[i + 1] : s.idx[i];
   }
-  my_id = id_r;
-  const float my_val = key_value((uint32_t)key_r);
+  s.key[VPL - 1] = pop ? 0u : s.key[VPL - 1];
+  s.idx[VPL - 1] = pop ? 0xffffffffu : s.idx[VPL - 1];
+  s.id_r = lane == r ? (int)win : s.id_r;
+  s.key_r = lane == r ? (int)top : s.key_r;
+}
+
+// After k rounds: lane j < k returns w_j, the softmax over the k selected
+// logits (renorm) or the full-softmax value.
+template <int VPL>
+__device__ __forceinline__ float topk_weight(const TopK<VPL>& s, const float (&val)[VPL], int E,
+                                             int k, int renorm, int lane) {
+  const float my_val = key_value((uint32_t)s.key_r);
   const float v0 = __shfl(my_val, 0, 64);
   const float z = (lane < k) ? expf(my_val - v0) : 0.0f;
   float denom;
   if (renorm) {
     denom = wave_sum_f32(z);
   } else {
-    float s = 0.0f;
+    float sum = 0.0f;
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
-      if (lane + 64 * i < E) s += expf(val[i] - v0);
-    denom = wave_sum_f32(s);
+      if (lane + 64 * i < E) sum += expf(val[i] - v0);
+    denom = wave_sum_f32(sum);
   }
-  my_w = z / denom;
+  return z / denom;
+}
+
+// Top-k of loaded logits with the calling wave; lane j < k returns (id_j, w_j).
+template <int VPL>
+__device__ __forceinline__ void route_select(const float (&val)[VPL], int E, int k, int renorm,
+                                             int lane, int& my_id, float& my_w) {
+  TopK<VPL> s;
+  topk_begin<VPL>(val, E, lane, s);
+  for (int r = 0; r < k; ++r) topk_round<VPL>(s, r, lane);
+  my_id = s.id_r;
+  my_w = topk_weight<VPL>(s, val, E, k, renorm, lane);
 }
 
 // Route one token with the calling wave; lane j < k returns (id_j, w_j).
