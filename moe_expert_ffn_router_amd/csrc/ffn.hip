@@ -25,7 +25,9 @@
 //    4 partial sums are added in wave order through LDS (deterministic).
 //    Bandwidth-bound: each touched expert's weights are read once.
 //  * prefill (many rows): m-tile = 64 rows staged in LDS, each wave owns
-//    16 x 4 output columns over the full K.
+//    16 x 4 output columns over the full K.  MXFP4 prefill takes 128-row
+//    tiles on 8 waves whose operands are copied into LDS by the memory path
+//    itself (no registers hold loads in flight), three K chunks deep.
 #include "ffn_common.h"
 
 namespace moe {
@@ -929,6 +931,273 @@ __global__ __launch_bounds__(256) void ffn_down_mx_kernel(FfnArgs a) {
   ffn_mx_pipe_body<FMT, false>(a);
 }
 
+// ---------------------------------------------------------------------------
+// MXFP4 prefill over an LDS-DMA pipeline: a 128-row x 256-weight-row tile on
+// 8 waves (2 row halves x 4 column quarters, 64 x 64 outputs per wave).
+// Every operand byte goes from global memory straight into LDS
+// (global_load_lds_dwordx4: lane l of one instruction writes 16 bytes at
+// base + 16 l), three K chunks deep, so no registers hold loads in flight.
+// Waits are explicit: at chunk c a wave waits for its own copies of chunk c
+// (vmcnt) and for its LDS reads of chunk c-1 (lgkmcnt), then one barrier
+// makes all copies visible and frees chunk c-1's stage for chunk c+2.
+// ---------------------------------------------------------------------------
+constexpr int kDmaBM = 128;
+struct MxDmaStage {
+  uint8_t ah[kDmaBM * 128];  // A hi [row][128 B]: 16-byte unit u stored at u ^ (row & 7)
+  uint8_t al[kDmaBM * 128];  // A lo, same layout
+  uint8_t b[256 * 64];       // weights [row][64 B]: unit u stored at u ^ ((row >> 1) & 3)
+  // scales, the chunk's 4 E8M0 bytes per row, ordered so that a lane's four
+  // subtiles are one 16-byte read: A row (half h, subtile i, l) at
+  // h*64 + 4l + i, weight row (quarter q, subtile j, l) at q*64 + 4l + j
+  __attribute__((aligned(16))) uint32_t as[kDmaBM];
+  __attribute__((aligned(16))) uint32_t bs[256];
+};
+
+// Copies of 16 bytes (4 bytes) per lane from base + off into LDS at lds +
+// 16 * lane (4 * lane).  Issued as inline assembly: the compiler then sees no
+// pending LDS write (it would otherwise wait for every copy in flight before
+// any LDS read it cannot prove disjoint), and every wait on these copies is
+// the explicit one in MOE_DMA_SYNC.  No register receives data (the address
+// registers are read at issue).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, const void* lds) {
+  const uint32_t l = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(off), "s"(base), "s"(l) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const uint8_t* base, uint32_t off, const void* lds) {
+  const uint32_t l = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(off), "s"(base), "s"(l) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// s_waitcnt vmcnt(N) lgkmcnt(0) (expcnt not waited), then a barrier that the
+// compiler moves no memory access across
+#define MOE_DMA_SYNC(N)                                  \
+  do {                                                   \
+    __builtin_amdgcn_s_waitcnt((N) | 0x070);             \
+    asm volatile("s_barrier" ::: "memory");              \
+  } while (0)
+
+template <bool GATED, int WAVES>
+__device__ __forceinline__ void ffn_mx_dma_body(const FfnArgs& a, MxDmaStage& s0, MxDmaStage& s1,
+                                                MxDmaStage& s2) {
+  static_assert(WAVES == 4 || WAVES == 8, "2 row halves x 2 or 4 column groups");
+  constexpr int WN = WAVES / 2;          // column groups
+  constexpr int NSUB = 16 / WN;          // 16-row weight subtiles per wave
+  constexpr int MSUB = 4, NH = GATED ? 2 : 4;
+  constexpr int NCOLB = GATED ? 128 : 256;  // output columns per block
+  constexpr int CPQ = 16 / WAVES;           // 1 KB copies per wave per operand and chunk
+  const int N_out = GATED ? a.I : a.H;
+  const int K = GATED ? a.H : a.I, nch = K / KC, KS = K / 32;
+  const int nnb = N_out / NCOLB;
+  const int G = (int)gridDim.x, b = (int)blockIdx.x;
+  const int lid = (b & 7) * (G >> 3) + (b >> 3);  // G is a multiple of 8
+  const int grp = lid / (kSuperM * nnb), gi = lid - grp * (kSuperM * nnb);
+  const int tile = grp * kSuperM + gi % kSuperM, nb = gi / kSuperM;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int mh = wave / WN, nw = wave % WN;
+
+  __shared__ int src_row[kDmaBM];
+  __shared__ TileInfo s_ti;
+  __shared__ int s_valid;
+  if (tid < 64) {
+    TileInfo ti;
+    const bool ok = find_tile<kDmaBM>(a.counts, a.offsets, a.E, tile, lane, ti);
+    if (lane == 0) {
+      s_valid = ok;
+      if (ok) s_ti = ti;
+    }
+  }
+  __syncthreads();
+  if (!s_valid) return;
+  const int e = __builtin_amdgcn_readfirstlane(s_ti.e);
+  const int seg0 = __builtin_amdgcn_readfirstlane(s_ti.seg0);
+  const int rows = __builtin_amdgcn_readfirstlane(s_ti.rows);
+  const uint8_t* rec = record_of(a, e);
+  const uint8_t* w = rec + (GATED ? a.off_w13 : a.off_w2);
+  const uint8_t* sc = rec + (GATED ? a.off_w13s : a.off_w2s);
+  // rows past the tile read its first row: valid memory, outputs discarded
+  if (tid < kDmaBM) {
+    const int rr = tid < rows ? tid : 0;
+    src_row[tid] = GATED ? a.sorted_idx[seg0 + rr] / a.k : seg0 + rr;
+  }
+  __syncthreads();
+  // weight row of block-local row br = (quarter br/64, subtile (br/16)%4,
+  // br%16); a gated quarter is 32 gate rows then the matching 32 up rows
+  auto wrow = [&](int br) {
+    const int q = br >> 6, j = (br >> 4) & 3, l = br & 15;
+    if constexpr (GATED) {
+      const int c0 = nb * NCOLB + q * (NH * 16);
+      return j < NH ? c0 + j * 16 + l : a.I + c0 + (j - NH) * 16 + l;
+    } else {
+      return nb * NCOLB + br;
+    }
+  };
+  // This wave's copies per chunk: A hi and lo units of rows 8n..8n+7 and the
+  // weights of rows 16n..16n+15 for n = CPQ*wave + q (16 B per lane each);
+  // one dword per lane of weight scales (waves 0-3, quarter = wave) and of A
+  // scales (two waves, half = their index).  32-bit offsets (the caller
+  // checks the sizes).
+  const bool has_as = WAVES == 8 ? (wave == 4 || wave == 5) : wave < 2;
+  const int as_half = WAVES == 8 ? wave - 4 : wave;
+  uint32_t ao[CPQ], wo[CPQ], sob = 0, soa = 0;
+#pragma unroll
+  for (int q = 0; q < CPQ; ++q) {
+    const int n = wave * CPQ + q;
+    const int ar = n * 8 + (lane >> 3);
+    ao[q] = (uint32_t)src_row[ar] * (uint32_t)K + (uint32_t)(((lane & 7) ^ (ar & 7)) * 16);
+    const int br = n * 16 + (lane >> 2);
+    wo[q] = (uint32_t)wrow(br) * (uint32_t)(K / 2) + (uint32_t)(((lane & 3) ^ ((br >> 1) & 3)) * 16);
+  }
+  if (wave < 4) sob = (uint32_t)wrow(wave * 64 + (lane & 3) * 16 + (lane >> 2)) * (uint32_t)KS;
+  if (has_as) soa = (uint32_t)src_row[as_half * 64 + (lane & 3) * 16 + (lane >> 2)] * (uint32_t)KS;
+  auto issue = [&](int c, MxDmaStage& S) {
+    const uint32_t ka = (uint32_t)(c * KC), kb = (uint32_t)(c * (KC / 2)), ks = (uint32_t)(c * 4);
+#pragma unroll
+    for (int q = 0; q < CPQ; ++q) {
+      const int n = wave * CPQ + q;
+      dma16(a.aq_hi, ao[q] + ka, S.ah + n * 1024);
+      dma16(a.aq_lo, ao[q] + ka, S.al + n * 1024);
+      dma16(w, wo[q] + kb, S.b + n * 1024);
+    }
+    if (wave < 4) dma4(sc, sob + ks, S.bs + wave * 64);
+    if (has_as) dma4(a.aq_sc, soa + ks, S.as + as_half * 64);
+  };
+
+  f32x4 acc[MSUB][NSUB];
+#pragma unroll
+  for (int i = 0; i < MSUB; ++i)
+#pragma unroll
+    for (int j = 0; j < NSUB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // the wave's weight subtiles, then its 4 row subtiles (the next one's A
+  // fragments read while the current one's MFMAs run)
+  auto compute = [&](const MxDmaStage& S) {
+    i32x4 bq[NSUB];
+    int sb[NSUB];
+#pragma unroll
+    for (int qq = 0; qq < NSUB / 4; ++qq) {
+      const int quarter = nw * (NSUB / 4) + qq;
+      const uint4 bsv = *reinterpret_cast<const uint4*>(&S.bs[quarter * 64 + l16 * 4]);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = qq * 4 + jj, br = quarter * 64 + jj * 16 + l16;
+        bq[j] = *reinterpret_cast<const i32x4*>(S.b + br * 64 + ((g ^ ((br >> 1) & 3)) * 16));
+        const uint32_t d = jj == 0 ? bsv.x : jj == 1 ? bsv.y : jj == 2 ? bsv.z : bsv.w;
+        sb[j] = (int)((d >> (8 * g)) & 0xffu);
+      }
+    }
+    const uint4 asv = *reinterpret_cast<const uint4*>(&S.as[mh * 64 + l16 * 4]);
+    auto frag = [&](int i, i32x8& h, i32x8& l, int& sa) {
+      const int r = mh * 64 + i * 16 + l16, sw = r & 7;
+      const uint8_t* ph = S.ah + r * 128;
+      const uint8_t* pl = S.al + r * 128;
+      const i32x4 h0 = *reinterpret_cast<const i32x4*>(ph + (((2 * g) ^ sw) * 16));
+      const i32x4 h1 = *reinterpret_cast<const i32x4*>(ph + (((2 * g + 1) ^ sw) * 16));
+      const i32x4 l0 = *reinterpret_cast<const i32x4*>(pl + (((2 * g) ^ sw) * 16));
+      const i32x4 l1 = *reinterpret_cast<const i32x4*>(pl + (((2 * g + 1) ^ sw) * 16));
+      h = i32x8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+      l = i32x8{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+      const uint32_t d = i == 0 ? asv.x : i == 1 ? asv.y : i == 2 ? asv.z : asv.w;
+      sa = (int)((d >> (8 * g)) & 0xffu);
+    };
+    i32x8 ah, al;
+    int sa;
+    frag(0, ah, al, sa);
+#pragma unroll
+    for (int i = 0; i < MSUB; ++i) {
+      i32x8 nh, nl;
+      int ns = 0;
+      if (i + 1 < MSUB) frag(i + 1, nh, nl, ns);
+#pragma unroll
+      for (int j = 0; j < NSUB; ++j) {
+        acc[i][j] = mfma_mx(ah, bq[j], sa, sb[j], acc[i][j]);
+        acc[i][j] = mfma_mx(al, bq[j], sa, sb[j], acc[i][j]);
+      }
+      if (i + 1 < MSUB) {
+        ah = nh;
+        al = nl;
+        sa = ns;
+      }
+    }
+  };
+
+  // K/128 >= 2 (even): chunks 0 and 1 in flight before the loop.  The three
+  // stages are separate LDS objects and each step names its own.
+  constexpr int ND = 3 * CPQ + (WAVES == 4 ? 2 : 1);  // copies per chunk of a full wave
+  const bool short_wave = WAVES == 8 ? wave >= 6 : wave >= 2;  // one scale copy fewer
+  auto step = [&](int c, const MxDmaStage& cur, MxDmaStage& nxt) {
+    if (c + 1 < nch) {
+      if (short_wave)
+        MOE_DMA_SYNC(ND - 1);
+      else
+        MOE_DMA_SYNC(ND);
+    } else {
+      MOE_DMA_SYNC(0);
+    }
+    if (c + 2 < nch) issue(c + 2, nxt);
+    compute(cur);
+  };
+  issue(0, s0);
+  issue(1, s1);
+  for (int c = 0;; c += 3) {
+    step(c, s0, s2);
+    if (c + 1 >= nch) break;
+    step(c + 1, s1, s0);
+    if (c + 2 >= nch) break;
+    step(c + 2, s2, s1);
+    if (c + 3 >= nch) break;
+  }
+
+  const int m_base = mh * 64;
+  if constexpr (GATED) {
+#pragma unroll
+    for (int qq = 0; qq < NSUB / 4; ++qq) {
+      const int c0 = nb * NCOLB + (nw * (NSUB / 4) + qq) * (NH * 16);
+#pragma unroll
+      for (int i = 0; i < MSUB; ++i)
+#pragma unroll
+        for (int jj = 0; jj < NH; ++jj)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = m_base + i * 16 + g * 4 + r;
+            if (m < rows) {
+              const float gv = acc[i][qq * 4 + jj][r], uv = acc[i][qq * 4 + NH + jj][r];
+              const float hv = gv / (1.0f + expf(-gv)) * uv;
+              a.hbuf[(size_t)(seg0 + m) * a.I + c0 + jj * 16 + l16] = f32_to_bf16_rne(hv);
+            }
+          }
+    }
+  } else {
+    const int ncol0 = nb * NCOLB + nw * (NSUB * 16);
+#pragma unroll
+    for (int i = 0; i < MSUB; ++i)
+#pragma unroll
+      for (int j = 0; j < NSUB; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m_base + i * 16 + g * 4 + r;
+          if (m < rows)
+            a.y_perm[(size_t)(seg0 + m) * a.H + ncol0 + j * 16 + l16] = f32_to_bf16_rne(acc[i][j][r]);
+        }
+  }
+}
+
+// 8 waves (two per SIMD); one wave per SIMD with 64 x 128 outputs each
+// measured 15 % slower (its LDS-read and barrier latencies go uncovered)
+constexpr int kDmaWaves = 8;
+__global__ __launch_bounds__(kDmaWaves * 64) void ffn_gateup_mxd_kernel(FfnArgs a) {
+  __shared__ MxDmaStage s0, s1, s2;
+  ffn_mx_dma_body<true, kDmaWaves>(a, s0, s1, s2);
+}
+__global__ __launch_bounds__(kDmaWaves * 64) void ffn_down_mxd_kernel(FfnArgs a) {
+  __shared__ MxDmaStage s0, s1, s2;
+  ffn_mx_dma_body<false, kDmaWaves>(a, s0, s1, s2);
+}
+
 // bf16 rows [R][K] -> E4M3 hi / lo (A order) and E8M0 scales per 32 along K;
 // workgroup b converts rows [8b, 8b + 8).
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ src, int R,
@@ -1051,13 +1320,22 @@ static void launch_ffn(const FfnArgs& a, bool decode, hipStream_t s) {
       g.aq_hi = ws + L.xq_hi; g.aq_lo = ws + L.xq_lo; g.aq_sc = ws + L.xq_sc;
       FfnArgs d = a;
       d.aq_hi = ws + L.hq_hi; d.aq_lo = ws + L.hq_lo; d.aq_sc = ws + L.hq_sc;
-      const int64_t mt = (max_tiles_for(a.A, a.E, 64) + kSuperM - 1) / kSuperM * kSuperM;
       quant_rows_kernel<<<(unsigned)((T + 7) / 8), 256, 0, s>>>(
           a.x, T, a.H, ws + L.xq_hi, ws + L.xq_lo, ws + L.xq_sc);
-      ffn_gateup_mx_kernel<FMT><<<(unsigned)(mt * (a.I / 128)), 256, 0, s>>>(g);
-      quant_rows_kernel<<<(unsigned)((a.A + 7) / 8), 256, 0, s>>>(
-          a.hbuf, a.A, a.I, ws + L.hq_hi, ws + L.hq_lo, ws + L.hq_sc);
-      ffn_down_mx_kernel<FMT><<<(unsigned)(mt * (a.H / 256)), 256, 0, s>>>(d);
+      if constexpr (FMT == MOE_W_MXFP4) {
+        // 128-row tiles on the LDS-DMA pipeline
+        const int64_t mt = (max_tiles_for(a.A, a.E, kDmaBM) + kSuperM - 1) / kSuperM * kSuperM;
+        ffn_gateup_mxd_kernel<<<(unsigned)(mt * (a.I / 128)), kDmaWaves * 64, 0, s>>>(g);
+        quant_rows_kernel<<<(unsigned)((a.A + 7) / 8), 256, 0, s>>>(
+            a.hbuf, a.A, a.I, ws + L.hq_hi, ws + L.hq_lo, ws + L.hq_sc);
+        ffn_down_mxd_kernel<<<(unsigned)(mt * (a.H / 256)), kDmaWaves * 64, 0, s>>>(d);
+      } else {
+        const int64_t mt = (max_tiles_for(a.A, a.E, 64) + kSuperM - 1) / kSuperM * kSuperM;
+        ffn_gateup_mx_kernel<FMT><<<(unsigned)(mt * (a.I / 128)), 256, 0, s>>>(g);
+        quant_rows_kernel<<<(unsigned)((a.A + 7) / 8), 256, 0, s>>>(
+            a.hbuf, a.A, a.I, ws + L.hq_hi, ws + L.hq_lo, ws + L.hq_sc);
+        ffn_down_mx_kernel<FMT><<<(unsigned)(mt * (a.H / 256)), 256, 0, s>>>(d);
+      }
       return;
     }
   }
