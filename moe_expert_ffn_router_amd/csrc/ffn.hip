@@ -942,15 +942,17 @@ __global__ __launch_bounds__(256) void ffn_down_mx_kernel(FfnArgs a) {
 // makes all copies visible and frees chunk c-1's stage for chunk c+2.
 // ---------------------------------------------------------------------------
 constexpr int kDmaBM = 128;
+template <int BN>
 struct MxDmaStage {
   uint8_t ah[kDmaBM * 128];  // A hi [row][128 B]: 16-byte unit u stored at u ^ (row & 7)
   uint8_t al[kDmaBM * 128];  // A lo, same layout
-  uint8_t b[256 * 64];       // weights [row][64 B]: unit u stored at u ^ ((row >> 1) & 3)
+  uint8_t b[BN * 64];        // weights [row][64 B]: unit u stored at u ^ ((row >> 1) & 3)
   // scales, the chunk's 4 E8M0 bytes per row, ordered so that a lane's four
-  // subtiles are one 16-byte read: A row (half h, subtile i, l) at
-  // h*64 + 4l + i, weight row (quarter q, subtile j, l) at q*64 + 4l + j
+  // subtiles of a 64-row group are one 16-byte read: A row (half h,
+  // subtile i, l) at h*64 + 4l + i, weight row (group q, subtile j, l) at
+  // q*64 + 4l + j
   __attribute__((aligned(16))) uint32_t as[kDmaBM];
-  __attribute__((aligned(16))) uint32_t bs[256];
+  __attribute__((aligned(16))) uint32_t bs[BN];
 };
 
 // Copies of 16 bytes (4 bytes) per lane from base + off into LDS at lds +
@@ -980,15 +982,19 @@ __device__ __forceinline__ void dma4(const uint8_t* base, uint32_t off, const vo
     asm volatile("s_barrier" ::: "memory");              \
   } while (0)
 
-template <bool GATED, int WAVES>
-__device__ __forceinline__ void ffn_mx_dma_body(const FfnArgs& a, MxDmaStage& s0, MxDmaStage& s1,
-                                                MxDmaStage& s2) {
-  static_assert(WAVES == 4 || WAVES == 8, "2 row halves x 2 or 4 column groups");
-  constexpr int WN = WAVES / 2;          // column groups
-  constexpr int NSUB = 16 / WN;          // 16-row weight subtiles per wave
+template <bool GATED, int BN, int STAGES>
+__device__ __forceinline__ void ffn_mx_dma_body(const FfnArgs& a, MxDmaStage<BN>& s0,
+                                                MxDmaStage<BN>& s1, MxDmaStage<BN>& s2) {
+  static_assert(BN == 256 || BN == 512, "256 or 512 weight rows per block");
+  static_assert(STAGES == 2 || STAGES == 3, "two or three stages");
+  constexpr int WAVES = 8, WN = 4;          // 2 row halves x 4 column groups
+  constexpr int NSUB = BN / 16 / WN;        // 16-row weight subtiles per wave
+  constexpr int NQ = NSUB / 4;              // 64-row weight groups per wave
   constexpr int MSUB = 4, NH = GATED ? 2 : 4;
-  constexpr int NCOLB = GATED ? 128 : 256;  // output columns per block
-  constexpr int CPQ = 16 / WAVES;           // 1 KB copies per wave per operand and chunk
+  constexpr int NCOLB = GATED ? BN / 2 : BN;  // output columns per block
+  constexpr int CPA = 16 / WAVES;             // 1 KB copies of A hi (and lo) per wave
+  constexpr int CPB = BN / 16 / WAVES;        // 1 KB copies of weights per wave
+  constexpr int NBS = BN / 64;                // 256 B copies of weight scales
   const int N_out = GATED ? a.I : a.H;
   const int K = GATED ? a.H : a.I, nch = K / KC, KS = K / 32;
   const int nnb = N_out / NCOLB;
@@ -1025,8 +1031,8 @@ __device__ __forceinline__ void ffn_mx_dma_body(const FfnArgs& a, MxDmaStage& s0
     src_row[tid] = GATED ? a.sorted_idx[seg0 + rr] / a.k : seg0 + rr;
   }
   __syncthreads();
-  // weight row of block-local row br = (quarter br/64, subtile (br/16)%4,
-  // br%16); a gated quarter is 32 gate rows then the matching 32 up rows
+  // weight row of block-local row br = (group br/64, subtile (br/16)%4,
+  // br%16); a gated group is 32 gate rows then the matching 32 up rows
   auto wrow = [&](int br) {
     const int q = br >> 6, j = (br >> 4) & 3, l = br & 15;
     if constexpr (GATED) {
@@ -1036,35 +1042,42 @@ __device__ __forceinline__ void ffn_mx_dma_body(const FfnArgs& a, MxDmaStage& s0
       return nb * NCOLB + br;
     }
   };
-  // This wave's copies per chunk: A hi and lo units of rows 8n..8n+7 and the
-  // weights of rows 16n..16n+15 for n = CPQ*wave + q (16 B per lane each);
-  // one dword per lane of weight scales (waves 0-3, quarter = wave) and of A
-  // scales (two waves, half = their index).  32-bit offsets (the caller
-  // checks the sizes).
-  const bool has_as = WAVES == 8 ? (wave == 4 || wave == 5) : wave < 2;
-  const int as_half = WAVES == 8 ? wave - 4 : wave;
-  uint32_t ao[CPQ], wo[CPQ], sob = 0, soa = 0;
+  // This wave's copies per chunk: A hi and lo units of rows 8n..8n+7 for
+  // n = CPA*wave + q, weights of rows 16n..16n+15 for n = CPB*wave + q (16 B
+  // per lane each), one dword per lane of weight scales (groups wave,
+  // wave + 8, ...) and, on waves 0 and 1, of A scales (half = wave).  32-bit
+  // offsets (the caller checks the sizes).
+  uint32_t ao[CPA], wo[CPB], sob[(NBS + WAVES - 1) / WAVES], soa = 0;
 #pragma unroll
-  for (int q = 0; q < CPQ; ++q) {
-    const int n = wave * CPQ + q;
-    const int ar = n * 8 + (lane >> 3);
+  for (int q = 0; q < CPA; ++q) {
+    const int ar = (wave * CPA + q) * 8 + (lane >> 3);
     ao[q] = (uint32_t)src_row[ar] * (uint32_t)K + (uint32_t)(((lane & 7) ^ (ar & 7)) * 16);
-    const int br = n * 16 + (lane >> 2);
+  }
+#pragma unroll
+  for (int q = 0; q < CPB; ++q) {
+    const int br = (wave * CPB + q) * 16 + (lane >> 2);
     wo[q] = (uint32_t)wrow(br) * (uint32_t)(K / 2) + (uint32_t)(((lane & 3) ^ ((br >> 1) & 3)) * 16);
   }
-  if (wave < 4) sob = (uint32_t)wrow(wave * 64 + (lane & 3) * 16 + (lane >> 2)) * (uint32_t)KS;
-  if (has_as) soa = (uint32_t)src_row[as_half * 64 + (lane & 3) * 16 + (lane >> 2)] * (uint32_t)KS;
-  auto issue = [&](int c, MxDmaStage& S) {
+#pragma unroll
+  for (int q = 0; q < (NBS + WAVES - 1) / WAVES; ++q) {
+    const int grp64 = wave + q * WAVES;
+    sob[q] = grp64 < NBS ? (uint32_t)wrow(grp64 * 64 + (lane & 3) * 16 + (lane >> 2)) * (uint32_t)KS : 0u;
+  }
+  if (wave < 2) soa = (uint32_t)src_row[wave * 64 + (lane & 3) * 16 + (lane >> 2)] * (uint32_t)KS;
+  auto issue = [&](int c, MxDmaStage<BN>& S) {
     const uint32_t ka = (uint32_t)(c * KC), kb = (uint32_t)(c * (KC / 2)), ks = (uint32_t)(c * 4);
 #pragma unroll
-    for (int q = 0; q < CPQ; ++q) {
-      const int n = wave * CPQ + q;
+    for (int q = 0; q < CPA; ++q) {
+      const int n = wave * CPA + q;
       dma16(a.aq_hi, ao[q] + ka, S.ah + n * 1024);
       dma16(a.aq_lo, ao[q] + ka, S.al + n * 1024);
-      dma16(w, wo[q] + kb, S.b + n * 1024);
     }
-    if (wave < 4) dma4(sc, sob + ks, S.bs + wave * 64);
-    if (has_as) dma4(a.aq_sc, soa + ks, S.as + as_half * 64);
+#pragma unroll
+    for (int q = 0; q < CPB; ++q) dma16(w, wo[q] + kb, S.b + (wave * CPB + q) * 1024);
+#pragma unroll
+    for (int q = 0; q < (NBS + WAVES - 1) / WAVES; ++q)
+      if (wave + q * WAVES < NBS) dma4(sc, sob[q] + ks, S.bs + (wave + q * WAVES) * 64);
+    if (wave < 2) dma4(a.aq_sc, soa + ks, S.as + wave * 64);
   };
 
   f32x4 acc[MSUB][NSUB];
@@ -1075,16 +1088,16 @@ __device__ __forceinline__ void ffn_mx_dma_body(const FfnArgs& a, MxDmaStage& s0
 
   // the wave's weight subtiles, then its 4 row subtiles (the next one's A
   // fragments read while the current one's MFMAs run)
-  auto compute = [&](const MxDmaStage& S) {
+  auto compute = [&](const MxDmaStage<BN>& S) {
     i32x4 bq[NSUB];
     int sb[NSUB];
 #pragma unroll
-    for (int qq = 0; qq < NSUB / 4; ++qq) {
-      const int quarter = nw * (NSUB / 4) + qq;
-      const uint4 bsv = *reinterpret_cast<const uint4*>(&S.bs[quarter * 64 + l16 * 4]);
+    for (int qq = 0; qq < NQ; ++qq) {
+      const int grp64 = nw * NQ + qq;
+      const uint4 bsv = *reinterpret_cast<const uint4*>(&S.bs[grp64 * 64 + l16 * 4]);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int j = qq * 4 + jj, br = quarter * 64 + jj * 16 + l16;
+        const int j = qq * 4 + jj, br = grp64 * 64 + jj * 16 + l16;
         bq[j] = *reinterpret_cast<const i32x4*>(S.b + br * 64 + ((g ^ ((br >> 1) & 3)) * 16));
         const uint32_t d = jj == 0 ? bsv.x : jj == 1 ? bsv.y : jj == 2 ? bsv.z : bsv.w;
         sb[j] = (int)((d >> (8 * g)) & 0xffu);
@@ -1109,54 +1122,75 @@ __device__ __forceinline__ void ffn_mx_dma_body(const FfnArgs& a, MxDmaStage& s0
     frag(0, ah, al, sa);
 #pragma unroll
     for (int i = 0; i < MSUB; ++i) {
+      // the next subtile's A fragments are read ahead when registers allow
+      constexpr bool AHEAD = NSUB <= 4;
       i32x8 nh, nl;
       int ns = 0;
-      if (i + 1 < MSUB) frag(i + 1, nh, nl, ns);
+      if (AHEAD && i + 1 < MSUB) frag(i + 1, nh, nl, ns);
 #pragma unroll
       for (int j = 0; j < NSUB; ++j) {
         acc[i][j] = mfma_mx(ah, bq[j], sa, sb[j], acc[i][j]);
         acc[i][j] = mfma_mx(al, bq[j], sa, sb[j], acc[i][j]);
+        if constexpr (!AHEAD) pin_a(acc[i][j]);  // accumulators in AGPRs
       }
       if (i + 1 < MSUB) {
-        ah = nh;
-        al = nl;
-        sa = ns;
+        if (AHEAD) {
+          ah = nh;
+          al = nl;
+          sa = ns;
+        } else {
+          frag(i + 1, ah, al, sa);
+        }
       }
     }
   };
 
-  // K/128 >= 2 (even): chunks 0 and 1 in flight before the loop.  The three
-  // stages are separate LDS objects and each step names its own.
-  constexpr int ND = 3 * CPQ + (WAVES == 4 ? 2 : 1);  // copies per chunk of a full wave
-  const bool short_wave = WAVES == 8 ? wave >= 6 : wave >= 2;  // one scale copy fewer
-  auto step = [&](int c, const MxDmaStage& cur, MxDmaStage& nxt) {
-    if (c + 1 < nch) {
-      if (short_wave)
-        MOE_DMA_SYNC(ND - 1);
-      else
-        MOE_DMA_SYNC(ND);
-    } else {
-      MOE_DMA_SYNC(0);
+  // K/128 >= 2 (even).  The stages are separate LDS objects and each step
+  // names its own.  Three stages: chunks c+1 and c+2 in flight while c is
+  // computed (a wave waits for all but its copies of chunk c+1); two stages:
+  // chunk c+1 in flight.
+  if constexpr (STAGES == 3) {
+    constexpr int ND = 2 * CPA + CPB + (NBS + WAVES - 1) / WAVES;  // waves 2.. (no A scales)
+    auto step = [&](int c, const MxDmaStage<BN>& cur, MxDmaStage<BN>& nxt) {
+      if (c + 1 < nch) {
+        if (wave < 2)
+          MOE_DMA_SYNC(ND + 1);
+        else
+          MOE_DMA_SYNC(ND);
+      } else {
+        MOE_DMA_SYNC(0);
+      }
+      if (c + 2 < nch) issue(c + 2, nxt);
+      compute(cur);
+    };
+    issue(0, s0);
+    issue(1, s1);
+    for (int c = 0;; c += 3) {
+      step(c, s0, s2);
+      if (c + 1 >= nch) break;
+      step(c + 1, s1, s0);
+      if (c + 2 >= nch) break;
+      step(c + 2, s2, s1);
+      if (c + 3 >= nch) break;
     }
-    if (c + 2 < nch) issue(c + 2, nxt);
-    compute(cur);
-  };
-  issue(0, s0);
-  issue(1, s1);
-  for (int c = 0;; c += 3) {
-    step(c, s0, s2);
-    if (c + 1 >= nch) break;
-    step(c + 1, s1, s0);
-    if (c + 2 >= nch) break;
-    step(c + 2, s2, s1);
-    if (c + 3 >= nch) break;
+  } else {
+    auto step = [&](int c, const MxDmaStage<BN>& cur, MxDmaStage<BN>& nxt) {
+      MOE_DMA_SYNC(0);
+      if (c + 1 < nch) issue(c + 1, nxt);
+      compute(cur);
+    };
+    issue(0, s0);
+    for (int c = 0; c < nch; c += 2) {  // nch even
+      step(c, s0, s1);
+      step(c + 1, s1, s0);
+    }
   }
 
   const int m_base = mh * 64;
   if constexpr (GATED) {
 #pragma unroll
-    for (int qq = 0; qq < NSUB / 4; ++qq) {
-      const int c0 = nb * NCOLB + (nw * (NSUB / 4) + qq) * (NH * 16);
+    for (int qq = 0; qq < NQ; ++qq) {
+      const int c0 = nb * NCOLB + (nw * NQ + qq) * (NH * 16);
 #pragma unroll
       for (int i = 0; i < MSUB; ++i)
 #pragma unroll
@@ -1186,16 +1220,20 @@ __device__ __forceinline__ void ffn_mx_dma_body(const FfnArgs& a, MxDmaStage& s0
   }
 }
 
-// 8 waves (two per SIMD); one wave per SIMD with 64 x 128 outputs each
-// measured 15 % slower (its LDS-read and barrier latencies go uncovered)
-constexpr int kDmaWaves = 8;
-__global__ __launch_bounds__(kDmaWaves * 64) void ffn_gateup_mxd_kernel(FfnArgs a) {
-  __shared__ MxDmaStage s0, s1, s2;
-  ffn_mx_dma_body<true, kDmaWaves>(a, s0, s1, s2);
+#ifndef MOE_DMA_BN
+#define MOE_DMA_BN 512
+#endif
+constexpr int kDmaBN = MOE_DMA_BN;                    // weight rows per block
+constexpr int kDmaStages = kDmaBN == 512 ? 2 : 3;     // what fits in 160 KB of LDS
+__global__ __launch_bounds__(512) void ffn_gateup_mxd_kernel(FfnArgs a) {
+  __shared__ MxDmaStage<kDmaBN> s0, s1;
+  __shared__ MxDmaStage<kDmaStages == 3 ? kDmaBN : 16> s2;
+  ffn_mx_dma_body<true, kDmaBN, kDmaStages>(a, s0, s1, *reinterpret_cast<MxDmaStage<kDmaBN>*>(&s2));
 }
-__global__ __launch_bounds__(kDmaWaves * 64) void ffn_down_mxd_kernel(FfnArgs a) {
-  __shared__ MxDmaStage s0, s1, s2;
-  ffn_mx_dma_body<false, kDmaWaves>(a, s0, s1, s2);
+__global__ __launch_bounds__(512) void ffn_down_mxd_kernel(FfnArgs a) {
+  __shared__ MxDmaStage<kDmaBN> s0, s1;
+  __shared__ MxDmaStage<kDmaStages == 3 ? kDmaBN : 16> s2;
+  ffn_mx_dma_body<false, kDmaBN, kDmaStages>(a, s0, s1, *reinterpret_cast<MxDmaStage<kDmaBN>*>(&s2));
 }
 
 // bf16 rows [R][K] -> E4M3 hi / lo (A order) and E8M0 scales per 32 along K;
@@ -1322,13 +1360,13 @@ static void launch_ffn(const FfnArgs& a, bool decode, hipStream_t s) {
       d.aq_hi = ws + L.hq_hi; d.aq_lo = ws + L.hq_lo; d.aq_sc = ws + L.hq_sc;
       quant_rows_kernel<<<(unsigned)((T + 7) / 8), 256, 0, s>>>(
           a.x, T, a.H, ws + L.xq_hi, ws + L.xq_lo, ws + L.xq_sc);
-      if constexpr (FMT == MOE_W_MXFP4) {
+      if (FMT == MOE_W_MXFP4 && a.I % (kDmaBN / 2) == 0 && a.H % kDmaBN == 0) {
         // 128-row tiles on the LDS-DMA pipeline
         const int64_t mt = (max_tiles_for(a.A, a.E, kDmaBM) + kSuperM - 1) / kSuperM * kSuperM;
-        ffn_gateup_mxd_kernel<<<(unsigned)(mt * (a.I / 128)), kDmaWaves * 64, 0, s>>>(g);
+        ffn_gateup_mxd_kernel<<<(unsigned)(mt * (a.I / (kDmaBN / 2))), 512, 0, s>>>(g);
         quant_rows_kernel<<<(unsigned)((a.A + 7) / 8), 256, 0, s>>>(
             a.hbuf, a.A, a.I, ws + L.hq_hi, ws + L.hq_lo, ws + L.hq_sc);
-        ffn_down_mxd_kernel<<<(unsigned)(mt * (a.H / 256)), kDmaWaves * 64, 0, s>>>(d);
+        ffn_down_mxd_kernel<<<(unsigned)(mt * (a.H / kDmaBN)), 512, 0, s>>>(d);
       } else {
         const int64_t mt = (max_tiles_for(a.A, a.E, 64) + kSuperM - 1) / kSuperM * kSuperM;
         ffn_gateup_mx_kernel<FMT><<<(unsigned)(mt * (a.I / 128)), 256, 0, s>>>(g);
