@@ -990,11 +990,10 @@ __device__ __forceinline__ void dma4(const uint8_t* base, uint32_t off, const vo
     asm volatile("s_barrier" ::: "memory");              \
   } while (0)
 
-template <bool GATED, int BN, int STAGES>
+template <bool GATED, int BN>
 __device__ __forceinline__ void ffn_mx_dma_body(const FfnArgs& a, MxDmaStage<BN>& s0,
-                                                MxDmaStage<BN>& s1, MxDmaStage<BN>& s2) {
+                                                MxDmaStage<BN>& s1) {
   static_assert(BN == 256 || BN == 512, "256 or 512 weight rows per block");
-  static_assert(STAGES == 2 || STAGES == 3, "two or three stages");
   constexpr int WAVES = 8, WN = 4;          // 2 row halves x 4 column groups
   constexpr int NSUB = BN / 16 / WN;        // 16-row weight subtiles per wave
   constexpr int NQ = NSUB / 4;              // 64-row weight groups per wave
@@ -1055,7 +1054,8 @@ __device__ __forceinline__ void ffn_mx_dma_body(const FfnArgs& a, MxDmaStage<BN>
   // per lane each), one dword per lane of weight scales (groups wave,
   // wave + 8, ...) and, on waves 0 and 1, of A scales (half = wave).  32-bit
   // offsets (the caller checks the sizes).
-  uint32_t ao[CPA], wo[CPB], sob[(NBS + WAVES - 1) / WAVES], soa = 0;
+  constexpr int NSB = (NBS + WAVES - 1) / WAVES;  // weight-scale copies per wave
+  uint32_t ao[CPA], wo[CPB], sob[NSB], soa = 0;
 #pragma unroll
   for (int q = 0; q < CPA; ++q) {
     const int ar = (wave * CPA + q) * 8 + (lane >> 3);
@@ -1067,7 +1067,7 @@ __device__ __forceinline__ void ffn_mx_dma_body(const FfnArgs& a, MxDmaStage<BN>
     wo[q] = (uint32_t)wrow(br) * (uint32_t)(K / 2) + (uint32_t)(((lane & 3) ^ b_swz(br)) * 16);
   }
 #pragma unroll
-  for (int q = 0; q < (NBS + WAVES - 1) / WAVES; ++q) {
+  for (int q = 0; q < NSB; ++q) {
     const int grp64 = wave + q * WAVES;
     sob[q] = grp64 < NBS ? (uint32_t)wrow(grp64 * 64 + (lane & 3) * 16 + (lane >> 2)) * (uint32_t)KS : 0u;
   }
@@ -1083,7 +1083,7 @@ __device__ __forceinline__ void ffn_mx_dma_body(const FfnArgs& a, MxDmaStage<BN>
 #pragma unroll
     for (int q = 0; q < CPB; ++q) dma16(w, wo[q] + kb, S.b + (wave * CPB + q) * 1024);
 #pragma unroll
-    for (int q = 0; q < (NBS + WAVES - 1) / WAVES; ++q)
+    for (int q = 0; q < NSB; ++q)
       if (wave + q * WAVES < NBS) dma4(sc, sob[q] + ks, S.bs + (wave + q * WAVES) * 64);
     if (wave < 2) dma4(a.aq_sc, soa + ks, S.as + wave * 64);
   };
@@ -1130,11 +1130,9 @@ __device__ __forceinline__ void ffn_mx_dma_body(const FfnArgs& a, MxDmaStage<BN>
     frag(0, ah, al, sa);
 #pragma unroll
     for (int i = 0; i < MSUB; ++i) {
-      // the next subtile's A fragments are read ahead when registers allow
-      constexpr bool AHEAD = true;
       i32x8 nh, nl;
       int ns = 0;
-      if (AHEAD && i + 1 < MSUB) frag(i + 1, nh, nl, ns);
+      if (i + 1 < MSUB) frag(i + 1, nh, nl, ns);
 #pragma unroll
       for (int j = 0; j < NSUB; ++j) {
         acc[i][j] = mfma_mx(ah, bq[j], sa, sb[j], acc[i][j]);
@@ -1142,56 +1140,24 @@ __device__ __forceinline__ void ffn_mx_dma_body(const FfnArgs& a, MxDmaStage<BN>
         if constexpr (NSUB > 4) pin_a(acc[i][j]);  // accumulators in AGPRs
       }
       if (i + 1 < MSUB) {
-        if (AHEAD) {
-          ah = nh;
-          al = nl;
-          sa = ns;
-        } else {
-          frag(i + 1, ah, al, sa);
-        }
+        ah = nh;
+        al = nl;
+        sa = ns;
       }
     }
   };
 
-  // K/128 >= 2 (even).  The stages are separate LDS objects and each step
-  // names its own.  Three stages: chunks c+1 and c+2 in flight while c is
-  // computed (a wave waits for all but its copies of chunk c+1); two stages:
-  // chunk c+1 in flight.
-  if constexpr (STAGES == 3) {
-    constexpr int ND = 2 * CPA + CPB + (NBS + WAVES - 1) / WAVES;  // waves 2.. (no A scales)
-    auto step = [&](int c, const MxDmaStage<BN>& cur, MxDmaStage<BN>& nxt) {
-      if (c + 1 < nch) {
-        if (wave < 2)
-          MOE_DMA_SYNC(ND + 1);
-        else
-          MOE_DMA_SYNC(ND);
-      } else {
-        MOE_DMA_SYNC(0);
-      }
-      if (c + 2 < nch) issue(c + 2, nxt);
-      compute(cur);
-    };
-    issue(0, s0);
-    issue(1, s1);
-    for (int c = 0;; c += 3) {
-      step(c, s0, s2);
-      if (c + 1 >= nch) break;
-      step(c + 1, s1, s0);
-      if (c + 2 >= nch) break;
-      step(c + 2, s2, s1);
-      if (c + 3 >= nch) break;
-    }
-  } else {
-    auto step = [&](int c, const MxDmaStage<BN>& cur, MxDmaStage<BN>& nxt) {
-      MOE_DMA_SYNC(0);
-      if (c + 1 < nch) issue(c + 1, nxt);
-      compute(cur);
-    };
-    issue(0, s0);
-    for (int c = 0; c < nch; c += 2) {  // nch even
-      step(c, s0, s1);
-      step(c + 1, s1, s0);
-    }
+  // K/128 >= 2 (even).  Two stages, separate LDS objects, each step naming
+  // its own: chunk c+1 is copied while chunk c is computed.
+  auto step = [&](int c, const MxDmaStage<BN>& cur, MxDmaStage<BN>& nxt) {
+    MOE_DMA_SYNC(0);
+    if (c + 1 < nch) issue(c + 1, nxt);
+    compute(cur);
+  };
+  issue(0, s0);
+  for (int c = 0; c < nch; c += 2) {
+    step(c, s0, s1);
+    step(c + 1, s1, s0);
   }
 
   const int m_base = mh * 64;
@@ -1228,20 +1194,16 @@ __device__ __forceinline__ void ffn_mx_dma_body(const FfnArgs& a, MxDmaStage<BN>
   }
 }
 
-#ifndef MOE_DMA_BN
-#define MOE_DMA_BN 512
-#endif
-constexpr int kDmaBN = MOE_DMA_BN;                    // weight rows per block
-constexpr int kDmaStages = kDmaBN == 512 ? 2 : 3;     // what fits in 160 KB of LDS
+// 512 weight rows per block over two stages (256 rows over three stages
+// measured 15 % slower)
+constexpr int kDmaBN = 512;
 __global__ __launch_bounds__(512) void ffn_gateup_mxd_kernel(FfnArgs a) {
   __shared__ MxDmaStage<kDmaBN> s0, s1;
-  __shared__ MxDmaStage<kDmaStages == 3 ? kDmaBN : 16> s2;
-  ffn_mx_dma_body<true, kDmaBN, kDmaStages>(a, s0, s1, *reinterpret_cast<MxDmaStage<kDmaBN>*>(&s2));
+  ffn_mx_dma_body<true, kDmaBN>(a, s0, s1);
 }
 __global__ __launch_bounds__(512) void ffn_down_mxd_kernel(FfnArgs a) {
   __shared__ MxDmaStage<kDmaBN> s0, s1;
-  __shared__ MxDmaStage<kDmaStages == 3 ? kDmaBN : 16> s2;
-  ffn_mx_dma_body<false, kDmaBN, kDmaStages>(a, s0, s1, *reinterpret_cast<MxDmaStage<kDmaBN>*>(&s2));
+  ffn_mx_dma_body<false, kDmaBN>(a, s0, s1);
 }
 
 // bf16 rows [R][K] -> E4M3 hi / lo (A order) and E8M0 scales per 32 along K;
@@ -1368,6 +1330,8 @@ static void launch_ffn(const FfnArgs& a, bool decode, hipStream_t s) {
       d.aq_hi = ws + L.hq_hi; d.aq_lo = ws + L.hq_lo; d.aq_sc = ws + L.hq_sc;
       quant_rows_kernel<<<(unsigned)((T + 7) / 8), 256, 0, s>>>(
           a.x, T, a.H, ws + L.xq_hi, ws + L.xq_lo, ws + L.xq_sc);
+      // (FP8 on these kernels, 256 rows per block, measured 2.00 ms against
+      // 1.50 ms on the 64-row kernels for its skewed 2048-token batch)
       if (FMT == MOE_W_MXFP4 && a.I % (kDmaBN / 2) == 0 && a.H % kDmaBN == 0) {
         // 128-row tiles on the LDS-DMA pipeline
         const int64_t mt =
