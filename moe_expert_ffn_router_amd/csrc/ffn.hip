@@ -1206,6 +1206,238 @@ __global__ __launch_bounds__(512) void ffn_down_mxd_kernel(FfnArgs a) {
   ffn_mx_dma_body<false, kDmaBN>(a, s0, s1);
 }
 
+// ---------------------------------------------------------------------------
+// NVFP4 prefill over the LDS-DMA pipeline: bf16 activations and E2M1 codes
+// with their E4M3 block scales copied straight into LDS (two stages), the
+// codes decoded to bf16 per lane right before the 32x32x16 bf16 MFMAs (that
+// shape runs at twice the rate of 16x16x32 here: 2.5 against 1.3 PFLOP/s
+// measured).  WAVES waves as MB row groups of 64 rows x WAVES/MB column
+// groups over BN weight rows; a wave owns 2 x NB output blocks of 32 x 32.
+//   32x32x16 operands (checked on the device): lane l holds row (A) or
+//   column (B) l % 32 and 8 consecutive K at 8*(l/32) of the step's 16; result
+//   value v of lane l is C[8*(v/4) + 4*(l/32) + v%4][l % 32].  Within a chunk
+//   the K order is permuted the same way for A and B: step s, lane half h,
+//   element e is K = 64h + 8s + e, so lane half h reads only the chunk's
+//   half h of the activation row (one 16-byte unit per step) and of the
+//   weight codes (32 bytes), and 4 of the row's 8 scale bytes.
+// ---------------------------------------------------------------------------
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void pin_a16(f32x16& acc) { asm volatile("" : "+a"(acc)); }
+
+template <int BM, int BN>
+struct NvDmaStage {
+  // activation rows, bf16: the chunk's first and second 64 K values (128 B
+  // each), 16-byte unit u stored at u ^ a_swz(row)
+  uint8_t a0[BM * 128];
+  uint8_t a1[BM * 128];
+  uint8_t b[BN * 64];                    // E2M1 codes [row][64 B], unit u at u ^ b_swz(row)
+  __attribute__((aligned(16))) uint2 bs[BN];  // the chunk's 8 E4M3 scale bytes per row
+};
+
+template <bool GATED, int MB, int WAVES, int BN>
+__device__ __forceinline__ void ffn_nv_dma_body(const FfnArgs& a, NvDmaStage<MB * 64, BN>& s0,
+                                                NvDmaStage<MB * 64, BN>& s1) {
+  static_assert(MB == 1 || MB == 2, "64 or 128 rows per block");
+  constexpr int BM = MB * 64, NWG = WAVES / MB;  // column groups
+  constexpr int WR = BN / NWG;                   // weight rows per wave
+  constexpr int NB = WR / 32;                    // 32-column blocks per wave
+  constexpr int NCOLB = GATED ? BN / 2 : BN;     // output columns per block
+  constexpr int CPA = BM / 8 / WAVES;            // 1 KB copies per activation half per wave
+  constexpr int CPB = BN / 16 / WAVES;           // 1 KB copies of codes per wave
+  constexpr int CPS = BN / 32 / WAVES;           // 256 B copies of scales per wave
+  static_assert(CPA >= 1 && CPB >= 1 && CPS >= 1 && NB % 2 == 0, "block shape");
+  using Stage = NvDmaStage<BM, BN>;
+  const int N_out = GATED ? a.I : a.H;
+  const int K = GATED ? a.H : a.I, nch = K / KC;
+  const int nnb = N_out / NCOLB;
+  const int G = (int)gridDim.x, b = (int)blockIdx.x;
+  const int lid = (b & 7) * (G >> 3) + (b >> 3);  // G is a multiple of 8
+  const int grp = lid / (kDmaSuperM * nnb), gi = lid - grp * (kDmaSuperM * nnb);
+  const int tile = grp * kDmaSuperM + gi % kDmaSuperM, nb = gi / kDmaSuperM;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int mh = wave / NWG, nw = wave % NWG;
+
+  __shared__ int src_row[BM];
+  __shared__ TileInfo s_ti;
+  __shared__ int s_valid;
+  if (tid < 64) {
+    TileInfo ti;
+    const bool ok = find_tile<BM>(a.counts, a.offsets, a.E, tile, lane, ti);
+    if (lane == 0) {
+      s_valid = ok;
+      if (ok) s_ti = ti;
+    }
+  }
+  __syncthreads();
+  if (!s_valid) return;
+  const int e = __builtin_amdgcn_readfirstlane(s_ti.e);
+  const int seg0 = __builtin_amdgcn_readfirstlane(s_ti.seg0);
+  const int rows = __builtin_amdgcn_readfirstlane(s_ti.rows);
+  const uint8_t* rec = record_of(a, e);
+  const uint8_t* w = rec + (GATED ? a.off_w13 : a.off_w2);
+  const uint8_t* sc = rec + (GATED ? a.off_w13s : a.off_w2s);
+  const uint8_t* asrc = reinterpret_cast<const uint8_t*>(GATED ? a.x : a.hbuf);
+  // the record's fp32 tensor scales (gate, up, down), read once up front
+  const float* tsp = reinterpret_cast<const float*>(rec + a.off_ts);
+  const float ts0 = tsp[GATED ? 0 : 2], ts1 = GATED ? tsp[1] : 1.0f;
+  // rows past the tile read its first row: valid memory, outputs discarded
+  if (tid < BM) {
+    const int rr = tid < rows ? tid : 0;
+    src_row[tid] = GATED ? a.sorted_idx[seg0 + rr] / a.k : seg0 + rr;
+  }
+  __syncthreads();
+  // weight row of block-local row br = (column group br/WR, 32-row block
+  // (br/32) % NB, row br%32); a gated group's first NB/2 blocks are gate rows,
+  // the rest the matching up rows
+  auto wrow = [&](int br) {
+    if constexpr (GATED) {
+      const int q = br / WR, n = (br >> 5) % NB, j = br & 31;
+      const int col = nb * NCOLB + q * (WR / 2) + (n % (NB / 2)) * 32 + j;
+      return n < NB / 2 ? col : a.I + col;
+    } else {
+      return nb * NCOLB + br;
+    }
+  };
+  // 32-bit byte offsets (the caller checks the sizes)
+  uint32_t ao[CPA], wo[CPB], so[CPS];
+#pragma unroll
+  for (int q = 0; q < CPA; ++q) {
+    const int ar = (wave * CPA + q) * 8 + (lane >> 3);
+    ao[q] = (uint32_t)src_row[ar] * (uint32_t)(K * 2) + (uint32_t)(((lane & 7) ^ a_swz(ar)) * 16);
+  }
+#pragma unroll
+  for (int q = 0; q < CPB; ++q) {
+    const int br = (wave * CPB + q) * 16 + (lane >> 2);
+    wo[q] = (uint32_t)wrow(br) * (uint32_t)(K / 2) + (uint32_t)(((lane & 3) ^ b_swz(br)) * 16);
+  }
+#pragma unroll
+  for (int q = 0; q < CPS; ++q) {
+    const int br = (wave * CPS + q) * 32 + (lane >> 1);
+    so[q] = (uint32_t)wrow(br) * (uint32_t)(K / 16) + (uint32_t)((lane & 1) * 4);
+  }
+  auto issue = [&](int c, Stage& S) {
+    const uint32_t ka = (uint32_t)(c * KC * 2), kb = (uint32_t)(c * (KC / 2)), ks = (uint32_t)(c * 8);
+#pragma unroll
+    for (int q = 0; q < CPA; ++q) {
+      const int n = wave * CPA + q;
+      dma16(asrc, ao[q] + ka, S.a0 + n * 1024);
+      dma16(asrc, ao[q] + ka + 128, S.a1 + n * 1024);
+    }
+#pragma unroll
+    for (int q = 0; q < CPB; ++q) dma16(w, wo[q] + kb, S.b + (wave * CPB + q) * 1024);
+#pragma unroll
+    for (int q = 0; q < CPS; ++q) dma4(sc, so[q] + ks, &S.bs[(wave * CPS + q) * 32]);
+  };
+
+  f32x16 acc[2][NB];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
+
+  auto compute = [&](const Stage& S) {
+    const uint8_t* ap = h ? S.a1 : S.a0;
+    uint4 code[NB][2];
+    float scl[NB][4];  // the lane's 4 block scales (K blocks 4h .. 4h+3) per column block
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const int br = nw * WR + n * 32 + l32;
+      const uint8_t* pb = S.b + br * 64;
+      code[n][0] = *reinterpret_cast<const uint4*>(pb + (((2 * h) ^ b_swz(br)) * 16));
+      code[n][1] = *reinterpret_cast<const uint4*>(pb + (((2 * h + 1) ^ b_swz(br)) * 16));
+      const uint2 sv = S.bs[br];
+      const int s4 = (int)(h ? sv.y : sv.x);
+      scl[n][0] = __builtin_amdgcn_cvt_f32_fp8(s4, 0);
+      scl[n][1] = __builtin_amdgcn_cvt_f32_fp8(s4, 1);
+      scl[n][2] = __builtin_amdgcn_cvt_f32_fp8(s4, 2);
+      scl[n][3] = __builtin_amdgcn_cvt_f32_fp8(s4, 3);
+    }
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      bf16x8 af[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int r = mh * 64 + mb * 32 + l32;
+        af[mb] = *reinterpret_cast<const bf16x8*>(ap + r * 128 + ((st ^ a_swz(r)) * 16));
+      }
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        const uint4 q = code[n][st >> 2];
+        const uint32_t d = (st & 3) == 0 ? q.x : (st & 3) == 1 ? q.y : (st & 3) == 2 ? q.z : q.w;
+        const bf16x8 bv = fp4x8_to_bf16_mul(d, scl[n][st >> 1]);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          acc[mb][n] = mfma32(af[mb], bv, acc[mb][n]);
+          pin_a16(acc[mb][n]);
+        }
+      }
+    }
+  };
+
+  // K/128 >= 2 (even): two stages, chunk c+1 copied while chunk c is computed
+  auto step = [&](int c, const Stage& cur, Stage& nxt) {
+    MOE_DMA_SYNC(0);
+    if (c + 1 < nch) issue(c + 1, nxt);
+    compute(cur);
+  };
+  issue(0, s0);
+  for (int c = 0; c < nch; c += 2) {
+    step(c, s0, s1);
+    step(c + 1, s1, s0);
+  }
+
+  // lane (l32, h), value v: row 8*(v/4) + 4h + v%4 of the 32-row block
+  if constexpr (GATED) {
+    const float tsg = ts0, tsu = ts1;
+#pragma unroll
+    for (int n = 0; n < NB / 2; ++n) {
+      const int col = nb * NCOLB + nw * (WR / 2) + n * 32 + l32;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = mh * 64 + mb * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (m < rows) {
+            const float gv = acc[mb][n][v] * tsg, uv = acc[mb][n + NB / 2][v] * tsu;
+            const float hv = gv / (1.0f + expf(-gv)) * uv;
+            a.hbuf[(size_t)(seg0 + m) * a.I + col] = f32_to_bf16_rne(hv);
+          }
+        }
+    }
+  } else {
+    const float tsd = ts0;
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const int col = nb * NCOLB + nw * WR + n * 32 + l32;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = mh * 64 + mb * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (m < rows)
+            a.y_perm[(size_t)(seg0 + m) * a.H + col] = f32_to_bf16_rne(acc[mb][n][v] * tsd);
+        }
+    }
+  }
+}
+
+// 64 rows x 256 weight rows on 4 waves: 68 KB of LDS, two blocks per CU
+// (measured 433 us for the 4096-token NVFP4 layer, against 463 us for 64 x 512
+// and 519 us for 128 x 512 on 8 waves, one block per CU)
+constexpr int kNvMB = 1, kNvWaves = 4, kNvBN = 256;
+__global__ __launch_bounds__(kNvWaves * 64) void ffn_gateup_nvd_kernel(FfnArgs a) {
+  __shared__ NvDmaStage<kNvMB * 64, kNvBN> s0, s1;
+  ffn_nv_dma_body<true, kNvMB, kNvWaves, kNvBN>(a, s0, s1);
+}
+__global__ __launch_bounds__(kNvWaves * 64) void ffn_down_nvd_kernel(FfnArgs a) {
+  __shared__ NvDmaStage<kNvMB * 64, kNvBN> s0, s1;
+  ffn_nv_dma_body<false, kNvMB, kNvWaves, kNvBN>(a, s0, s1);
+}
+
 // bf16 rows [R][K] -> E4M3 hi / lo (A order) and E8M0 scales per 32 along K;
 // workgroup b converts rows [8b, 8b + 8).
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ src, int R,
@@ -1355,6 +1587,18 @@ static void launch_ffn(const FfnArgs& a, bool decode, hipStream_t s) {
     ffn_gateup_decode_kernel<FMT><<<(unsigned)(mt * (a.I / kGuCols)), 256, 0, s>>>(a);
     ffn_down_decode_kernel<FMT><<<(unsigned)(mt * (a.H / kDnCols)), 256, 0, s>>>(a);
   } else if (pipe_ok(a)) {
+    if constexpr (FMT == MOE_W_NVFP4) {
+      // the activations are read as bytes with 32-bit offsets
+      const bool fits = (int64_t)(a.A / a.k) * a.H * 2 < (1ll << 32) &&
+                        (int64_t)a.A * a.I * 2 < (1ll << 32);
+      if (fits && a.I % (kNvBN / 2) == 0 && a.H % kNvBN == 0) {
+        const int64_t mt =
+            (max_tiles_for(a.A, a.E, kNvMB * 64) + kDmaSuperM - 1) / kDmaSuperM * kDmaSuperM;
+        ffn_gateup_nvd_kernel<<<(unsigned)(mt * (a.I / (kNvBN / 2))), kNvWaves * 64, 0, s>>>(a);
+        ffn_down_nvd_kernel<<<(unsigned)(mt * (a.H / kNvBN)), kNvWaves * 64, 0, s>>>(a);
+        return;
+      }
+    }
     // 64 rows per wave (more needs too many registers for two waves per SIMD);
     // a 128-row tile over 8 waves (MH = 2) measured slower than 64-row tiles
     launch_pipe<4, 1>(a, ffn_gateup_pipe_kernel<FMT, 4, 1>, ffn_down_pipe_kernel<FMT, 4, 1>, s);
