@@ -241,7 +241,9 @@ def main():
         ffn_bytes += wl.T * wl.E * 4 + wl.T * wl.H * 2
         achieved = ffn_bytes / (ffn_ms / 1e3) / 1e9
         roof.update({"achieved": round(achieved, 1), "frac": round(achieved / HBM_PEAK_GBS, 4)})
-    if whole and use_graph:
+    if use_graph and args.tokens is None:
+        # HBM bytes per step of the timed kernels, from the committed counter
+        # readings of this workload's configuration (None without them)
         roof["traffic"] = measured_traffic(wl.name)
     roof.update({"kernel": ("moe_forward_decode: token-major gate/up with routing + token-major "
                             "down with combine (2 launches)" if whole and wl.T <= 16 else
