@@ -52,6 +52,9 @@ def parse():
                     help="only run a plain 64 MiB device copy (for HBM counter calibration)")
     ap.add_argument("--resident", action="store_true",
                     help="cache workloads: keep every expert in HBM instead of the slot pool")
+    ap.add_argument("--fill-groups", type=int, default=8,
+                    help="cache workloads: copy groups the FFN runs behind (0 = fill all misses, "
+                         "then run the FFN)")
     ap.add_argument("--tokens", type=int, default=None,
                     help="override the workload's batch size T (e.g. a decode batch-size sweep)")
     return ap.parse_args()
@@ -327,6 +330,9 @@ def bench_cached(args, wl):
     setup_s = time.time() - t0
 
     def step(i):
+        if args.fill_groups > 0:
+            return layer.forward_streamed(logits[i % nb], xs[i % nb], 0, cache, pool_W, table,
+                                          side=side, groups=args.fill_groups)[1]
         return layer.forward_cached(logits[i % nb], xs[i % nb], 0, cache, pool_W, table,
                                     side=side)[1]
 
@@ -414,9 +420,15 @@ def bench_cached(args, wl):
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": E, "I": wl.I, "k": wl.k,
                    "weights": wl.fmt, "global_batch": wl.T, "pool_slots": S,
                    "domains": wl.domains, "batches_rotated": nb,
-                   "boundary": "route+permute -> counts to host -> expert_cache_lookup -> "
-                               "expert_cache_fill (side stream, pinned bank) -> expert_ffn on "
-                               "the pool via the slot table -> combine; eager",
+                   "boundary": ("route+permute -> counts to host -> expert_cache_lookup -> "
+                                "expert_cache_fill_groups (%d copy groups on a side stream, "
+                                "pinned bank) -> expert_ffn on the pool via the slot table for "
+                                "the hits at once and for each group as it lands -> combine; "
+                                "eager" % args.fill_groups) if args.fill_groups > 0 else
+                               ("route+permute -> counts to host -> expert_cache_lookup -> "
+                                "expert_cache_fill (side stream, pinned bank) -> expert_ffn on "
+                                "the pool via the slot table -> combine; eager"),
+                   "fill_groups": args.fill_groups,
                    "parallelism": "none (1 GPU)", "setup_s": round(setup_s, 1)},
         "cache": {"touched_mean": round(float(np.mean(touched)), 1),
                   "misses_mean": round(float(np.mean(misses)), 1),

@@ -266,6 +266,33 @@ int expert_cache_fill(moe_cache_t cache, int32_t layer, const int32_t* miss_expe
                       const int32_t* miss_slot, int32_t n_miss, moe_stream_t side,
                       moe_stream_t compute);
 
+/* expert_cache_fill_groups — the fills of one lookup as groups that expert
+ * FFN work can run behind (FlashML-org / FreeToken README feature list,
+ * "full-layer double-buffered prefill streaming"; the article on FreeToken's
+ * design, its section on full-layer double-buffered prefill streaming: copy
+ * the next block's weights while the current block computes):
+ *   1. the layer's slot-table row is copied host->device on `compute` (hit
+ *      entries are unchanged; a miss entry names a slot whose bytes land with
+ *      its group);
+ *   2. `side` waits for all work already enqueued on `compute` (no victim slot
+ *      is overwritten while an earlier FFN still reads it);
+ *   3. the misses, in lookup order, are split into n_groups consecutive groups
+ *      of equal size (to within one); group g's copies are issued on `side`
+ *      and its end is recorded in the handle's event g.
+ * `compute` is NOT made to wait: work on `compute` that reads only hit experts
+ * may run at once; work that reads group g's experts must come after
+ * expert_cache_wait_group(g).  n_groups in [1, min(16, n_miss)], or 0 when
+ * n_miss is 0.  Miss arrays as returned by expert_cache_lookup for the same
+ * layer.  Errors leave the copies already enqueued in place.              */
+int expert_cache_fill_groups(moe_cache_t cache, int32_t layer, const int32_t* miss_expert,
+                             const int32_t* miss_slot, int32_t n_miss, int32_t n_groups,
+                             moe_stream_t side, moe_stream_t compute);
+
+/* expert_cache_wait_group — make `compute` wait for group `group` (0..15) of
+ * the latest expert_cache_fill_groups call (a group index past that call's
+ * n_groups names an older, already recorded group). */
+int expert_cache_wait_group(moe_cache_t cache, int32_t group, moe_stream_t compute);
+
 /* Counters since creation: steps, hits, misses, bytes copied host->device. */
 int moe_cache_stats(moe_cache_t cache, int64_t* steps, int64_t* hits, int64_t* misses,
                     int64_t* bytes_filled);

@@ -69,6 +69,8 @@ _SIGS = {
     "moe_cache_destroy": (None, [_p]),
     "expert_cache_lookup": (ctypes.c_int, [_p, _i32, _p, _p, _p, _p, _p, _p]),
     "expert_cache_fill": (ctypes.c_int, [_p, _i32, _p, _p, _i32, _p, _p]),
+    "expert_cache_fill_groups": (ctypes.c_int, [_p, _i32, _p, _p, _i32, _i32, _p, _p]),
+    "expert_cache_wait_group": (ctypes.c_int, [_p, _i32, _p]),
     "moe_cache_stats": (ctypes.c_int, [_p, _p, _p, _p, _p]),
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
@@ -248,6 +250,18 @@ class ExpertCache:
         ms = miss_slot.to(torch.int32).contiguous()
         _check(_lib.expert_cache_fill(self._h, layer, _ptr(me), _ptr(ms), int(me.numel()),
                                       _stream(side), _stream(compute)), "expert_cache_fill")
+
+    def expert_cache_fill_groups(self, layer: int, miss_expert, miss_slot, n_groups: int,
+                                 side=None, compute=None):
+        me = miss_expert.to(torch.int32).contiguous()
+        ms = miss_slot.to(torch.int32).contiguous()
+        _check(_lib.expert_cache_fill_groups(self._h, layer, _ptr(me), _ptr(ms), int(me.numel()),
+                                             n_groups, _stream(side), _stream(compute)),
+               "expert_cache_fill_groups")
+
+    def expert_cache_wait_group(self, group: int, compute=None):
+        _check(_lib.expert_cache_wait_group(self._h, group, _stream(compute)),
+               "expert_cache_wait_group")
 
     def stats(self) -> dict:
         v = [ctypes.c_int64() for _ in range(4)]

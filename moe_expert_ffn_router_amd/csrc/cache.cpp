@@ -16,6 +16,7 @@
 namespace {
 
 constexpr int kRing = 8;
+constexpr int kMaxGroups = 16;  // fill groups of expert_cache_fill_groups
 
 struct Cache {
   int L = 0, E = 0, S = 0;
@@ -33,6 +34,7 @@ struct Cache {
   bool ring_used[kRing] = {};
   int ring_next = 0;
   hipEvent_t compute_mark = nullptr, side_done = nullptr;
+  hipEvent_t group_done[kMaxGroups] = {};
 };
 
 }  // namespace
@@ -71,6 +73,8 @@ extern "C" int moe_cache_create(moe_cache_t* out, int32_t n_layers, int32_t E, i
               hipEventCreateWithFlags(&c->side_done, hipEventDisableTiming) == hipSuccess;
     for (int i = 0; ok && i < kRing; ++i)
       ok = hipEventCreateWithFlags(&c->ring_done[i], hipEventDisableTiming) == hipSuccess;
+    for (int i = 0; ok && i < kMaxGroups; ++i)
+      ok = hipEventCreateWithFlags(&c->group_done[i], hipEventDisableTiming) == hipSuccess;
     if (!ok) {
       moe_cache_destroy(c);
       return set_error(MOE_ERR_HIP, "moe_cache_create: hipEventCreate failed");
@@ -87,6 +91,8 @@ extern "C" void moe_cache_destroy(moe_cache_t c) {
       if (c->ring_used[i]) (void)hipEventSynchronize(c->ring_done[i]);
       (void)hipEventDestroy(c->ring_done[i]);
     }
+  for (int i = 0; i < kMaxGroups; ++i)
+    if (c->group_done[i]) (void)hipEventDestroy(c->group_done[i]);
   if (c->compute_mark) (void)hipEventDestroy(c->compute_mark);
   if (c->side_done) (void)hipEventDestroy(c->side_done);
   if (c->ring) (void)hipHostFree(c->ring);
@@ -200,6 +206,78 @@ extern "C" int expert_cache_fill(moe_cache_t c, int32_t layer, const int32_t* mi
   if (err != hipSuccess)
     return set_error(MOE_ERR_HIP, "expert_cache_fill: %s", hipGetErrorString(err));
   c->st_bytes += (int64_t)n_miss * c->slot_bytes;
+  return MOE_OK;
+}
+
+// The fills of one lookup as groups the caller can compute behind: the slot
+// table row is published on `compute` first (hit entries are unchanged; miss
+// entries name slots whose bytes land with their group), `side` waits for
+// everything already enqueued on `compute` (no victim slot is overwritten
+// while an earlier FFN still reads it), then copies the misses group by group
+// and marks each group's end; `compute` is not made to wait.
+extern "C" int expert_cache_fill_groups(moe_cache_t c, int32_t layer, const int32_t* miss_expert,
+                                        const int32_t* miss_slot, int32_t n_miss,
+                                        int32_t n_groups, moe_stream_t side,
+                                        moe_stream_t compute) {
+  if (!c) return set_error(MOE_ERR_INVALID_ARG, "expert_cache_fill_groups: null handle");
+  if (!c->pool || !c->bank || !c->table_dev || !c->ring)
+    return set_error(MOE_ERR_INVALID_ARG, "expert_cache_fill_groups: handle has no pool/bank/table");
+  if (layer < 0 || layer >= c->L || n_miss < 0 || n_miss > c->E ||
+      (n_miss > 0 && (!miss_expert || !miss_slot)))
+    return set_error(MOE_ERR_INVALID_ARG, "expert_cache_fill_groups: bad layer or miss list");
+  if (n_groups < (n_miss > 0 ? 1 : 0) || n_groups > kMaxGroups || n_groups > (n_miss > 0 ? n_miss : 0))
+    return set_error(MOE_ERR_INVALID_ARG,
+                     "expert_cache_fill_groups: n_groups %d must be in [1, min(%d, n_miss=%d)] "
+                     "(0 when there are no misses)", n_groups, kMaxGroups, n_miss);
+  for (int i = 0; i < n_miss; ++i) {
+    const int e = miss_expert[i], s = miss_slot[i];
+    if (e < 0 || e >= c->E || s < 0 || s >= c->S || c->owner[s] != (int64_t)layer * c->E + e)
+      return set_error(MOE_ERR_INVALID_ARG,
+                       "expert_cache_fill_groups: miss %d (expert %d -> slot %d) is not a pending "
+                       "fill of layer %d", i, e, s, layer);
+  }
+  hipStream_t sd = reinterpret_cast<hipStream_t>(side);
+  hipStream_t cp = reinterpret_cast<hipStream_t>(compute);
+  const int r = c->ring_next;
+  c->ring_next = (r + 1) % kRing;
+  if (c->ring_used[r] && hipEventSynchronize(c->ring_done[r]) != hipSuccess)
+    return set_error(MOE_ERR_HIP, "expert_cache_fill_groups: ring wait failed");
+  int32_t* row = c->ring + (size_t)r * c->E;
+  const int64_t key0 = (int64_t)layer * c->E;
+  for (int e = 0; e < c->E; ++e) row[e] = c->where[key0 + e];
+
+  hipError_t err = hipMemcpyAsync(c->table_dev + key0, row, sizeof(int32_t) * c->E,
+                                  hipMemcpyHostToDevice, cp);
+  if (err == hipSuccess) err = hipEventRecord(c->ring_done[r], cp);
+  if (err == hipSuccess) c->ring_used[r] = true;
+  if (err == hipSuccess) err = hipEventRecord(c->compute_mark, cp);
+  if (err == hipSuccess) err = hipStreamWaitEvent(sd, c->compute_mark, 0);
+  for (int gi = 0; err == hipSuccess && gi < n_groups; ++gi) {
+    const int i0 = (int)((int64_t)n_miss * gi / n_groups);
+    const int i1 = (int)((int64_t)n_miss * (gi + 1) / n_groups);
+    for (int i = i0; err == hipSuccess && i < i1; ++i) {
+      const int e = miss_expert[i], s = miss_slot[i];
+      err = hipMemcpyAsync(c->pool + (size_t)s * c->slot_bytes,
+                           c->bank + ((size_t)layer * c->E + e) * c->slot_bytes, c->slot_bytes,
+                           hipMemcpyHostToDevice, sd);
+    }
+    if (err == hipSuccess) err = hipEventRecord(c->group_done[gi], sd);
+  }
+  if (err != hipSuccess)
+    return set_error(MOE_ERR_HIP, "expert_cache_fill_groups: %s", hipGetErrorString(err));
+  c->st_bytes += (int64_t)n_miss * c->slot_bytes;
+  return MOE_OK;
+}
+
+extern "C" int expert_cache_wait_group(moe_cache_t c, int32_t group, moe_stream_t compute) {
+  if (!c || !c->ring)
+    return set_error(MOE_ERR_INVALID_ARG, "expert_cache_wait_group: handle has no device side");
+  if (group < 0 || group >= kMaxGroups)
+    return set_error(MOE_ERR_INVALID_ARG, "expert_cache_wait_group: group %d of %d", group,
+                     kMaxGroups);
+  if (hipStreamWaitEvent(reinterpret_cast<hipStream_t>(compute), c->group_done[group], 0) !=
+      hipSuccess)
+    return set_error(MOE_ERR_HIP, "expert_cache_wait_group: hipStreamWaitEvent failed");
   return MOE_OK;
 }
 

@@ -4,11 +4,15 @@ Owns the device buffers of one layer (routing results, permutation,
 workspaces, outputs) and issues route -> permute -> expert_ffn -> combine on
 one stream through the C ABI.  With an expert cache, the slot-table path is
 route -> permute -> counts to host -> expert_cache_lookup -> expert_cache_fill
--> expert_ffn (through the slot table) -> combine.  No arithmetic happens
-here; it only sequences library calls.
+-> expert_ffn (through the slot table) -> combine; the streamed variant
+computes the hit experts while the misses are copied, each group of misses
+as soon as it lands, and takes a step that needs more experts than the pool
+has slots in waves.  No arithmetic happens here; it only sequences library
+calls.
 """
 from __future__ import annotations
 
+import numpy as np
 import torch
 
 from . import (Experts, experts, moe_combine, moe_expert_ffn, moe_expert_ffn_workspace,
@@ -18,6 +22,26 @@ from . import (Experts, experts, moe_combine, moe_expert_ffn, moe_expert_ffn_wor
 
 def _i32(n, dev):
     return torch.empty(max(int(n), 1), dtype=torch.int32, device=dev)
+
+
+def plan_waves(counts_host, S: int, resident=None) -> list[list[int]]:
+    """The experts one step needs (counts > 0) in waves of at most S: resident
+    experts first (resident[e] >= 0), each class ascending, so that a wave's
+    fills never evict an expert a later wave of the same step could have hit."""
+    c = np.asarray(counts_host).reshape(-1)
+    needed = [int(e) for e in np.nonzero(c > 0)[0]]
+    if resident is not None:
+        r = np.asarray(resident).reshape(-1)
+        needed = [e for e in needed if r[e] >= 0] + [e for e in needed if r[e] < 0]
+    if not needed:
+        return []
+    return [needed[i:i + S] for i in range(0, len(needed), S)]
+
+
+def split_groups(n: int, groups: int) -> list[tuple[int, int]]:
+    """[i0, i1) of each of `groups` consecutive groups of n items, equal to within one (the
+    split expert_cache_fill_groups makes)."""
+    return [(n * g // groups, n * (g + 1) // groups) for g in range(groups)]
 
 
 class MoELayer:
@@ -130,3 +154,53 @@ class MoELayer:
         self.expert_ffn(pool_W, x, T, row, variant, stream)
         self.combine(T, False, stream)
         return self.y[:T], {"misses": n_miss, "hits": n_hit, "fills": list(zip(me.tolist(), ms.tolist()))}
+
+    def forward_streamed(self, logits: torch.Tensor, x: torch.Tensor, layer: int, cache,
+                         pool_W: Experts, slot_table: torch.Tensor, side=None, groups: int = 4,
+                         variant="auto", stream=None) -> tuple[torch.Tensor, dict]:
+        """Slot-table path with the FFN behind the fills.  Per wave (plan_waves: at most
+        S experts): lookup, then expert_cache_fill_groups (the misses in `groups` copy
+        groups on `side`), the expert FFN over the wave's hit experts at once, and over
+        each group's experts once the group has landed (expert_cache_wait_group).  Every
+        FFN call is moe_expert_ffn with the counts of the other experts zeroed: the same
+        tiles, so y is bit-identical to forward_cached whenever that one fits."""
+        T = logits.shape[0]
+        E = self.E
+        cs = stream if stream is not None else torch.cuda.current_stream()
+        self.route_permute(logits, cs)
+        counts_host = self.counts[:E].to("cpu")          # the one host sync of the step
+        ch = counts_host.numpy()
+        if not hasattr(self, "_rows"):
+            self._rows = {}
+        row_dev = slot_table[layer * E:(layer + 1) * E]
+        waves = plan_waves(ch, cache.S, self._rows.get(layer))
+        n_hit_all = n_miss_all = 0
+        fills = []
+        for wave in waves:
+            cw = np.zeros(E, dtype=np.int32)
+            cw[wave] = ch[wave]
+            me, ms, n_miss, n_hit, row = cache.expert_cache_lookup(layer, torch.from_numpy(cw))
+            self._rows[layer] = row.numpy().copy()
+            G = min(groups, n_miss)
+            miss = me.tolist()
+            masks = np.zeros((1 + G, (E + 3) // 4 * 4), dtype=np.int32)  # rows 16-byte aligned
+            hit = sorted(set(wave) - set(miss))
+            masks[0, hit] = ch[hit]
+            for g, (i0, i1) in enumerate(split_groups(n_miss, G)):
+                masks[1 + g, miss[i0:i1]] = ch[miss[i0:i1]]
+            with torch.cuda.stream(cs):
+                dm = torch.from_numpy(masks).pin_memory().to(self.device, non_blocking=True)
+            cache.expert_cache_fill_groups(layer, me, ms, G, side=side, compute=cs)
+            if hit:
+                moe_expert_ffn(pool_W, row_dev, x, T, self.k, dm[0], self.offsets, self.sorted_idx,
+                               self.y_perm, self.ffn_ws, variant, cs)
+            for g in range(G):
+                cache.expert_cache_wait_group(g, cs)
+                moe_expert_ffn(pool_W, row_dev, x, T, self.k, dm[1 + g], self.offsets,
+                               self.sorted_idx, self.y_perm, self.ffn_ws, variant, cs)
+            n_hit_all += n_hit
+            n_miss_all += n_miss
+            fills += list(zip(me.tolist(), ms.tolist()))
+        self.combine(T, False, cs)
+        return self.y[:T], {"misses": n_miss_all, "hits": n_hit_all, "waves": len(waves),
+                            "fills": fills}

@@ -148,3 +148,121 @@ def test_cache_full_size_fp8_pool():
     wl = synth.WORKLOADS["fp8_lru_pool"]
     flush(f"[cache-full] {wl.name}")
     _run_cache_workload(wl, wl.pool_slots, 3, gen_device="cuda", check_tokens=[0, 2047])
+
+
+# ---------------------------------------------------------------------------
+# streamed path: FFN behind grouped fills, waves when a step needs > S experts
+# ---------------------------------------------------------------------------
+def _pool_set(wl, S, gen_device="cpu"):
+    stride = synth.record_layout(wl.fmt, wl.H, wl.I)["stride"]
+    recs = synth.make_expert_records(wl.fmt, wl.E, wl.H, wl.I, wl.seed, device=gen_device)
+    bank = torch.empty((wl.E, stride), dtype=torch.uint8, pin_memory=True)
+    bank.copy_(recs.cpu())
+    pool = torch.empty((S, stride), dtype=torch.uint8, device=DEV)
+    table = torch.full((wl.E,), -1, dtype=torch.int32, device=DEV)
+    cache = moe.ExpertCache(1, wl.E, S, stride, pool, bank, table)
+    layer = moe.MoELayer(wl.fmt, wl.E, wl.H, wl.I, wl.k, wl.T, stride)
+    pool_W = moe.experts(wl.fmt, wl.E, wl.H, wl.I, pool, stride)
+    return dict(stride=stride, dev=recs.to(DEV), bank=bank, pool=pool, table=table, cache=cache,
+                layer=layer, pool_W=pool_W)
+
+
+def _batch(wl, b):
+    lg = torch.from_numpy(synth.make_logits(wl, b)).to(DEV)
+    x = torch.from_numpy(synth.make_x(wl, b).view(np.int16)).to(DEV).view(torch.bfloat16)
+    return lg, x
+
+
+@pytest.mark.parametrize("fmt,groups", [("fp8_b128", 3), ("mxfp4", 1), ("nvfp4", 4),
+                                        ("bf16", 2)])
+def test_streamed_matches_cached(fmt, groups):
+    """With every step within the pool, the streamed path makes the same fills
+    and gives bit-identical outputs to the one-fill path."""
+    wl = synth.Workload("stream_eq", T=96, H=512, E=32, I=256, k=4, fmt=fmt, seed=47, zipf=1.2,
+                        domains=6, batches=8)
+    S = max(_touched(wl, b) for b in range(8)) + 2
+    flush(f"[stream-eq] {fmt} S={S} groups={groups}")
+    a, s = _pool_set(wl, S), _pool_set(wl, S)
+    side_a, side_s = torch.cuda.Stream(), torch.cuda.Stream()
+    for b in range(8):
+        lg, x = _batch(wl, b)
+        y_a, ia = a["layer"].forward_cached(lg, x, 0, a["cache"], a["pool_W"], a["table"],
+                                            side=side_a)
+        y_s, is_ = s["layer"].forward_streamed(lg, x, 0, s["cache"], s["pool_W"], s["table"],
+                                               side=side_s, groups=groups)
+        torch.cuda.synchronize()
+        assert is_["waves"] == 1 and is_["fills"] == ia["fills"]
+        assert (is_["hits"], is_["misses"]) == (ia["hits"], ia["misses"])
+        assert torch.equal(y_a.view(torch.int16), y_s.view(torch.int16)), f"batch {b}"
+    assert torch.equal(a["table"], s["table"])
+    for d in (a, s):
+        d["cache"].close()
+
+
+@pytest.mark.parametrize("fmt", ["fp8_b128", "mxfp4"])
+def test_streamed_waves_exceed_pool(fmt):
+    """A pool smaller than one step's experts: the streamed path runs the step
+    in waves; fills follow the oracle LRU applied wave by wave, every slot holds
+    its bank record, and y is bit-identical to the all-resident run."""
+    wl = synth.Workload("stream_waves", T=96, H=512, E=32, I=256, k=4, fmt=fmt, seed=48, zipf=1.0,
+                        domains=3, batches=6)
+    S = 6
+    d = _pool_set(wl, S)
+    ora = OL.LruSlots(S)
+    side = torch.cuda.Stream()
+    resident = None
+    for b in range(6):
+        lg, x = _batch(wl, b)
+        y_s, info = d["layer"].forward_streamed(lg, x, 0, d["cache"], d["pool_W"], d["table"],
+                                                side=side, groups=2)
+        y_s = y_s.clone()
+        torch.cuda.synchronize()
+        ids, _ = OR.route(synth.make_logits(wl, b), wl.k)
+        counts, *_ = OP.permute(ids, wl.E)
+        assert int((counts > 0).sum()) > S
+        fills = []
+        from moe_expert_ffn_router_amd.layer import plan_waves
+        waves = plan_waves(counts, S, resident)
+        for wave in waves:
+            cw = np.zeros(wl.E, dtype=np.int64)
+            cw[wave] = counts[wave]
+            fills += ora.step(0, cw)["fills"]
+            resident = ora.slot_table(0, wl.E)
+        assert info["waves"] == len(waves) and info["fills"] == fills, b
+        # all-resident run through the same separate calls
+        lay = d["layer"]
+        lay.route_permute(lg)
+        lay.expert_ffn(lay.weights(d["dev"]), x, wl.T)
+        lay.combine(wl.T, False)
+        y_r = lay.y[:wl.T].clone()
+        torch.cuda.synchronize()
+        assert torch.equal(y_s.view(torch.int16), y_r.view(torch.int16)), f"batch {b}"
+        flush(f"   batch {b}: waves {info['waves']} hits {info['hits']} misses {info['misses']}")
+    tab = d["table"].cpu().numpy()
+    pool_h = d["pool"].cpu()
+    for (L, e), s in ora.where.items():
+        assert tab[e] == s and torch.equal(pool_h[s], d["bank"][e]), (e, s)
+    d["cache"].close()
+
+
+def test_fill_groups_argument_checks():
+    wl = synth.Workload("stream_args", T=64, H=256, E=16, I=128, k=4, fmt="mxfp4", seed=49)
+    d = _pool_set(wl, 4)
+    cache = d["cache"]
+    counts = torch.zeros(wl.E, dtype=torch.int32)
+    counts[:3] = 1
+    me, ms, nm, nh, _ = cache.expert_cache_lookup(0, counts)
+    assert nm == 3
+    for bad in (0, 4, 17):  # 1..min(16, n_miss) only
+        with pytest.raises(moe.MoeError):
+            cache.expert_cache_fill_groups(0, me, ms, bad)
+    with pytest.raises(moe.MoeError):
+        cache.expert_cache_wait_group(16)
+    cache.expert_cache_fill_groups(0, me, ms, 3)
+    for g in range(3):
+        cache.expert_cache_wait_group(g)
+    torch.cuda.synchronize()
+    assert d["table"].cpu().tolist()[:3] == ms.tolist()
+    for i, e in enumerate(me.tolist()):
+        assert torch.equal(d["pool"][ms[i]].cpu(), d["bank"][e])
+    cache.close()
