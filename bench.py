@@ -52,6 +52,9 @@ def parse():
                     help="only run a plain 64 MiB device copy (for HBM counter calibration)")
     ap.add_argument("--resident", action="store_true",
                     help="cache workloads: keep every expert in HBM instead of the slot pool")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="decode-sized workloads: one step = this many MoE layers chained "
+                         "(each layer's y is the next one's x; one graph per run)")
     ap.add_argument("--fill-groups", type=int, default=8,
                     help="cache workloads: copy groups the FFN runs behind (0 = fill all misses, "
                          "then run the FFN)")
@@ -165,10 +168,20 @@ def main():
     # down+combine); otherwise the separate calls
     whole = layer.decode_ws is not None and Ws is None and args.variant == "auto"
 
+    L = args.layers
+    if L > 1 and not whole:
+        print("bench.py: --layers needs a decode-sized workload (whole-layer decode path)",
+              file=sys.stderr)
+        sys.exit(2)
+    stack = [layer] + [moe.MoELayer(wl.fmt, wl.E, wl.H, wl.I, wl.k, wl.T, stride)
+                       for _ in range(L - 1)]
+
     def step(i):
         b = i % nb
         if whole:
-            layer.forward_decode(logits[b], xs[b], Wsets[i % rot])
+            x = xs[b]
+            for li, lay_l in enumerate(stack):  # layer li of step i: its own weight set
+                x = lay_l.forward_decode(logits[(b + li) % nb], x, Wsets[(i * L + li) % rot])
             return
         layer.route_permute(logits[b])
         layer.expert_ffn(Wsets[i % rot], xs[b], wl.T, variant=args.variant)
@@ -218,14 +231,16 @@ def main():
     # else the expert-FFN launches replayed on their own
     ffn_ms = total_ms / steps if whole else timed(ffn_only, warmup) / steps
     ms_per_step = total_ms / steps
-    tokens_per_s = wl.T * steps / (total_ms / 1e3)
+    # MoE-layer tokens: each of the L chained layers of a step processes T tokens
+    tokens_per_s = wl.T * L * steps / (total_ms / 1e3)
 
     # ---- roofline of the dominant kernel (expert FFN) -------------------------
     A = wl.T * wl.k
-    step_batches = [(warmup + i) % nb for i in range(steps)]
+    step_batches = [(warmup + i + li) % nb for i in range(steps) for li in range(L)]
     t_mean = float(np.mean([touched[b] for b in step_batches]))
-    ffn_bytes = t_mean * payload + wl.T * wl.H * 2 + 2 * A * wl.I * 2 + A * wl.H * 2
-    ffn_flops = 2.0 * A * 3 * wl.H * wl.I
+    # per step: L layers (one unless --layers)
+    ffn_bytes = L * (t_mean * payload + wl.T * wl.H * 2 + 2 * A * wl.I * 2 + A * wl.H * 2)
+    ffn_flops = L * 2.0 * A * 3 * wl.H * wl.I
     # binding roofline: the larger of the HBM floor and the MFMA floor
     # (bf16 rate: the rate of the instructions the prefill kernels issue)
     t_hbm = ffn_bytes / (HBM_PEAK_GBS * 1e9)
@@ -241,10 +256,10 @@ def main():
                 "traffic": None}
     if whole:
         # the two launches also read logits, write routing outputs and y
-        ffn_bytes += wl.T * wl.E * 4 + wl.T * wl.H * 2
+        ffn_bytes += L * (wl.T * wl.E * 4 + wl.T * wl.H * 2)
         achieved = ffn_bytes / (ffn_ms / 1e3) / 1e9
         roof.update({"achieved": round(achieved, 1), "frac": round(achieved / HBM_PEAK_GBS, 4)})
-    if use_graph and args.tokens is None:
+    if use_graph and args.tokens is None and L == 1:
         # HBM bytes per step of the timed kernels, from the committed counter
         # readings of this workload's configuration (None without them)
         roof["traffic"] = measured_traffic(wl.name)
@@ -253,8 +268,9 @@ def main():
                             "moe_forward_decode (4 launches)" if whole
                             else "moe_expert_ffn (gate/up + down launches)"),
                  "ffn_ms": round(ffn_ms, 5),
-                 "timing": ("HIP events around one replay of a graph of the %d launches"
-                            % steps) if use_graph else "HIP events, eager",
+                 "timing": ("HIP events around one replay of a graph of the %d steps"
+                            % steps + (" (%d layers each)" % L if L > 1 else ""))
+                           if use_graph else "HIP events, eager",
                  "algorithmic_bytes_per_launch": int(ffn_bytes),
                  "algorithmic_flops_per_launch": int(ffn_flops),
                  "touched_experts_mean": round(t_mean, 2)})
@@ -280,6 +296,7 @@ def main():
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "I": wl.I, "k": wl.k,
                    "weights": wl.fmt, "shared_I": wl.shared_I, "global_batch": wl.T,
                    "weight_sets_rotated": rot, "batches_rotated": nb,
+                   "layers_per_step": L, "us_per_layer": round(ms_per_step * 1e3 / L, 2),
                    "boundary": ("route->permute->expert_ffn->combine on one stream, "
                                 + ("as two whole-layer launches, " if whole else "")
                                 + ("one captured HIP graph of the K steps" if use_graph

@@ -9,7 +9,8 @@
 * repeated calls with varying batch sizes on one workspace and
   bit-repeatable results;
 * slot-table indirection;
-* replays of a captured graph, checked against eager results every time.
+* replays of a captured graph, checked against eager results every time,
+  also for several layers chained in one graph.
 """
 from __future__ import annotations
 
@@ -191,6 +192,59 @@ def test_decode_layer_graph_replays_match_eager():
         for o, e in zip(outs, eager):
             assert torch.equal(o.view(torch.int16), e.view(torch.int16)), f"replay {rep}"
         layer.forward_decode(batches[1][0], batches[1][1], W)  # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_chained_layers_in_one_graph():
+    """Several decode layers chained (each layer's y is the next one's x), captured
+    once: every replay reproduces the eager chain bit for bit, and each layer's
+    output matches the oracle given the bf16 input that layer actually received."""
+    wl = DEC["mxfp4"]
+    L = 4
+    flush("[decode-chain-graph] L=%d" % L)
+    layers, Ws, logits = [], [], []
+    for li in range(L):
+        recs = synth.make_expert_records(wl.fmt, wl.E, wl.H, wl.I, wl.seed, layer=li,
+                                         device="cuda").to(DEV)
+        lay = moe.MoELayer(wl.fmt, wl.E, wl.H, wl.I, wl.k, wl.T, recs.shape[1])
+        layers.append((lay, recs))
+        Ws.append(lay.weights(recs))
+        logits.append(torch.from_numpy(synth.make_logits(wl, 300 + li)).to(DEV))
+    x0 = torch.from_numpy(synth.make_x(wl, 300).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+    def chain():
+        x = x0
+        for (lay, _), W, lg in zip(layers, Ws, logits):
+            x = lay.forward_decode(lg, x, W)
+        return x
+
+    ins, outs = [x0.clone()], []
+    x = x0
+    for (lay, _), W, lg in zip(layers, Ws, logits):
+        x = lay.forward_decode(lg, x, W)
+        torch.cuda.synchronize()
+        outs.append(x.clone())
+        ins.append(x.clone())
+    eager = outs[-1]
+
+    # per layer against the oracle, on the input that layer saw
+    for li, (lay, recs) in enumerate(layers):
+        rec_np = recs.cpu().numpy()
+        ex = OL.ExpertSet(wl.fmt, wl.H, wl.I, lambda e, r=rec_np: r[e])
+        xin = ins[li].view(torch.int16).cpu().numpy().view(np.uint16)
+        ref = OL.forward(logits[li].cpu().numpy(), xin, wl.k, ex)
+        assert rel_err(bf16_to_np(outs[li]), ref["y"]) <= TOL, f"layer {li}"
+
+    out = torch.empty_like(eager)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out.copy_(chain())
+    for rep in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+        layers[1][0].forward_decode(logits[0], x0, Ws[1])  # eager work between replays
         torch.cuda.synchronize()
 
 
