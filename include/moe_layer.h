@@ -293,6 +293,34 @@ int expert_cache_fill_groups(moe_cache_t cache, int32_t layer, const int32_t* mi
  * n_groups names an older, already recorded group). */
 int expert_cache_wait_group(moe_cache_t cache, int32_t group, moe_stream_t compute);
 
+/* moe_cache_resize — change the pool to new_S slots at run time, without
+ * reloading the experts that stay resident (FlashML-org / FreeToken README
+ * feature list, elastic VRAM: the expert cache and the KV cache re-split while
+ * the engine runs; guide, "expert bank & LRU slot cache": the LRU keeps each
+ * (layer, expert)'s last active step).  The pages give no rule for what a
+ * smaller pool keeps; read here as LRU order:
+ *   kept   = the min(new_S, resident count) residents with the latest
+ *            last-active step (ties: lower slot); the others are dropped
+ *   placed = kept residents in ascending old-slot order into slots 0, 1, ...
+ *   last-active steps and the step clock are unchanged.
+ *   new_pool_dev  device, new_S * slot_bytes bytes: the pool from now on; or
+ *                 NULL to keep the current pool, which must then hold
+ *                 new_S * slot_bytes bytes (the caller's allocation)
+ *   move_from, move_to  host int32 [min(S, new_S)] (out, may be NULL): old and
+ *                 new slot of every kept resident, in placement order
+ *   n_moves       host (out, may be NULL): number of kept residents
+ * Device side (handles created with pool, bank and table): `compute` waits
+ * for every fill already issued on `side`; kept records are copied device to
+ * device on `compute` (in place, only those whose slot changes; the ascending
+ * packing never overwrites a record before it has moved); every layer's
+ * slot-table row is rewritten; the call returns once `compute` has drained
+ * (host-synchronous, not for graph capture), so the old pool may be freed on
+ * return.  Host-only handles update the metadata alone (new_pool_dev NULL).
+ * Experts descriptors built over the old pool must be rebuilt over the new. */
+int moe_cache_resize(moe_cache_t cache, int32_t new_S, void* new_pool_dev, int32_t* move_from,
+                     int32_t* move_to, int32_t* n_moves, moe_stream_t side,
+                     moe_stream_t compute);
+
 /* Counters since creation: steps, hits, misses, bytes copied host->device. */
 int moe_cache_stats(moe_cache_t cache, int64_t* steps, int64_t* hits, int64_t* misses,
                     int64_t* bytes_filled);

@@ -71,6 +71,7 @@ _SIGS = {
     "expert_cache_fill": (ctypes.c_int, [_p, _i32, _p, _p, _i32, _p, _p]),
     "expert_cache_fill_groups": (ctypes.c_int, [_p, _i32, _p, _p, _i32, _i32, _p, _p]),
     "expert_cache_wait_group": (ctypes.c_int, [_p, _i32, _p]),
+    "moe_cache_resize": (ctypes.c_int, [_p, _i32, _p, _p, _p, _p, _p, _p]),
     "moe_cache_stats": (ctypes.c_int, [_p, _p, _p, _p, _p]),
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
@@ -262,6 +263,21 @@ class ExpertCache:
     def expert_cache_wait_group(self, group: int, compute=None):
         _check(_lib.expert_cache_wait_group(self._h, group, _stream(compute)),
                "expert_cache_wait_group")
+
+    def moe_cache_resize(self, new_S: int, pool=None, side=None, compute=None):
+        """Resize to new_S slots (into `pool` if given, else in place); returns the
+        (old slot, new slot) pairs of the kept residents as two int32 tensors."""
+        m = min(self.S, new_S)
+        frm = torch.zeros(m, dtype=torch.int32)
+        to = torch.zeros(m, dtype=torch.int32)
+        n = ctypes.c_int32()
+        _check(_lib.moe_cache_resize(self._h, new_S, _ptr(pool), _ptr(frm), _ptr(to),
+                                     ctypes.byref(n), _stream(side), _stream(compute)),
+               "moe_cache_resize")
+        self.S = new_S
+        if pool is not None:
+            self._keep = (pool,) + self._keep[1:]
+        return frm[:n.value].clone(), to[:n.value].clone()
 
     def stats(self) -> dict:
         v = [ctypes.c_int64() for _ in range(4)]

@@ -8,6 +8,7 @@
 // earlier copy from it may still be pending).
 #include <string.h>
 
+#include <algorithm>
 #include <new>
 #include <vector>
 
@@ -278,6 +279,76 @@ extern "C" int expert_cache_wait_group(moe_cache_t c, int32_t group, moe_stream_
   if (hipStreamWaitEvent(reinterpret_cast<hipStream_t>(compute), c->group_done[group], 0) !=
       hipSuccess)
     return set_error(MOE_ERR_HIP, "expert_cache_wait_group: hipStreamWaitEvent failed");
+  return MOE_OK;
+}
+
+// Elastic pool size: keep the residents used most recently (ties: lower slot),
+// as many as the new size allows, pack them in their old slot order into the
+// lowest slots, drop the rest.  Packing in ascending order only ever moves a
+// record down to a slot that is free or already vacated, so in-place moves on
+// one stream never overwrite a record that is still to be moved.
+extern "C" int moe_cache_resize(moe_cache_t c, int32_t new_S, void* new_pool_dev,
+                                int32_t* move_from, int32_t* move_to, int32_t* n_moves,
+                                moe_stream_t side, moe_stream_t compute) {
+  if (!c) return set_error(MOE_ERR_INVALID_ARG, "moe_cache_resize: null handle");
+  if (new_S < 1) return set_error(MOE_ERR_INVALID_ARG, "moe_cache_resize: new_S %d < 1", new_S);
+  const bool dev = c->pool && c->bank && c->table_dev && c->ring;
+  if (!dev && new_pool_dev)
+    return set_error(MOE_ERR_INVALID_ARG, "moe_cache_resize: handle has no device pool to move");
+  const int S = c->S;
+  std::vector<int> res;
+  for (int s = 0; s < S; ++s)
+    if (c->owner[s] >= 0) res.push_back(s);
+  // most recent first, lower slot first among equals
+  std::vector<int> order(res);
+  std::sort(order.begin(), order.end(), [&](int a, int b) {
+    return c->recency[a] != c->recency[b] ? c->recency[a] > c->recency[b] : a < b;
+  });
+  const int n_keep = (int)order.size() < new_S ? (int)order.size() : new_S;
+  std::vector<char> keep(S, 0);
+  for (int i = 0; i < n_keep; ++i) keep[order[i]] = 1;
+  std::vector<int> from;
+  for (int s : res)
+    if (keep[s]) from.push_back(s);  // ascending old slot
+
+  uint8_t* dst_pool = new_pool_dev ? static_cast<uint8_t*>(new_pool_dev) : c->pool;
+  std::vector<int64_t> owner(new_S, -1), recency(new_S, -1);
+  for (int p = 0; p < n_keep; ++p) {
+    owner[p] = c->owner[from[p]];
+    recency[p] = c->recency[from[p]];
+  }
+  std::vector<int32_t> where((size_t)c->L * c->E, -1);
+  for (int p = 0; p < n_keep; ++p) where[owner[p]] = p;
+
+  if (dev) {
+    hipStream_t sd = reinterpret_cast<hipStream_t>(side);
+    hipStream_t cp = reinterpret_cast<hipStream_t>(compute);
+    // every fill already issued on `side` lands before anything moves
+    hipError_t err = hipEventRecord(c->side_done, sd);
+    if (err == hipSuccess) err = hipStreamWaitEvent(cp, c->side_done, 0);
+    for (int p = 0; err == hipSuccess && p < n_keep; ++p) {
+      if (dst_pool == c->pool && from[p] == p) continue;
+      err = hipMemcpyAsync(dst_pool + (size_t)p * c->slot_bytes,
+                           c->pool + (size_t)from[p] * c->slot_bytes, c->slot_bytes,
+                           hipMemcpyDeviceToDevice, cp);
+    }
+    if (err == hipSuccess)
+      err = hipMemcpyAsync(c->table_dev, where.data(), sizeof(int32_t) * where.size(),
+                           hipMemcpyHostToDevice, cp);
+    if (err == hipSuccess) err = hipStreamSynchronize(cp);
+    if (err != hipSuccess)
+      return set_error(MOE_ERR_HIP, "moe_cache_resize: %s", hipGetErrorString(err));
+  }
+  c->pool = dst_pool;
+  c->S = new_S;
+  c->owner.swap(owner);
+  c->recency.swap(recency);
+  c->where.swap(where);
+  for (int p = 0; p < n_keep; ++p) {
+    if (move_from) move_from[p] = from[p];
+    if (move_to) move_to[p] = p;
+  }
+  if (n_moves) *n_moves = n_keep;
   return MOE_OK;
 }
 

@@ -20,8 +20,16 @@ reading, taken here, is:
 Outputs per step: the slot of every needed expert, the (expert, slot) fills in
 order, hit and miss counts.
 
+Resize (README feature list, elastic VRAM: the pool changes size while the
+engine runs, no reload).  The pages give no rule for what a smaller pool
+keeps; the reading taken is LRU order: keep the min(new S, resident count)
+residents with the latest recency (ties: lower slot), drop the rest, and place
+the kept ones, in ascending order of their old slot, into slots 0, 1, ...;
+recencies and the clock are unchanged.
+
 Parity: pinned by a hand-worked trace (tests/golden), by the textbook LRU
-stack-distance rule on single-expert steps, and by invariants.
+stack-distance rule on single-expert steps, by a textbook recency-list LRU
+whose capacity changes between steps, and by invariants.
 """
 from __future__ import annotations
 
@@ -71,6 +79,23 @@ class LruSlots:
             "hits": len(needed) - len(misses),
             "misses": len(misses),
         }
+
+    def resize(self, new_S: int) -> list:
+        """New pool size; returns the (old slot, new slot) of every kept resident."""
+        if new_S < 1:
+            raise ValueError("S >= 1")
+        resident = [s for s in range(self.S) if self.owner[s] is not None]
+        by_recency = sorted(resident, key=lambda q: (-self.recency[q], q))
+        kept = sorted(by_recency[:new_S])
+        owner = [None] * new_S
+        recency = [-1] * new_S
+        moves = []
+        for p, q in enumerate(kept):
+            owner[p], recency[p] = self.owner[q], self.recency[q]
+            moves.append((q, p))
+        self.S, self.owner, self.recency = new_S, owner, recency
+        self.where = {key: p for p, key in enumerate(owner) if key is not None}
+        return moves
 
     def slot_table(self, layer: int, E: int) -> np.ndarray:
         """Slot of every expert of `layer` that is resident, -1 otherwise."""

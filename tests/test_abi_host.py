@@ -142,6 +142,46 @@ def test_cpp_lru_matches_oracle(seed):
     assert st["bytes_filled"] == 0 and st["steps"] > 0
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_cpp_resize_matches_oracle(seed):
+    """Pool resizes between steps (host-only handle): the same kept residents and
+    placements as the oracle, then the same fills."""
+    rng = np.random.default_rng(40 + seed)
+    L, E, S = 3, 32, 12
+    cpp = m.ExpertCache(L, E, S, 256)
+    ora = OL.LruSlots(S)
+    for step in range(250):
+        if rng.random() < 0.08:
+            new_S = int(rng.integers(1, 20))
+            frm, to = cpp.moe_cache_resize(new_S, side=0, compute=0)
+            assert list(zip(frm.tolist(), to.tolist())) == ora.resize(new_S)
+            for layer in range(L):
+                counts = np.zeros(E, np.int32)
+                _, _, nm, nh, row = cpp.expert_cache_lookup(layer, torch.from_numpy(counts))
+                assert np.array_equal(row.numpy(), ora.slot_table(layer, E))
+                ora.step(layer, counts)
+            continue
+        layer = int(rng.integers(0, L))
+        n = int(rng.integers(0, ora.S + 1))
+        counts = np.zeros(E, np.int32)
+        counts[rng.permutation(E)[:n]] = rng.integers(1, 9, size=n)
+        r = ora.step(layer, counts)
+        me, ms, nm, nh, row = cpp.expert_cache_lookup(layer, torch.from_numpy(counts))
+        assert list(zip(me.tolist(), ms.tolist())) == r["fills"]
+        assert np.array_equal(row.numpy(), ora.slot_table(layer, E))
+
+
+def test_cache_resize_argument_checks():
+    c = m.ExpertCache(1, 8, 3, 256)
+    with pytest.raises(m.MoeError) as e:
+        c.moe_cache_resize(0, side=0, compute=0)
+    assert e.value.status == m.MOE_ERR_INVALID_ARG
+    with pytest.raises(m.MoeError) as e:   # host-only handle: no pool to move into
+        c.moe_cache_resize(4, pool=torch.zeros(4 * 256, dtype=torch.uint8), side=0, compute=0)
+    assert e.value.status == m.MOE_ERR_INVALID_ARG
+    assert c.S == 3
+
+
 def test_cache_fill_requires_device_pieces():
     c = m.ExpertCache(1, 8, 3, 256)
     with pytest.raises(m.MoeError):

@@ -107,3 +107,85 @@ def test_compulsory_misses_only_when_everything_fits():
         misses += r["misses"]
         seen |= set(r["needed"])
     assert misses == len(seen)
+
+
+def test_resize_hand_worked():
+    """S = 4, one layer: experts 1, 2, 3, 4 fill slots 0..3 at steps 0..3, expert 2
+    is used again at step 4.  Shrinking to 2 keeps the two most recently used
+    (expert 2 in slot 1, step 4; expert 4 in slot 3, step 3), packed in slot
+    order; growing to 3 keeps both where they are; the next miss takes slot 2."""
+    c = lru.LruSlots(4)
+    for e in (1, 2, 3, 4, 2):
+        counts = np.zeros(8, np.int32)
+        counts[e] = 1
+        c.step(0, counts)
+    assert c.resize(2) == [(1, 0), (3, 1)]
+    assert c.slot_table(0, 8).tolist() == [-1, -1, 0, -1, 1, -1, -1, -1]
+    assert c.resize(3) == [(0, 0), (1, 1)]
+    counts = np.zeros(8, np.int32)
+    counts[[2, 5]] = 1
+    r = c.step(0, counts)
+    assert r["fills"] == [(5, 2)] and r["hits"] == 1
+
+
+def _textbook_lru_hits(seq, caps):
+    """Textbook LRU as a recency list (most recent first) whose capacity is
+    caps[i] when access i is made: a key is cached iff it is among the first
+    `capacity` entries; a capacity change truncates the list."""
+    stack, hits = [], []
+    for key, cap in zip(seq, caps):
+        del stack[cap:]
+        hits.append(key in stack)
+        if key in stack:
+            stack.remove(key)
+        stack.insert(0, key)
+        del stack[cap:]
+    return hits
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_resize_single_expert_steps_match_textbook_lru(seed):
+    rng = np.random.default_rng(50 + seed)
+    seq = [(int(rng.integers(0, 3)), int(rng.integers(0, 10))) for _ in range(300)]
+    caps, cap = [], int(rng.integers(1, 8))
+    for i in range(len(seq)):
+        if i and rng.random() < 0.05:
+            cap = int(rng.integers(1, 12))
+        caps.append(cap)
+    c = lru.LruSlots(caps[0])
+    got = []
+    for (layer, e), cap in zip(seq, caps):
+        if cap != c.S:
+            c.resize(cap)
+        counts = np.zeros(10, np.int32)
+        counts[e] = 2
+        got.append(c.step(layer, counts)["hits"] == 1)
+    assert got == _textbook_lru_hits(seq, caps)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_resize_invariants_multi_expert(seed):
+    rng = np.random.default_rng(300 + seed)
+    E = 24
+    c = lru.LruSlots(10)
+    for step in range(200):
+        if rng.random() < 0.1:
+            new_S = int(rng.integers(1, 16))
+            before = {key: (s, c.recency[s]) for key, s in c.where.items()}
+            moves = c.resize(new_S)
+            kept = {c.owner[p] for p in range(len(moves))}
+            assert len(moves) == min(new_S, len(before)) == len(c.where)
+            assert [p for _, p in moves] == list(range(len(moves)))
+            assert [q for q, _ in moves] == sorted(q for q, _ in moves)
+            for q, p in moves:                          # bytes follow their owner
+                assert before[c.owner[p]][0] == q
+            if kept:                                    # nothing dropped is more recent
+                worst = min(before[k][1] for k in kept)
+                assert all(r <= worst for k, (s, r) in before.items() if k not in kept)
+            continue
+        layer = int(rng.integers(0, 2))
+        n = int(rng.integers(0, c.S + 1))
+        counts = np.zeros(E, np.int32)
+        counts[rng.permutation(E)[:n]] = 1
+        r = c.step(layer, counts)
+        assert len(set(r["slot_of"].values())) == n and all(0 <= s < c.S for s in r["slot_of"].values())

@@ -132,6 +132,35 @@ class _LruMru(LR.LruSlots):
                 "fills": fills, "hits": len(needed) - len(misses), "misses": len(misses)}
 
 
+class _LruResizeKeepsOldest(LR.LruSlots):
+    def resize(self, new_S):
+        # keeps the LEAST recently used residents
+        resident = [s for s in range(self.S) if self.owner[s] is not None]
+        kept = sorted(sorted(resident, key=lambda q: (self.recency[q], q))[:new_S])
+        owner = [self.owner[q] for q in kept] + [None] * (new_S - len(kept))
+        recency = [self.recency[q] for q in kept] + [-1] * (new_S - len(kept))
+        self.S, self.owner, self.recency = new_S, owner, recency
+        self.where = {key: p for p, key in enumerate(owner) if key is not None}
+        return [(q, p) for p, q in enumerate(kept)]
+
+
+class _LruResizeNoPacking(LR.LruSlots):
+    def resize(self, new_S):
+        # keeps the right residents but leaves them in their old slots when they fit
+        resident = [s for s in range(self.S) if self.owner[s] is not None]
+        kept = sorted(sorted(resident, key=lambda q: (-self.recency[q], q))[:new_S])
+        owner, recency = [None] * new_S, [-1] * new_S
+        free = [p for p in range(new_S) if p not in kept]
+        moves = []
+        for q in kept:
+            p = q if q < new_S else free.pop(0)
+            owner[p], recency[p] = self.owner[q], self.recency[q]
+            moves.append((q, p))
+        self.S, self.owner, self.recency = new_S, owner, recency
+        self.where = {key: p for p, key in enumerate(owner) if key is not None}
+        return moves
+
+
 CASES = [
     ("e2m1 exponent bias", F, "e2m1_value", _e2m1_wrong_bias, lambda: T_fmt.test_e2m1_published_table()),
     ("nibble order", F, "unpack_e2m1", _unpack_swapped, lambda: T_fmt.test_nibble_order_low_first()),
@@ -143,6 +172,10 @@ CASES = [
     ("combine weight order", C, "combine", _combine_reversed, lambda: T_ffn.test_combine_k1_and_one_hot()),
     ("gate/up swapped in decode", F, "decode_record", _decode_gate_up_swapped, lambda: test_bf16_record_gate_rows_first()),
     ("LRU evicts most recent", LR, "LruSlots", _LruMru, lambda: T_lru.test_hand_worked_trace()),
+    ("resize keeps least recent", LR, "LruSlots", _LruResizeKeepsOldest,
+     lambda: [T_lru.test_resize_single_expert_steps_match_textbook_lru(s) for s in range(8)]),
+    ("resize does not pack", LR, "LruSlots", _LruResizeNoPacking,
+     lambda: T_lru.test_resize_hand_worked()),
 ]
 
 
