@@ -55,6 +55,11 @@ def parse():
     ap.add_argument("--layers", type=int, default=1,
                     help="decode-sized workloads: one step = this many MoE layers chained "
                          "(each layer's y is the next one's x; one graph per run)")
+    ap.add_argument("--slots", type=int, default=None,
+                    help="cache workloads: pool slots (default: the workload's)")
+    ap.add_argument("--slot-sweep", type=str, default=None,
+                    help="cache workloads: comma-separated pool sizes; replays the run's routing "
+                         "through the same LRU policy at each size (misses per layer-step)")
     ap.add_argument("--fill-groups", type=int, default=8,
                     help="cache workloads: copy groups the FFN runs behind (0 = fill all misses, "
                          "then run the FFN)")
@@ -170,8 +175,8 @@ def main():
 
     L = args.layers
     if L > 1 and not whole:
-        print("bench.py: --layers needs a decode-sized workload (whole-layer decode path)",
-              file=sys.stderr)
+        print("bench.py: --layers needs a decode-sized workload (whole-layer decode path) "
+              "or a cache workload", file=sys.stderr)
         sys.exit(2)
     stack = [layer] + [moe.MoELayer(wl.fmt, wl.E, wl.H, wl.I, wl.k, wl.T, stride)
                        for _ in range(L - 1)]
@@ -327,48 +332,98 @@ def bench_cached(args, wl):
     dev = torch.device("cuda")
     lay = synth.record_layout(wl.fmt, wl.H, wl.I)
     stride, payload = lay["stride"], lay["payload"]
-    E, S = wl.E, wl.pool_slots
+    E = wl.E
+    S = args.slots or wl.pool_slots
+    L = args.layers  # a stack of L layers sharing the one pool, keys (layer, expert)
 
     t0 = time.time()
-    bank = torch.empty((E, stride), dtype=torch.uint8, pin_memory=True)
-    for e0 in range(0, E, 16):
-        ids = list(range(e0, min(E, e0 + 16)))
-        bank[e0:e0 + len(ids)].copy_(
-            synth.make_expert_records(wl.fmt, E, wl.H, wl.I, wl.seed, device=dev, experts=ids))
+    bank = torch.empty((L * E, stride), dtype=torch.uint8, pin_memory=True)
+    for li in range(L):
+        for e0 in range(0, E, 16):
+            ids = list(range(e0, min(E, e0 + 16)))
+            bank[li * E + e0:li * E + e0 + len(ids)].copy_(
+                synth.make_expert_records(wl.fmt, E, wl.H, wl.I, wl.seed, layer=li, device=dev,
+                                          experts=ids))
     pool = torch.empty((S, stride), dtype=torch.uint8, device=dev)
-    table = torch.full((E,), -1, dtype=torch.int32, device=dev)
-    cache = moe.ExpertCache(1, E, S, stride, pool, bank, table)
+    table = torch.full((L * E,), -1, dtype=torch.int32, device=dev)
+    cache = moe.ExpertCache(L, E, S, stride, pool, bank, table)
     layer = moe.MoELayer(wl.fmt, E, wl.H, wl.I, wl.k, wl.T, stride)
     pool_W = moe.experts(wl.fmt, E, wl.H, wl.I, pool, stride)
-    logits = [torch.from_numpy(synth.make_logits(wl, b)).to(dev) for b in range(nb)]
+    logits = [[torch.from_numpy(synth.make_logits(wl, b, layer=li)).to(dev) for b in range(nb)]
+              for li in range(L)]
     xs = [torch.from_numpy(synth.make_x(wl, b).view(np.int16)).to(dev).view(torch.bfloat16)
           for b in range(nb)]
     side = torch.cuda.Stream()
     setup_s = time.time() - t0
 
     def step(i):
-        if args.fill_groups > 0:
-            return layer.forward_streamed(logits[i % nb], xs[i % nb], 0, cache, pool_W, table,
-                                          side=side, groups=args.fill_groups)[1]
-        return layer.forward_cached(logits[i % nb], xs[i % nb], 0, cache, pool_W, table,
-                                    side=side)[1]
+        """One step: every layer of the stack on batch i (each layer's own router logits)."""
+        infos = []
+        for li in range(L):
+            lg, x = logits[li][i % nb], xs[i % nb]
+            if args.fill_groups > 0:
+                infos.append(layer.forward_streamed(lg, x, li, cache, pool_W, table, side=side,
+                                                    groups=args.fill_groups)[1])
+            else:
+                infos.append(layer.forward_cached(lg, x, li, cache, pool_W, table,
+                                                  side=side)[1])
+        return infos
 
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     st0 = cache.stats()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    touched, misses = [], []
+    touched, misses, waves = [], [], []
     start.record()
     for i in range(steps):
-        info = step(warmup + i)
-        touched.append(info["hits"] + info["misses"])
-        misses.append(info["misses"])
+        for info in step(warmup + i):
+            touched.append(info["hits"] + info["misses"])
+            misses.append(info["misses"])
+            waves.append(info.get("waves", 1))
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     st1 = cache.stats()
     filled = st1["bytes_filled"] - st0["bytes_filled"]
+
+    # miss rate against pool size: the run's own routing (device route + permute, counts
+    # to host) replayed through the same policy on host-only handles, waves as above
+    sweep = None
+    if args.slot_sweep:
+        from moe_expert_ffn_router_amd.layer import plan_waves
+        counts = {}
+        for li in range(L):
+            for b in range(nb):
+                layer.route_permute(logits[li][b])
+                counts[li, b] = layer.counts[:E].cpu().numpy().copy()
+        sweep = []
+        for S_s in [int(v) for v in args.slot_sweep.split(",")]:
+            h = moe.ExpertCache(L, E, S_s, stride)
+            m_t = n_t = w_t = 0
+            for i in range(warmup + steps):
+                for li in range(L):
+                    c = counts[li, i % nb]
+                    for wave in plan_waves(c, S_s, h.expert_cache_row(li).numpy()):
+                        cw = np.zeros(E, dtype=np.int32)
+                        cw[wave] = c[wave]
+                        _, _, nm, nh, _ = h.expert_cache_lookup(li, torch.from_numpy(cw))
+                        if i >= warmup:
+                            m_t, n_t, w_t = m_t + nm, n_t + nm + nh, w_t + 1
+            h.close()
+            sweep.append({"slots": S_s, "misses_per_layer_step": round(m_t / (steps * L), 2),
+                          "hit_rate": round(1 - m_t / max(1, n_t), 4),
+                          "waves_per_layer_step": round(w_t / (steps * L), 2),
+                          "fill_gb_per_layer_step": round(m_t * payload / (steps * L) / 1e9, 3)})
+
+    # elastic resize of the live pool (in place): halve it, keeping the most recently
+    # used residents, then grow back; wall time of each host-synchronous call
+    t_r = time.time()
+    cache.moe_cache_resize(max(1, S // 2), side=side)
+    shrink_ms = (time.time() - t_r) * 1e3
+    t_r = time.time()
+    cache.moe_cache_resize(S, side=side)
+    grow_ms = (time.time() - t_r) * 1e3
 
     # pinned host -> HBM copy rate of this box (the fill path's ceiling)
     n_copy = min(64, S)
@@ -384,7 +439,7 @@ def bench_cached(args, wl):
     # hit path: the expert FFN on the pool with every expert of the last batch resident,
     # replayed in a graph (slot table: touched expert -> its slot)
     b = (warmup + steps - 1) % nb
-    layer.route_permute(logits[b])
+    layer.route_permute(logits[0][b])
     ids_needed = torch.nonzero(layer.counts[:E] > 0).flatten().to(torch.int32)
     ident = torch.full((E,), 0, dtype=torch.int32, device=dev)
     ident[ids_needed.long()] = torch.arange(len(ids_needed), dtype=torch.int32, device=dev)
@@ -419,11 +474,11 @@ def bench_cached(args, wl):
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, bank, None, args.cpu_seconds)
+        cpu = cpu_baseline(wl, bank[:E], None, args.cpu_seconds)
 
     out = {
         "metric": "MoE-layer tokens/s at 1 GPU; % HBM roofline (decode), % MFMA peak (prefill)",
-        "value": round(wl.T * steps / (total_ms / 1e3), 1),
+        "value": round(wl.T * L * steps / (total_ms / 1e3), 1),  # MoE-layer tokens
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": steps,
@@ -436,6 +491,7 @@ def bench_cached(args, wl):
         "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": E, "I": wl.I, "k": wl.k,
                    "weights": wl.fmt, "global_batch": wl.T, "pool_slots": S,
+                   "layers_per_step": L, "ms_per_layer": round(total_ms / steps / L, 4),
                    "domains": wl.domains, "batches_rotated": nb,
                    "boundary": ("route+permute -> counts to host -> expert_cache_lookup -> "
                                 "expert_cache_fill_groups (%d copy groups on a side stream, "
@@ -449,10 +505,15 @@ def bench_cached(args, wl):
                    "parallelism": "none (1 GPU)", "setup_s": round(setup_s, 1)},
         "cache": {"touched_mean": round(float(np.mean(touched)), 1),
                   "misses_mean": round(float(np.mean(misses)), 1),
+                  "waves_mean": round(float(np.mean(waves)), 2),
+                  "per": "layer-step",
                   "hit_rate": round(1 - sum(misses) / max(1, sum(touched)), 4),
                   "bytes_filled": int(filled),
                   "fill_gb_per_step": round(filled / steps / 1e9, 3),
-                  "pinned_h2d_gbs": round(h2d_gbs, 1)},
+                  "pinned_h2d_gbs": round(h2d_gbs, 1),
+                  "resize_ms": {"to_%d" % max(1, S // 2): round(shrink_ms, 2),
+                                "to_%d" % S: round(grow_ms, 2)},
+                  "slot_sweep": sweep},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

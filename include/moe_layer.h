@@ -253,6 +253,12 @@ int expert_cache_lookup(moe_cache_t cache, int32_t layer, const int32_t* counts_
                         int32_t* miss_expert, int32_t* miss_slot, int32_t* n_miss,
                         int32_t* n_hit, int32_t* slot_row_host);
 
+/* expert_cache_row — the current slot of every expert of `layer` (host int32
+ * [E] out; -1 = not resident), as the policy state stands now (other layers'
+ * lookups may have evicted some since this layer's last lookup).  Host-only;
+ * changes nothing. */
+int expert_cache_row(moe_cache_t cache, int32_t layer, int32_t* slot_row_host);
+
 /* expert_cache_fill — make the lookup's misses resident and publish the slot
  * table row for `layer`:
  *   1. `side` waits for all work already enqueued on `compute` (so a victim

@@ -68,6 +68,7 @@ _SIGS = {
     "moe_cache_create": (ctypes.c_int, [ctypes.POINTER(_p), _i32, _i32, _i32, _i64, _p, _p, _p]),
     "moe_cache_destroy": (None, [_p]),
     "expert_cache_lookup": (ctypes.c_int, [_p, _i32, _p, _p, _p, _p, _p, _p]),
+    "expert_cache_row": (ctypes.c_int, [_p, _i32, _p]),
     "expert_cache_fill": (ctypes.c_int, [_p, _i32, _p, _p, _i32, _p, _p]),
     "expert_cache_fill_groups": (ctypes.c_int, [_p, _i32, _p, _p, _i32, _i32, _p, _p]),
     "expert_cache_wait_group": (ctypes.c_int, [_p, _i32, _p]),
@@ -245,6 +246,11 @@ class ExpertCache:
                                         _ptr(self.row)), "expert_cache_lookup")
         n = nm.value
         return (self.miss_e[:n].clone(), self.miss_s[:n].clone(), n, nh.value, self.row.clone())
+
+    def expert_cache_row(self, layer: int) -> torch.Tensor:
+        row = torch.zeros(self.E, dtype=torch.int32)
+        _check(_lib.expert_cache_row(self._h, layer, _ptr(row)), "expert_cache_row")
+        return row
 
     def expert_cache_fill(self, layer: int, miss_expert, miss_slot, side=None, compute=None):
         me = miss_expert.to(torch.int32).contiguous()

@@ -162,6 +162,15 @@ extern "C" int expert_cache_lookup(moe_cache_t c, int32_t layer, const int32_t* 
   return MOE_OK;
 }
 
+extern "C" int expert_cache_row(moe_cache_t c, int32_t layer, int32_t* slot_row_host) {
+  if (!c || !slot_row_host) return set_error(MOE_ERR_INVALID_ARG, "expert_cache_row: null argument");
+  if (layer < 0 || layer >= c->L)
+    return set_error(MOE_ERR_INVALID_ARG, "expert_cache_row: layer %d of %d", layer, c->L);
+  const int64_t key0 = (int64_t)layer * c->E;
+  for (int e = 0; e < c->E; ++e) slot_row_host[e] = c->where[key0 + e];
+  return MOE_OK;
+}
+
 extern "C" int expert_cache_fill(moe_cache_t c, int32_t layer, const int32_t* miss_expert,
                                  const int32_t* miss_slot, int32_t n_miss, moe_stream_t side,
                                  moe_stream_t compute) {

@@ -170,17 +170,14 @@ class MoELayer:
         self.route_permute(logits, cs)
         counts_host = self.counts[:E].to("cpu")          # the one host sync of the step
         ch = counts_host.numpy()
-        if not hasattr(self, "_rows"):
-            self._rows = {}
         row_dev = slot_table[layer * E:(layer + 1) * E]
-        waves = plan_waves(ch, cache.S, self._rows.get(layer))
+        waves = plan_waves(ch, cache.S, cache.expert_cache_row(layer).numpy())
         n_hit_all = n_miss_all = 0
         fills = []
         for wave in waves:
             cw = np.zeros(E, dtype=np.int32)
             cw[wave] = ch[wave]
             me, ms, n_miss, n_hit, row = cache.expert_cache_lookup(layer, torch.from_numpy(cw))
-            self._rows[layer] = row.numpy().copy()
             G = min(groups, n_miss)
             miss = me.tolist()
             masks = np.zeros((1 + G, (E + 3) // 4 * 4), dtype=np.int32)  # rows 16-byte aligned

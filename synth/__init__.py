@@ -310,12 +310,17 @@ def expert_bias(E: int, s: float | None, seed: int, domain: int = 0) -> np.ndarr
     return (-s * np.log(rank.astype(np.float64))).astype(np.float32)
 
 
-def make_logits(wl: Workload, batch: int = 0, T: int | None = None) -> np.ndarray:
+def make_logits(wl: Workload, batch: int = 0, T: int | None = None, layer: int = 0) -> np.ndarray:
+    """Router logits of one batch: N(0,1) noise + the batch's domain bias.  Layers other
+    than 0 (a stack of layers) draw their own noise and their own expert ranking for
+    the same domain."""
     T = wl.T if T is None else T
-    rng = np.random.default_rng(sub_seed(wl.seed, _LOGITS, batch))
+    extra = (layer,) if layer else ()
+    rng = np.random.default_rng(sub_seed(wl.seed, _LOGITS, batch, *extra))
     noise = rng.standard_normal((T, wl.E), dtype=np.float32)
     domain = (batch % wl.domains) if wl.domains else 0
-    return (noise + expert_bias(wl.E, wl.zipf, wl.seed, domain)[None, :]).astype(np.float32)
+    bseed = sub_seed(wl.seed, layer) if layer else wl.seed
+    return (noise + expert_bias(wl.E, wl.zipf, bseed, domain)[None, :]).astype(np.float32)
 
 
 def make_x(wl: Workload, batch: int = 0, T: int | None = None) -> np.ndarray:

@@ -138,6 +138,8 @@ def test_cpp_lru_matches_oracle(seed):
         assert list(zip(me.tolist(), ms.tolist())) == r["fills"]
         assert (nm, nh) == (r["misses"], r["hits"])
         assert np.array_equal(row.numpy(), ora.slot_table(layer, E))
+        other = int(rng.integers(0, L))   # another layer's current row, as it stands now
+        assert np.array_equal(cpp.expert_cache_row(other).numpy(), ora.slot_table(other, E))
     st = cpp.stats()
     assert st["bytes_filled"] == 0 and st["steps"] > 0
 
@@ -156,10 +158,8 @@ def test_cpp_resize_matches_oracle(seed):
             frm, to = cpp.moe_cache_resize(new_S, side=0, compute=0)
             assert list(zip(frm.tolist(), to.tolist())) == ora.resize(new_S)
             for layer in range(L):
-                counts = np.zeros(E, np.int32)
-                _, _, nm, nh, row = cpp.expert_cache_lookup(layer, torch.from_numpy(counts))
-                assert np.array_equal(row.numpy(), ora.slot_table(layer, E))
-                ora.step(layer, counts)
+                assert np.array_equal(cpp.expert_cache_row(layer).numpy(),
+                                      ora.slot_table(layer, E))
             continue
         layer = int(rng.integers(0, L))
         n = int(rng.integers(0, ora.S + 1))

@@ -5,7 +5,8 @@
   every expert resident;
 * the fills made by expert_cache_lookup/fill equal the oracle LRU's;
 * after the fills, each resident slot holds exactly its bank record;
-* outputs match the oracle within tolerance.
+* outputs match the oracle within tolerance;
+* several layers sharing one pool across run-time resizes of the pool.
 """
 from __future__ import annotations
 
@@ -243,6 +244,88 @@ def test_streamed_waves_exceed_pool(fmt):
     for (L, e), s in ora.where.items():
         assert tab[e] == s and torch.equal(pool_h[s], d["bank"][e]), (e, s)
     d["cache"].close()
+
+
+def test_shared_pool_layers_with_resizes():
+    """Three layers share one pool (keys (layer, expert)); the pool shrinks in
+    place, grows in place and moves into a new, larger allocation between
+    steps.  After each resize every kept slot holds its bank record and every
+    layer's slot-table row is the oracle's; the streamed path's fills follow the
+    oracle LRU (waves where a step needs more experts than the pool holds) and
+    y is bit-identical to the all-resident run."""
+    wl = synth.Workload("pool_resize", T=48, H=512, E=32, I=256, k=2, fmt="mxfp4", seed=51,
+                        zipf=1.3, domains=2, batches=12)
+    L, S0, S_cap = 2, 24, 40
+    stride = synth.record_layout(wl.fmt, wl.H, wl.I)["stride"]
+    bank = torch.empty((L * wl.E, stride), dtype=torch.uint8, pin_memory=True)
+    dev_sets = []
+    for li in range(L):
+        recs = synth.make_expert_records(wl.fmt, wl.E, wl.H, wl.I, wl.seed, layer=li)
+        bank[li * wl.E:(li + 1) * wl.E].copy_(recs)
+        dev_sets.append(recs.to(DEV))
+    pool = torch.zeros((S_cap, stride), dtype=torch.uint8, device=DEV)  # room to grow in place
+    table = torch.full((L * wl.E,), -1, dtype=torch.int32, device=DEV)
+    cache = moe.ExpertCache(L, wl.E, S0, stride, pool, bank, table)
+    layer = moe.MoELayer(wl.fmt, wl.E, wl.H, wl.I, wl.k, wl.T, stride)
+    pool_W = moe.experts(wl.fmt, wl.E, wl.H, wl.I, pool, stride)
+    ora = OL.LruSlots(S0)
+    side = torch.cuda.Stream()
+    from moe_expert_ffn_router_amd.layer import plan_waves
+    plan = {4: ("shrink", 9), 8: ("grow", 30), 12: ("move", 48), 16: ("shrink", 16)}
+    flush(f"[pool-resize] L={L} S0={S0}")
+    hits_after_resize = 0
+
+    def check_pool(tag, whole_table):
+        tab = table.cpu().numpy()
+        pool_h = pool.cpu()
+        if whole_table:  # a resize rewrites every row; fills publish only their own layer's
+            for li in range(L):
+                assert np.array_equal(tab[li * wl.E:(li + 1) * wl.E],
+                                      ora.slot_table(li, wl.E)), tag
+        for (li, e), s in ora.where.items():
+            assert tab[li * wl.E + e] == s, (tag, li, e)
+            assert torch.equal(pool_h[s], bank[li * wl.E + e]), (tag, li, e, s)
+
+    for step in range(20):
+        if step in plan:
+            kind, new_S = plan[step]
+            if kind == "move":
+                pool = torch.zeros((new_S, stride), dtype=torch.uint8, device=DEV)
+                moves = cache.moe_cache_resize(new_S, pool, side=side)
+                pool_W = moe.experts(wl.fmt, wl.E, wl.H, wl.I, pool, stride)
+            else:
+                moves = cache.moe_cache_resize(new_S, side=side)
+            exp = ora.resize(new_S)
+            assert list(zip(*(t.tolist() for t in moves))) == exp, step
+            check_pool(f"after {kind} to {new_S}", True)
+            flush(f"   step {step}: {kind} to {new_S}, kept {len(exp)}")
+        li = step % L
+        b = step % wl.batches
+        lg, x = _batch(wl, b)
+        ids, _ = OR.route(synth.make_logits(wl, b), wl.k)
+        counts, *_ = OP.permute(ids, wl.E)
+        fills = []
+        for wave in plan_waves(counts, ora.S, ora.slot_table(li, wl.E)):
+            cw = np.zeros(wl.E, dtype=np.int64)
+            cw[wave] = counts[wave]
+            fills += ora.step(li, cw)["fills"]
+        y_s, info = layer.forward_streamed(lg, x, li, cache, pool_W, table, side=side, groups=2)
+        y_s = y_s.clone()
+        torch.cuda.synchronize()
+        assert info["fills"] == fills, step
+        if step >= min(plan):
+            hits_after_resize += info["hits"]
+        layer.route_permute(lg)
+        layer.expert_ffn(layer.weights(dev_sets[li]), x, wl.T)
+        layer.combine(wl.T, False)
+        y_r = layer.y[:wl.T].clone()
+        torch.cuda.synchronize()
+        assert torch.equal(y_s.view(torch.int16), y_r.view(torch.int16)), step
+        flush(f"   step {step} layer {li}: waves {info['waves']} hits {info['hits']} "
+              f"misses {info['misses']}")
+    check_pool("end", False)
+    assert hits_after_resize > 0
+    cache.close()
 
 
 def test_fill_groups_argument_checks():
