@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of graph replay")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 64 MiB device copy (for HBM counter calibration)")
+    ap.add_argument("--calibrate-read", action="store_true",
+                    help="only time plain streaming reads of several sizes (the practical HBM "
+                         "read ceiling next to the published peak)")
     ap.add_argument("--resident", action="store_true",
                     help="cache workloads: keep every expert in HBM instead of the slot pool")
     ap.add_argument("--layers", type=int, default=1,
@@ -111,6 +114,45 @@ def calibrate_copy():
     print(json.dumps({"calibration_copy_bytes": n, "launches": 5}), flush=True)
 
 
+def calibrate_read():
+    """moe_hbm_read_probe over sizes from a decode launch's bytes to 1 GiB, 24 launches
+    in one graph replay; each launch reads a region the previous launches did not (the
+    buffer spans 8x the largest size, well past the memory-side cache)."""
+    import torch
+    import moe_expert_ffn_router_amd as moe
+    big = 1 << 30
+    buf = torch.ones(8 * big, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(8192 * 256, dtype=torch.int32, device="cuda")
+    rows = []
+    for nbytes in (16 << 20, 34_000_000, 68_000_000, 96_404_480, 256 << 20, big):
+        n = nbytes // 16 * 16
+        regions = buf.numel() // n
+        for grid in (512, 1024, 2048, 4096):
+            for r in range(3):
+                moe.moe_hbm_read_probe(buf[(r % regions) * n:], n, grid, sink)
+            reps = 24
+            g = torch.cuda.CUDAGraph()  # launches back to back, no host gaps
+            with torch.cuda.graph(g):
+                for r in range(reps):
+                    moe.moe_hbm_read_probe(buf[((3 + r) % regions) * n:], n, grid, sink)
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            rows.append({"bytes": n, "grid": grid, "us": round(us, 2),
+                         "tb_s": round(n / (us * 1e-6) / 1e12, 3)})
+    best = {}
+    for r in rows:
+        if r["bytes"] not in best or r["us"] < best[r["bytes"]]["us"]:
+            best[r["bytes"]] = r
+    print(json.dumps({"calibration_read": rows, "best_per_size": list(best.values())}),
+          flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -119,6 +161,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.calibrate_read:
+        calibrate_read()
         return
     import torch
 

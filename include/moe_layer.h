@@ -333,6 +333,17 @@ int moe_cache_stats(moe_cache_t cache, int64_t* steps, int64_t* hits, int64_t* m
 
 /* ---------------------------------------------------------------------------
  * Diagnostics. */
+/* ---------------------------------------------------------------------------
+ * Measurement helper (not a step of the layer).  moe_hbm_read_probe enqueues
+ * one plain streaming read of `bytes` bytes at `src` (device, 16-byte
+ * aligned, bytes a multiple of 16) by `grid` workgroups of 256 threads; each
+ * thread writes one fold of what it read to sink[block*256 + thread] (device,
+ * grid*256 uint32, caller-owned).  Its time is the cost of a pure read of that
+ * many bytes on this chip: the practical ceiling for a bandwidth-bound kernel
+ * of the same size, next to the 8 TB/s published peak. */
+int moe_hbm_read_probe(const void* src, int64_t bytes, int32_t grid, uint32_t* sink,
+                       moe_stream_t stream);
+
 const char* moe_status_str(int status);
 const char* moe_last_error(void); /* thread-local; "" when none */
 int moe_version(void);            /* ABI version, currently 1 */

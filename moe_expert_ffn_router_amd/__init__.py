@@ -74,6 +74,7 @@ _SIGS = {
     "expert_cache_wait_group": (ctypes.c_int, [_p, _i32, _p]),
     "moe_cache_resize": (ctypes.c_int, [_p, _i32, _p, _p, _p, _p, _p, _p]),
     "moe_cache_stats": (ctypes.c_int, [_p, _p, _p, _p, _p]),
+    "moe_hbm_read_probe": (ctypes.c_int, [_p, _i64, _i32, _p, _p]),
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_version": (ctypes.c_int, []),
@@ -289,6 +290,13 @@ class ExpertCache:
         v = [ctypes.c_int64() for _ in range(4)]
         _check(_lib.moe_cache_stats(self._h, *[ctypes.byref(x) for x in v]), "moe_cache_stats")
         return dict(zip(("steps", "hits", "misses", "bytes_filled"), (x.value for x in v)))
+
+
+def moe_hbm_read_probe(src: torch.Tensor, nbytes: int, grid: int, sink: torch.Tensor,
+                       stream=None) -> None:
+    assert nbytes <= src.numel() * src.element_size() and sink.numel() >= grid * 256
+    _check(_lib.moe_hbm_read_probe(_ptr(src), nbytes, grid, _ptr(sink), _stream(stream)),
+           "moe_hbm_read_probe")
 
 
 def moe_version() -> int:

@@ -19,7 +19,7 @@ OBJ = os.path.join(ROOT, "_build", "obj")
 ARCH = "gfx950"
 
 SOURCES = ["status.cpp", "cache.cpp", "route.hip", "permute.hip", "ffn.hip", "combine.hip",
-           "decode.hip"]
+           "decode.hip", "probe.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -1,0 +1,37 @@
+// HBM read calibration: a plain streaming read of `bytes` bytes (grid-strided
+// 16-byte loads, 256-thread workgroups), each thread folding what it read into
+// one word written to `sink`.  It does none of the layer's arithmetic; its
+// time for a given byte count is what a pure read of those bytes costs on
+// this chip, the practical ceiling the bandwidth-bound kernels are held to.
+#include "moe_internal.h"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void hbm_read_kernel(const uint4* __restrict__ src, size_t n16,
+                                                       uint32_t* __restrict__ sink) {
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t step = (size_t)gridDim.x * 256;
+  uint32_t a = 0;
+#pragma unroll 8
+  for (; i < n16; i += step) {
+    const uint4 v = src[i];
+    a ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  sink[(size_t)blockIdx.x * 256 + threadIdx.x] = a;
+}
+
+}  // namespace moe
+
+extern "C" int moe_hbm_read_probe(const void* src, int64_t bytes, int32_t grid, uint32_t* sink,
+                                  moe_stream_t stream) {
+  using namespace moe;
+  if (!src || !sink || bytes <= 0 || bytes % 16 || grid < 1 || grid > 65536)
+    return set_error(MOE_ERR_INVALID_ARG,
+                     "moe_hbm_read_probe: need src, sink, bytes > 0 and a multiple of 16, "
+                     "1 <= grid <= 65536");
+  if (!aligned16(src))
+    return set_error(MOE_ERR_INVALID_ARG, "moe_hbm_read_probe: src must be 16-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hbm_read_kernel<<<grid, 256, 0, s>>>(static_cast<const uint4*>(src), (size_t)bytes / 16, sink);
+  return check_launch("moe_hbm_read_probe");
+}

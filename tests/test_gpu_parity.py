@@ -340,3 +340,18 @@ def test_layer_empty_batch():
     y = layer.forward(case.logits[:0], case.x[:0], W)
     torch.cuda.synchronize()
     assert y.shape == (0, wl.H)
+
+
+def test_hbm_read_probe_reads_every_word():
+    """The read calibration reads each 16-byte piece exactly once: the XOR of all
+    threads' folds is the XOR of every 32-bit word of the region."""
+    rng = np.random.default_rng(7)
+    n = (3 << 20) + 16 * 37  # not a multiple of the grid's stride
+    host = rng.integers(0, 2**32, size=n // 4, dtype=np.uint32)
+    src = torch.from_numpy(host.view(np.int32)).to("cuda")
+    for grid in (1, 300, 2048):
+        sink = torch.zeros(grid * 256, dtype=torch.int32, device="cuda")
+        moe.moe_hbm_read_probe(src, n, grid, sink)
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        assert got == np.bitwise_xor.reduce(host), grid
