@@ -180,7 +180,11 @@ int moe_combine(const uint16_t* y_perm, const int32_t* inv_idx, const float* top
  * T <= 16 (H <= 2048): two launches, token-major — gate/up workgroups route
  * their own token (one wave, from the logits) and store h by assignment; the
  * down workgroups fold in the combine, and one extra workgroup writes the
- * permutation outputs.  16 < T <= 64: four launches — route + permute in one
+ * permutation outputs.  With MXFP4 weights and T*k*(I/128) >= 256 the first
+ * launch does the whole expert FFN instead: a workgroup per (token, expert
+ * slot, 128 h-columns) computes those h-columns and their share of the down
+ * projection for every output column (fp32 partials in the workspace); the
+ * second sums the partials and combines.  16 < T <= 64: four launches — route + permute in one
  * workgroup, gate/up and down as persistent grids over 16-row expert tiles,
  * combine.  Writes every output
  * of moe_route_permute + moe_expert_ffn + moe_combine: topk_ids / topk_w
@@ -194,8 +198,9 @@ int moe_combine(const uint16_t* y_perm, const int32_t* inv_idx, const float* top
  * moe_forward_decode_supported(H, I, T, k) return MOE_ERR_UNSUPPORTED (use
  * the separate calls): T <= 64, T*k <= 256, H and I in {512, 1024, 1536,
  * 2048}, T*(H+8)*2 bytes of x fitting in LDS beside the tile table.
- *   ws: device, >= moe_forward_decode_workspace(W, T, k) bytes (holds h and
- *   y_perm; contents on entry are ignored).                                 */
+ *   ws: device, >= moe_forward_decode_workspace(W, T, k) bytes (holds h,
+ *   y_perm and the partials; contents on entry are ignored; the size for T
+ *   also serves every smaller batch).                                       */
 int moe_forward_decode_supported(int32_t H, int32_t I, int32_t T, int32_t k);
 size_t moe_forward_decode_workspace(const moe_experts* W, int32_t T, int32_t k);
 int moe_forward_decode(const moe_experts* W, const int32_t* slot_of_expert, const float* logits,

@@ -36,6 +36,7 @@ struct DecArgs {
   int* inv;
   const uint16_t* y_shared;
   uint16_t* y;
+  float* part;  // fused path: per-(token, slot, h-slice) down partials [T*k][I/128][H]
 };
 
 // ----------------------------------------------------------------------------
@@ -835,6 +836,213 @@ __global__ __launch_bounds__(256) void dec_down_tok_kernel(DecArgs p) {
   }
 }
 
+// ----------------------------------------------------------------------------
+// fused token-major layer (MXFP4 weights, small T).  Workgroup u (16 waves)
+// serves unit (t, j, q), u = t + T*(j + k*q): token t, its expert slot j and
+// the 128 h-columns [128q, 128q + 128).  It routes token t itself (wave 0,
+// rounds 0..j), computes those h-columns in full and then their share of the
+// down projection for every output column:
+//   gate/up: wave w owns h-columns 128q + 8w .. + 8; the MFMA's 16 B columns
+//            are their 8 gate rows (lanes 0..7) and 8 up rows (lanes 8..15),
+//            all of K (H/128 chunks); the token's x row is A row 0;
+//   h:       SiLU(gate)*up, rounded to bf16, split into E4M3 hi + lo with an
+//            E8M0 scale per 32 (one K chunk of the down projection);
+//   down:    wave w owns output rows [w*H/16, (w+1)*H/16), K = the slice;
+//            fp32 partial outputs go to part[(t*k + j)*(I/128) + q][H].
+// The slice's down weights are loaded while the second half of the gate/up
+// chunks is computed, so the workgroup's loads form one stream; the layer
+// is one weight stream over the whole chip instead of two launches' worth.
+// Workgroup 0 also routes all T tokens (one wave each) and writes ids,
+// weights, counts, offsets, sorted_idx and inv_idx while its loads fly.
+// dec_fused_combine_kernel then sums each expert's partials (q ascending),
+// rounds to bf16 (the y_perm value) and combines in top-k order.
+// ----------------------------------------------------------------------------
+constexpr int kFuWaves = 16, kFuSlice = 128, kFuMinUnits = 256;
+
+// NC = H/128 gate/up chunks per wave, NS = H/256 down subtiles per wave.
+template <int NC, int VPL>
+__global__ __launch_bounds__(1024) void dec_fused_tok_kernel(DecArgs p) {
+  static_assert(NC % 4 == 0, "H is a multiple of 512");
+  constexpr int NS = NC / 2, NSV = NC / 4;
+  const FfnArgs& a = p.f;
+  __shared__ __attribute__((aligned(32))) uint8_t mx[2 * kTokMaxH + kTokMaxH / 32 + 32];
+  __shared__ __attribute__((aligned(32))) uint8_t hx[2 * kFuSlice + 32];
+  __shared__ __attribute__((aligned(16))) uint16_t hb[kFuSlice];
+  __shared__ float gu[kFuWaves][16];
+  __shared__ int eslot[kMaxK];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int T = p.T, k = a.k, E = a.E, H = a.H, I = a.I, Q = I / kFuSlice;
+  const int u = (int)blockIdx.x, t = u % T, r_ = u / T, j = r_ % k, q = r_ / k;
+  uint8_t *mh = mx, *ml = mx + kTokMaxH, *ms = mx + 2 * kTokMaxH;
+  uint8_t* mz = ms + kTokMaxH / 32;  // 32 zero bytes: A rows 1..15
+  uint8_t *hh = hx, *hl = hx + kFuSlice, *hs = hx + 2 * kFuSlice;  // h slice: hi, lo, 4 scales
+  if (tid < 8) reinterpret_cast<uint32_t*>(mz)[tid] = 0u;
+  // one round trip: (wave 0) the token's logits row; waves 1..15 split its x row
+  // Workgroup 0 also routes every token (wave w: token w) and writes the
+  // routing and permutation outputs while its weight loads are in flight; its
+  // waves < T load their logits rows now, with the rest of the prologue.
+  const bool writer = u == 0;
+  float lv[VPL];
+  if (wave == 0 || (writer && wave < T))
+    route_load<VPL>(p.logits + (size_t)(wave == 0 ? t : wave) * E, E, lane, lv);
+  if (wave > 0)
+    prep_a_mx<(kFuWaves - 1) * 64>(a.x + (size_t)t * H, 1, H, H, mh, ml, ms, tid - 64);
+  TopK<VPL> st;
+  if (wave == 0) {
+    topk_begin<VPL>(lv, E, lane, st);
+    for (int r = 0; r <= j; ++r) topk_round<VPL>(st, r, lane);
+    if (lane == j) eslot[0] = a.slot_of ? a.slot_of[st.id_r] : st.id_r;
+  }
+  __syncthreads();
+  const uint8_t* rec = a.base + (size_t)eslot[0] * a.stride;
+  // gate/up loads: chunk c of B column l16, and the row's H/32 scale bytes
+  const int hcol = q * kFuSlice + wave * 8 + (l16 & 7);
+  const int wrow = (l16 < 8 ? 0 : I) + hcol;
+  const uint8_t* wp = rec + a.off_w13 + (size_t)wrow * (H / 2) + g * 16;
+  const uint8_t* sp = rec + a.off_w13s + (size_t)wrow * (H / 32);
+  // scales first: loads complete in issue order, and chunk 0 needs its scale
+  uint4 w[NC];
+  uint4 sv[NSV];
+#pragma unroll
+  for (int i = 0; i < NSV; ++i) sv[i] = *reinterpret_cast<const uint4*>(sp + 16 * i);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) w[c] = *reinterpret_cast<const uint4*>(wp + c * (KC / 2));
+  if (writer) {
+    __shared__ int pid[kDA];
+    if (wave < T) {  // wave 0 has token 0's rounds 0..j (j = 0) done
+      if (wave > 0) {
+        topk_begin<VPL>(lv, E, lane, st);
+        topk_round<VPL>(st, 0, lane);
+      }
+      for (int r = 1; r < k; ++r) topk_round<VPL>(st, r, lane);
+      const float wv = topk_weight<VPL>(st, lv, E, k, p.renorm, lane);
+      if (lane < k) {
+        p.ids[wave * k + lane] = st.id_r;
+        p.wts[wave * k + lane] = wv;
+        pid[wave * k + lane] = st.id_r;
+      }
+    }
+    __syncthreads();
+    // stable counting sort by expert, brute force over the A <= 256 ids
+    const int A = T * k;
+    for (int e = tid; e < E; e += 1024) {
+      int cnt = 0, below = 0;
+      for (int i = 0; i < A; ++i) {
+        const int v = pid[i];
+        cnt += v == e;
+        below += v < e;
+      }
+      p.counts[e] = cnt;
+      p.offsets[e] = below;
+    }
+    if (tid == 0) p.offsets[E] = A;
+    if (tid < A) {
+      const int e = pid[tid];
+      int pos = 0;
+      for (int i = 0; i < A; ++i) {
+        const int v = pid[i];
+        pos += v < e || (v == e && i < tid);
+      }
+      p.sorted[pos] = tid;
+      p.inv[tid] = pos;
+    }
+  }
+  uint4 w2[NS];
+  uint32_t s2[NS];
+  const int drow0 = wave * (H / kFuWaves) + l16;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (c == NC / 2) {  // the slice's down weights, behind the first half of the chunks
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int row = drow0 + s * 16;
+        w2[s] = *reinterpret_cast<const uint4*>(rec + a.off_w2 + (size_t)row * (I / 2) +
+                                                q * (kFuSlice / 2) + g * 16);
+        s2[s] = *reinterpret_cast<const uint32_t*>(rec + a.off_w2s + (size_t)row * (I / 32) +
+                                                   q * 4);
+      }
+    }
+    // A row 0 is the token; lanes of rows 1..15 read a zero block (scale 1)
+    const int off = l16 == 0 ? c * KC + g * 32 : -1;
+    const i32x8 ah = *reinterpret_cast<const i32x8*>(off < 0 ? mz : mh + off);
+    const i32x8 al = *reinterpret_cast<const i32x8*>(off < 0 ? mz : ml + off);
+    const int sa = off < 0 ? 127 : ms[c * 4 + g];
+    const uint4 sq = sv[c / 4];
+    const uint32_t d = (c & 3) == 0 ? sq.x : (c & 3) == 1 ? sq.y : (c & 3) == 2 ? sq.z : sq.w;
+    const int sb = (int)((d >> (8 * g)) & 0xffu);
+    const i32x4 bq = {(int)w[c].x, (int)w[c].y, (int)w[c].z, (int)w[c].w};
+    acc = mfma_mx(ah, bq, sa, sb, acc);
+    acc = mfma_mx(al, bq, sa, sb, acc);
+    pin(acc);
+  }
+  // row 0 of the 16x16 result: lanes 0..15, element 0 (gate in 0..7, up in 8..15)
+  if (g == 0) gu[wave][l16] = acc[0];
+  __syncthreads();
+  if (tid < kFuSlice) {
+    const float gv = gu[tid >> 3][tid & 7], uv = gu[tid >> 3][8 + (tid & 7)];
+    hb[tid] = f32_to_bf16_rne(gv / (1.0f + expf(-gv)) * uv);
+  }
+  __syncthreads();
+  if (wave == 0) {  // the h slice as one A row of the down MFMA (16 pieces of 8)
+    uint4 v[4] = {};
+    if (lane < kFuSlice / 8) v[0] = reinterpret_cast<const uint4*>(hb)[lane];
+    prep_a_mx_store<64>(v, 1, kFuSlice, 0, lane, hh, hl, hs);
+  }
+  __syncthreads();
+  const int offh = l16 == 0 ? g * 32 : -1;
+  const i32x8 dh = *reinterpret_cast<const i32x8*>(offh < 0 ? mz : hh + offh);
+  const i32x8 dl = *reinterpret_cast<const i32x8*>(offh < 0 ? mz : hl + offh);
+  const int sd = offh < 0 ? 127 : hs[g];
+  float* out = p.part + ((size_t)(t * k + j) * Q + q) * H;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const i32x4 bq = {(int)w2[s].x, (int)w2[s].y, (int)w2[s].z, (int)w2[s].w};
+    const int sb = (int)((s2[s] >> (8 * g)) & 0xffu);
+    f32x4 y4 = f32x4{0.f, 0.f, 0.f, 0.f};
+    y4 = mfma_mx(dh, bq, sd, sb, y4);
+    y4 = mfma_mx(dl, bq, sd, sb, y4);
+    pin(y4);  // keeps the MFMAs (and their operands) out of the g == 0 branch: every lane feeds them
+    if (g == 0) out[drow0 + s * 16] = y4[0];
+  }
+}
+
+// y[t] = bf16( sum_j w_tj * bf16( sum_q part[t, j, q] ) (+ y_shared[t]) ), sums
+// in q then j order.  Workgroup (t, 64 columns): thread (j, column pair) sums
+// one expert's partials for two columns (all its loads in one round trip),
+// then 64 threads combine the experts in top-k order.
+constexpr int kFuCols = 64;
+
+__global__ __launch_bounds__(256) void dec_fused_combine_kernel(DecArgs p) {
+  const int k = p.f.k, H = p.f.H, Q = p.f.I / kFuSlice, n_cb = H / kFuCols;
+  __shared__ float ew[kMaxK];
+  __shared__ float yp[kMaxK][kFuCols];
+  const int tid = threadIdx.x, t = blockIdx.x / n_cb;
+  const int c0 = (blockIdx.x - t * n_cb) * kFuCols, pr = tid & 31;
+  if (tid < k) ew[tid] = p.wts[t * k + tid];
+  for (int jj = tid >> 5; jj < k; jj += 8) {
+    const float* src = p.part + (size_t)(t * k + jj) * Q * H + c0 + 2 * pr;
+    float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll 4
+    for (int qq = 0; qq < Q; ++qq) {
+      const float2 v = *reinterpret_cast<const float2*>(src + (size_t)qq * H);
+      s0 += v.x;
+      s1 += v.y;
+    }
+    yp[jj][2 * pr] = bf16_to_f32(f32_to_bf16_rne(s0));
+    yp[jj][2 * pr + 1] = bf16_to_f32(f32_to_bf16_rne(s1));
+  }
+  __syncthreads();
+  if (tid < kFuCols) {
+    const int c = c0 + tid;
+    float y = 0.0f;
+    for (int jj = 0; jj < k; ++jj) y = fmaf(ew[jj], yp[jj][tid], y);
+    if (p.y_shared) y += bf16_to_f32(p.y_shared[(size_t)t * H + c]);
+    p.y[(size_t)t * H + c] = f32_to_bf16_rne(y);
+  }
+}
+
 static int g_cus = 0;
 
 // Raise a kernel's dynamic-LDS limit once (the largest request so far is kept).
@@ -914,10 +1122,39 @@ static int launch_gateup_tok_vpl(const DecArgs& p, hipStream_t s) {
   return p.f.E <= 256 ? launch_gateup_tok<FMT, CPW, 4>(p, s) : launch_gateup_tok<FMT, CPW, 16>(p, s);
 }
 
+// The fused path: MXFP4 weights, E <= 256 (routing state in few registers),
+// token-major shapes with at least one unit per compute unit of the chip
+// (256 on MI355X).
+static bool fused_path(int fmt, int E, int T, int k, int H, int I) {
+  return fmt == MOE_W_MXFP4 && E <= 256 && token_major(T, H) && I % kFuSlice == 0 &&
+         H % 512 == 0 && T * k * (I / kFuSlice) >= kFuMinUnits;
+}
+
+template <int NC>
+static int launch_fused_nc(const DecArgs& p, hipStream_t s) {
+  const int U = p.T * p.f.k * (p.f.I / kFuSlice);
+  dec_fused_tok_kernel<NC, 4><<<U, 1024, 0, s>>>(p);  // E <= 256: 4 logits per lane
+  return MOE_OK;
+}
+
+static int launch_fused(const DecArgs& p, hipStream_t s) {
+  int st;
+  switch (p.f.H / 128) {
+    case 4: st = launch_fused_nc<4>(p, s); break;
+    case 8: st = launch_fused_nc<8>(p, s); break;
+    case 12: st = launch_fused_nc<12>(p, s); break;
+    default: st = launch_fused_nc<16>(p, s); break;
+  }
+  if (st) return st;
+  dec_fused_combine_kernel<<<p.T * (p.f.H / kFuCols), 256, 0, s>>>(p);
+  return check_launch("moe_forward_decode");
+}
+
 // K chunks per wave: H / 512 for gate/up, I / 512 for the tile-major down
 template <int FMT>
 static int launch_decode(DecArgs& p, hipStream_t s) {
   int st;
+  if (fused_path(FMT, p.f.E, p.T, p.f.k, p.f.H, p.f.I)) return launch_fused(p, s);
   if (token_major(p.T, p.f.H)) {
     switch (p.f.H / 512) {
       case 1: st = launch_gateup_tok_vpl<FMT, 1>(p, s); break;
@@ -964,11 +1201,21 @@ using namespace moe;
 
 static size_t dec_align(size_t v) { return (v + 255) / 256 * 256; }
 
-// Workspace: h [A][I] bf16 | y_perm [A][H] bf16.
+// Workspace: h [A][I] bf16 | y_perm [A][H] bf16 (| fused path: down partials
+// [A][I/128][H] fp32).
+static size_t dec_ws_bytes(int fmt, int E, int H, int I, int T, int k) {
+  const size_t A = (size_t)T * k;
+  size_t n = dec_align(A * I * 2) + dec_align(A * H * 2);
+  if (fused_path(fmt, E, T, k, H, I)) n += dec_align(A * (I / kFuSlice) * H * 4);
+  return n;
+}
+
+// Enough for every batch of at most T tokens (the partials exist for T <= 16 only).
 extern "C" size_t moe_forward_decode_workspace(const moe_experts* W, int32_t T, int32_t k) {
   if (!W || T < 0 || k < 1) return 0;
-  const size_t A = (size_t)T * k;
-  return dec_align(A * W->I * 2) + dec_align(A * W->H * 2);
+  const size_t a = dec_ws_bytes(W->fmt, W->E, W->H, W->I, T, k);
+  const size_t b = dec_ws_bytes(W->fmt, W->E, W->H, W->I, T < kTokMaxT ? T : kTokMaxT, k);
+  return a > b ? a : b;
 }
 
 extern "C" int moe_forward_decode(const moe_experts* W, const int32_t* slot_of_expert,
@@ -1021,6 +1268,9 @@ extern "C" int moe_forward_decode(const moe_experts* W, const int32_t* slot_of_e
   uint8_t* wsb = static_cast<uint8_t*>(ws);
   f.hbuf = reinterpret_cast<uint16_t*>(wsb);
   f.y_perm = reinterpret_cast<uint16_t*>(wsb + dec_align(A * W->I * 2));
+  p.part = fused_path(W->fmt, W->E, T, k, W->H, W->I)
+               ? reinterpret_cast<float*>(wsb + dec_align(A * W->I * 2) + dec_align(A * W->H * 2))
+               : nullptr;
   p.logits = logits;
   p.T = T;
   p.renorm = renorm;
