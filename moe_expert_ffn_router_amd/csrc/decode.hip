@@ -1020,7 +1020,8 @@ __global__ __launch_bounds__(256) void dec_fused_combine_kernel(DecArgs p) {
   __shared__ float yp[kMaxK][kFuCols];
   const int tid = threadIdx.x, t = blockIdx.x / n_cb;
   const int c0 = (blockIdx.x - t * n_cb) * kFuCols, pr = tid & 31;
-  if (tid < k) ew[tid] = p.wts[t * k + tid];
+  // the routing weight is loaded with the partials (one round trip), stored after
+  const float wv = tid < k ? p.wts[t * k + tid] : 0.0f;
   for (int jj = tid >> 5; jj < k; jj += 8) {
     const float* src = p.part + (size_t)(t * k + jj) * Q * H + c0 + 2 * pr;
     float s0 = 0.0f, s1 = 0.0f;
@@ -1033,6 +1034,7 @@ __global__ __launch_bounds__(256) void dec_fused_combine_kernel(DecArgs p) {
     yp[jj][2 * pr] = bf16_to_f32(f32_to_bf16_rne(s0));
     yp[jj][2 * pr + 1] = bf16_to_f32(f32_to_bf16_rne(s1));
   }
+  if (tid < k) ew[tid] = wv;
   __syncthreads();
   if (tid < kFuCols) {
     const int c = c0 + tid;
