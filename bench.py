@@ -71,15 +71,21 @@ def parse():
     return ap.parse_args()
 
 
-KERNEL_SOURCES = ("decode.hip", "ffn.hip", "ffn_common.h", "moe_internal.h", "route.hip",
-                  "route_common.h", "permute.hip", "combine.hip")
+# kernel sources the timed launches of each workload are compiled from
+KERNEL_SOURCES = {
+    "decode": ("decode.hip", "ffn_common.h", "moe_internal.h", "route_common.h"),
+    "layer": ("ffn.hip", "ffn_common.h", "moe_internal.h", "route.hip", "route_common.h",
+              "permute.hip", "combine.hip"),
+}
 
 
-def source_hash() -> str:
-    """sha256 over the kernel sources: counter readings are valid only for these bytes."""
+def source_hash(workload: str) -> str:
+    """sha256 over the workload's kernel sources: counter readings are valid only for these
+    bytes (decode_mxfp4 runs the decode-layer kernels, the other workloads the separate
+    route / permute / expert FFN / combine kernels)."""
     import hashlib
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in KERNEL_SOURCES["decode" if workload == "decode_mxfp4" else "layer"]:
         with open(os.path.join(ROOT, "moe_expert_ffn_router_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -94,7 +100,7 @@ def measured_traffic(workload: str):
     for line in open(path):
         if line.startswith("TRAFFIC "):
             rec = json.loads(line[len("TRAFFIC "):])
-            if rec.get("source_hash") != source_hash():
+            if rec.get("source_hash") != source_hash(workload):
                 return None
             return int(sum(k["fetch_kib"] * 1024 * rec["fetch_scale"] +
                            k["write_kib"] * 1024 * rec["write_scale"]
