@@ -180,7 +180,8 @@ int moe_combine(const uint16_t* y_perm, const int32_t* inv_idx, const float* top
  * T <= 16 (H <= 2048): two launches, token-major — gate/up workgroups route
  * their own token (one wave, from the logits) and store h by assignment; the
  * down workgroups fold in the combine, and one extra workgroup writes the
- * permutation outputs.  With MXFP4 weights and T*k*(I/128) >= 256 the first
+ * permutation outputs.  With MXFP4 weights, E <= 256 and T*k*(I/128) a
+ * multiple of 256 (whole rounds of one workgroup per compute unit) the first
  * launch does the whole expert FFN instead: a workgroup per (token, expert
  * slot, 128 h-columns) computes those h-columns and their share of the down
  * projection for every output column (fp32 partials in the workspace); the

@@ -1125,11 +1125,13 @@ static int launch_gateup_tok_vpl(const DecArgs& p, hipStream_t s) {
 }
 
 // The fused path: MXFP4 weights, E <= 256 (routing state in few registers),
-// token-major shapes with at least one unit per compute unit of the chip
-// (256 on MI355X).
+// token-major shapes whose units fill the chip's compute units (256 on
+// MI355X, one unit each) in whole rounds: a partial last round would cost a
+// whole round.
 static bool fused_path(int fmt, int E, int T, int k, int H, int I) {
+  const int U = T * k * (I / kFuSlice);
   return fmt == MOE_W_MXFP4 && E <= 256 && token_major(T, H) && I % kFuSlice == 0 &&
-         H % 512 == 0 && T * k * (I / kFuSlice) >= kFuMinUnits;
+         H % 512 == 0 && U >= kFuMinUnits && U % kFuMinUnits == 0;
 }
 
 template <int NC>
