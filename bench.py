@@ -319,8 +319,8 @@ def main():
         # HBM bytes per step of the timed kernels, from the committed counter
         # readings of this workload's configuration (None without them)
         roof["traffic"] = measured_traffic(wl.name)
-    roof.update({"kernel": ("moe_forward_decode: token-major gate/up with routing + token-major "
-                            "down with combine (2 launches)" if whole and wl.T <= 16 else
+    roof.update({"kernel": ("moe_forward_decode, token-major (2 launches: the expert FFN with "
+                            "routing, then the combine)" if whole and wl.T <= 16 else
                             "moe_forward_decode (4 launches)" if whole
                             else "moe_expert_ffn (gate/up + down launches)"),
                  "ffn_ms": round(ffn_ms, 5),
