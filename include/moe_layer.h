@@ -219,6 +219,23 @@ int moe_dequant_expert(const moe_experts* W, int32_t expert, float* w13, float* 
                        moe_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_shared_ffn — the always-on shared expert (the large-prefill workload's
+ * "plus 1 always-on shared expert", added to every token's output with
+ * weight 1 by moe_combine / moe_forward_decode through y_shared): the dense
+ * SwiGLU FFN of every token row with one BF16 expert record (W->base points
+ * at it; W->fmt BF16, W->H, W->I its sizes), no routing or permutation.
+ *   x:  device bf16 [T][H];  y: device bf16 [T][H] (out)
+ *   gate/up and down are bf16 GEMMs with fp32 accumulation (hipBLASLt);
+ *   h = bf16(SiLU(gate) * up) between them, from the fp32 gate/up values.
+ *   ws: device, >= moe_shared_ffn_workspace(W, T) bytes (fp32 gate/up
+ *   values, h, and the GEMM library's scratch); enqueued on `stream`.
+ * Other formats return MOE_ERR_UNSUPPORTED (moe_expert_ffn with E = 1, k = 1
+ * computes the same for any format). */
+size_t moe_shared_ffn_workspace(const moe_experts* W, int32_t T);
+int moe_shared_ffn(const moe_experts* W, const uint16_t* x, int32_t T, uint16_t* y, void* ws,
+                   size_t ws_bytes, moe_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Expert-slot cache (guide, "expert bank & LRU slot cache", "MoE strategies"
  * offload, "minimum cache constraint").  A fixed pool of S slots in HBM,
  * shared by all layers, holds expert records; the slot table maps

@@ -75,6 +75,8 @@ _SIGS = {
     "moe_cache_resize": (ctypes.c_int, [_p, _i32, _p, _p, _p, _p, _p, _p]),
     "moe_cache_stats": (ctypes.c_int, [_p, _p, _p, _p, _p]),
     "moe_hbm_read_probe": (ctypes.c_int, [_p, _i64, _i32, _p, _p]),
+    "moe_shared_ffn_workspace": (_sz, [ctypes.POINTER(Experts), _i32]),
+    "moe_shared_ffn": (ctypes.c_int, [ctypes.POINTER(Experts), _p, _i32, _p, _p, _sz, _p]),
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_version": (ctypes.c_int, []),
@@ -290,6 +292,16 @@ class ExpertCache:
         v = [ctypes.c_int64() for _ in range(4)]
         _check(_lib.moe_cache_stats(self._h, *[ctypes.byref(x) for x in v]), "moe_cache_stats")
         return dict(zip(("steps", "hits", "misses", "bytes_filled"), (x.value for x in v)))
+
+
+def moe_shared_ffn_workspace(W: Experts, T: int) -> int:
+    return int(_lib.moe_shared_ffn_workspace(ctypes.byref(W), T))
+
+
+def moe_shared_ffn(W: Experts, x: torch.Tensor, T: int, y: torch.Tensor, ws: torch.Tensor,
+                   stream=None) -> None:
+    _check(_lib.moe_shared_ffn(ctypes.byref(W), _ptr(x), T, _ptr(y), _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream(stream)), "moe_shared_ffn")
 
 
 def moe_hbm_read_probe(src: torch.Tensor, nbytes: int, grid: int, sink: torch.Tensor,

@@ -17,6 +17,7 @@ import torch
 
 from . import (Experts, experts, moe_combine, moe_expert_ffn, moe_expert_ffn_workspace,
                moe_forward_decode, moe_forward_decode_supported, moe_forward_decode_workspace,
+               moe_shared_ffn, moe_shared_ffn_workspace,
                moe_permute, moe_permute_workspace, moe_route, moe_route_permute)
 
 
@@ -71,11 +72,8 @@ class MoELayer:
         self.shared_I = shared_I
         if shared_I:
             self.shared_stride = shared_stride
-            self.s_counts = torch.tensor([T_max], dtype=torch.int32, device=dev)
-            self.s_offsets = torch.tensor([0, T_max], dtype=torch.int32, device=dev)
-            self.s_sorted = torch.arange(T_max, dtype=torch.int32, device=dev)
-            sp = Experts(0, 1, H, shared_I, None, shared_stride)
-            self.s_ws = torch.empty(max(moe_expert_ffn_workspace(sp, T_max, 1), 256),
+            sp = Experts(FMT["bf16"], 1, H, shared_I, None, shared_stride)
+            self.s_ws = torch.empty(max(moe_shared_ffn_workspace(sp, T_max), 256),
                                     dtype=torch.uint8, device=dev)
             self.y_shared = torch.empty((T_max, H), dtype=torch.bfloat16, device=dev)
         # decode-sized batches: the two-launch whole-layer path
@@ -100,11 +98,8 @@ class MoELayer:
                        self.y_perm, self.ffn_ws, variant, stream)
 
     def shared_ffn(self, Ws: Experts, x: torch.Tensor, T: int, variant="auto", stream=None):
-        if T != self.T_max:
-            self.s_counts.fill_(T)
-            self.s_offsets[1].fill_(T)
-        moe_expert_ffn(Ws, None, x, T, 1, self.s_counts, self.s_offsets, self.s_sorted,
-                       self.y_shared, self.s_ws, variant, stream)
+        """The always-on shared expert (bf16 record): dense, every token (moe_shared_ffn)."""
+        moe_shared_ffn(Ws, x, T, self.y_shared, self.s_ws, stream)
 
     def combine(self, T: int, with_shared: bool, stream=None):
         moe_combine(self.y_perm, self.inv_idx, self.w, T, self.k, self.H,

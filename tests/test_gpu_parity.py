@@ -355,3 +355,30 @@ def test_hbm_read_probe_reads_every_word():
         torch.cuda.synchronize()
         got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
         assert got == np.bitwise_xor.reduce(host), grid
+
+
+@pytest.mark.parametrize("T,H,I", [(1, 512, 256), (37, 512, 256), (300, 1024, 512)])
+def test_shared_ffn_dense(T, H, I):
+    """moe_shared_ffn (dense bf16 GEMMs) against the oracle's SwiGLU and against the
+    routed-expert kernels run as one expert with k = 1 over every token."""
+    from oracle import ffn as OFF
+    flush(f"[shared-ffn] T={T} H={H} I={I}")
+    rec = synth.make_shared_record(81, H, I, device="cuda")
+    W = moe.experts("bf16", 1, H, I, rec, rec.shape[1])
+    xb = synth.make_x(synth.Workload("sh", T=T, H=H, E=1, I=I, k=1, fmt="bf16", seed=82), 0)
+    x = torch.from_numpy(xb.view(np.int16)).to("cuda").view(torch.bfloat16)
+    y = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(moe.moe_shared_ffn_workspace(W, T), dtype=torch.uint8, device="cuda")
+    moe.moe_shared_ffn(W, x, T, y, ws)
+    # the same FFN through moe_expert_ffn: one expert, k = 1, identity permutation
+    counts = torch.tensor([T], dtype=torch.int32, device="cuda")
+    offsets = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+    sidx = torch.arange(T, dtype=torch.int32, device="cuda")
+    y2 = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+    ws2 = torch.empty(moe.moe_expert_ffn_workspace(W, T, 1), dtype=torch.uint8, device="cuda")
+    moe.moe_expert_ffn(W, None, x, T, 1, counts, offsets, sidx, y2, ws2)
+    torch.cuda.synchronize()
+    ex = OL.ExpertSet("bf16", H, I, lambda e: rec[0].cpu().numpy())
+    ref = OFF.swiglu(OF.bf16_value(xb), *ex.weights(0))
+    assert rel_err(bf16_to_np(y), ref) <= TOL
+    assert rel_err(bf16_to_np(y), bf16_to_np(y2)) <= TOL
