@@ -5,7 +5,8 @@
   and of the separate-call path, in every weight format;
 * every supported K chunking (H and I of 512 .. 2048), both down-projection
   forms (token-major for small T, tile-major + combine above it) and k not a
-  multiple of the 4 waves;
+  multiple of the 4 waves; the MXFP4 one-stream path at every H/128 chunk
+  count and with two rounds of units;
 * repeated calls with varying batch sizes on one workspace and
   bit-repeatable results;
 * slot-table indirection;
@@ -93,6 +94,20 @@ def _check_case(wl, seed_note=""):
 def test_decode_layer_matches_oracle_and_separate_calls(fmt):
     flush(f"[decode-layer] {fmt}")
     _check_case(DEC[fmt])
+
+
+# MXFP4 shapes that take the one-stream path (T*k*(I/128) a multiple of 256,
+# E <= 256): every H/128 chunk count, two rounds of units (T = 16, or I = 1024),
+# and the full decode workload's expert count
+@pytest.mark.parametrize("H,I,T,k,E", [(1024, 512, 8, 8, 64), (1536, 512, 8, 8, 64),
+                                       (2048, 512, 16, 8, 256), (512, 1024, 8, 8, 128),
+                                       (2048, 512, 8, 8, 256)])
+def test_decode_layer_one_stream_shapes(H, I, T, k, E):
+    flush(f"[decode-one-stream] H={H} I={I} T={T} k={k} E={E}")
+    assert (T * k * (I // 128)) % 256 == 0
+    wl = synth.Workload(f"dec_fu_{H}_{I}_{T}", T=T, H=H, E=E, I=I, k=k, fmt="mxfp4",
+                        seed=90 + H // 512 + T)
+    _check_case(wl)
 
 
 @pytest.mark.parametrize("H,I,T,k", [(1024, 1536, 6, 4), (2048, 2048, 6, 4), (1536, 1024, 6, 4),
