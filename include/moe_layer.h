@@ -228,7 +228,9 @@ int moe_dequant_expert(const moe_experts* W, int32_t expert, float* w13, float* 
  *   gate/up and down are bf16 GEMMs with fp32 accumulation (hipBLASLt);
  *   h = bf16(SiLU(gate) * up) between them, from the fp32 gate/up values.
  *   ws: device, >= moe_shared_ffn_workspace(W, T) bytes (fp32 gate/up
- *   values, h, and the GEMM library's scratch); enqueued on `stream`.
+ *   values, h, and the GEMM library's scratch); enqueued on `stream`.  The
+ *   first call on a device creates a hipBLASLt handle (that library's own
+ *   allocation, kept until the process ends); later calls allocate nothing.
  * Other formats return MOE_ERR_UNSUPPORTED (moe_expert_ffn with E = 1, k = 1
  * computes the same for any format). */
 size_t moe_shared_ffn_workspace(const moe_experts* W, int32_t T);
