@@ -1214,12 +1214,17 @@ static size_t dec_ws_bytes(int fmt, int E, int H, int I, int T, int k) {
   return n;
 }
 
-// Enough for every batch of at most T tokens (the partials exist for T <= 16 only).
+// Enough for every batch of at most T tokens: the partials exist only for the
+// batch sizes that take the one-stream path (some T' <= 16), so the size is
+// the largest over T' <= T.
 extern "C" size_t moe_forward_decode_workspace(const moe_experts* W, int32_t T, int32_t k) {
   if (!W || T < 0 || k < 1) return 0;
-  const size_t a = dec_ws_bytes(W->fmt, W->E, W->H, W->I, T, k);
-  const size_t b = dec_ws_bytes(W->fmt, W->E, W->H, W->I, T < kTokMaxT ? T : kTokMaxT, k);
-  return a > b ? a : b;
+  size_t n = dec_ws_bytes(W->fmt, W->E, W->H, W->I, T, k);
+  for (int t2 = 1; t2 <= T && t2 <= kTokMaxT; ++t2) {
+    const size_t m = dec_ws_bytes(W->fmt, W->E, W->H, W->I, t2, k);
+    n = m > n ? m : n;
+  }
+  return n;
 }
 
 extern "C" int moe_forward_decode(const moe_experts* W, const int32_t* slot_of_expert,

@@ -190,3 +190,18 @@ def test_cache_fill_requires_device_pieces():
     with pytest.raises(m.MoeError) as e:
         m.ExpertCache(1, 8, 0, 256)
     assert e.value.status == m.MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("fmt", synth.FORMATS)
+@pytest.mark.parametrize("H,I,E", [(2048, 512, 256), (512, 1024, 128), (2048, 2048, 64)])
+def test_decode_workspace_serves_smaller_batches(fmt, H, I, E):
+    """The decode-layer workspace sized for T also fits every batch of T' <= T tokens
+    (the MXFP4 one-stream path's partials exist only for some batch sizes)."""
+    W = m.experts(fmt, E, H, I, None, synth.record_layout(fmt, H, I)["stride"])
+    k = 8
+    sizes = [m.moe_forward_decode_workspace(W, T, k) for T in range(0, 65)]
+    for T in range(65):
+        assert sizes[T] >= max(sizes[:T + 1]), (T, sizes[T], max(sizes[:T + 1]))
+    # the h and y_perm sections alone
+    for T in (1, 8, 16, 64):
+        assert sizes[T] >= T * k * (I + H) * 2

@@ -110,6 +110,24 @@ def test_decode_layer_one_stream_shapes(H, I, T, k, E):
     _check_case(wl)
 
 
+def test_one_stream_batch_inside_a_larger_workspace():
+    """A layer sized for 12 tokens runs an 8-token batch on the one-stream path (its
+    partials need more workspace than 12 tokens on the two-kernel path), then 12
+    and 3 tokens on the same workspace, each matching the oracle."""
+    wl = synth.Workload("dec_ws12", T=12, H=512, E=64, I=512, k=8, fmt="mxfp4", seed=97)
+    flush("[decode-ws] T_max=12")
+    case = Case(wl)
+    layer = _layer(case)
+    W = layer.weights(case.records)
+    ex = case.oracle_experts()
+    for T in (8, 12, 3, 8):
+        lg = case.logits[:T].contiguous()
+        x = case.x[:T].contiguous()
+        d = _decode(layer, W, lg, x)
+        ref = OL.forward(case.logits_np[:T], case.x_np[:T], wl.k, ex)
+        assert rel_err(bf16_to_np(d["y"][:T]), ref["y"]) <= TOL, T
+
+
 @pytest.mark.parametrize("H,I,T,k", [(1024, 1536, 6, 4), (2048, 2048, 6, 4), (1536, 1024, 6, 4),
                                      (512, 512, 16, 13), (512, 1024, 32, 4), (2048, 512, 24, 8)])
 def test_decode_layer_chunkings(H, I, T, k):
