@@ -143,7 +143,7 @@ int moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t k, int3
  * scales are applied to fp32 partial sums.  For the block-scaled MFMA the
  * bf16 activations (x, then h) are split into E4M3 hi + lo with one E8M0
  * scale per 32; hi + lo differs from the bf16 value by at most 2^-10 times
- * the block scale, i.e. less than 2^-17 of the block's largest magnitude.  The activation
+ * the block scale, i.e. at most 2^-17 of the block's largest magnitude.  The activation
  * is not named on the pages; SwiGLU is the plainest reading for the MoE
  * families the guide lists.
  *   slot_of_expert  device int32 [E] or NULL (identity); only entries of
@@ -164,7 +164,11 @@ int moe_expert_ffn(const moe_experts* W, const int32_t* slot_of_expert, const ui
                    size_t ws_bytes, moe_stream_t stream);
 
 /* ---------------------------------------------------------------------------
- * moe_combine — weighted sum of each token's k expert outputs:
+ * moe_combine — weighted sum of each token's k expert outputs.  The pages
+ * say a token activates a few experts of its layer (guide, "MoE strategies";
+ * feature article, its activated-experts passage) and print no formula for
+ * how their outputs merge; the plainest reading, taken here, is the
+ * routing-weighted sum of the activated experts' outputs:
  *   y[t] = sum_{j<k} topk_w[t][j] * y_perm[inv_idx[t*k+j]]  (+ y_shared[t])
  * summed in j order in fp32, rounded once to bf16 (nearest-even).
  *   y_perm device bf16 [T*k][H]; inv_idx device int32 [T*k];
@@ -358,17 +362,6 @@ int moe_cache_stats(moe_cache_t cache, int64_t* steps, int64_t* hits, int64_t* m
 
 /* ---------------------------------------------------------------------------
  * Diagnostics. */
-/* ---------------------------------------------------------------------------
- * Measurement helper (not a step of the layer).  moe_hbm_read_probe enqueues
- * one plain streaming read of `bytes` bytes at `src` (device, 16-byte
- * aligned, bytes a multiple of 16) by `grid` workgroups of 256 threads; each
- * thread writes one fold of what it read to sink[block*256 + thread] (device,
- * grid*256 uint32, caller-owned).  Its time is the cost of a pure read of that
- * many bytes on this chip: the practical ceiling for a bandwidth-bound kernel
- * of the same size, next to the 8 TB/s published peak. */
-int moe_hbm_read_probe(const void* src, int64_t bytes, int32_t grid, uint32_t* sink,
-                       moe_stream_t stream);
-
 const char* moe_status_str(int status);
 const char* moe_last_error(void); /* thread-local; "" when none */
 int moe_version(void);            /* ABI version, currently 1 */

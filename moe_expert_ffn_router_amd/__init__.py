@@ -74,7 +74,6 @@ _SIGS = {
     "expert_cache_wait_group": (ctypes.c_int, [_p, _i32, _p]),
     "moe_cache_resize": (ctypes.c_int, [_p, _i32, _p, _p, _p, _p, _p, _p]),
     "moe_cache_stats": (ctypes.c_int, [_p, _p, _p, _p, _p]),
-    "moe_hbm_read_probe": (ctypes.c_int, [_p, _i64, _i32, _p, _p]),
     "moe_shared_ffn_workspace": (_sz, [ctypes.POINTER(Experts), _i32]),
     "moe_shared_ffn": (ctypes.c_int, [ctypes.POINTER(Experts), _p, _i32, _p, _p, _sz, _p]),
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -302,13 +301,6 @@ def moe_shared_ffn(W: Experts, x: torch.Tensor, T: int, y: torch.Tensor, ws: tor
                    stream=None) -> None:
     _check(_lib.moe_shared_ffn(ctypes.byref(W), _ptr(x), T, _ptr(y), _ptr(ws),
                                ws.numel() * ws.element_size(), _stream(stream)), "moe_shared_ffn")
-
-
-def moe_hbm_read_probe(src: torch.Tensor, nbytes: int, grid: int, sink: torch.Tensor,
-                       stream=None) -> None:
-    assert nbytes <= src.numel() * src.element_size() and sink.numel() >= grid * 256
-    _check(_lib.moe_hbm_read_probe(_ptr(src), nbytes, grid, _ptr(sink), _stream(stream)),
-           "moe_hbm_read_probe")
 
 
 def moe_version() -> int:

@@ -19,7 +19,10 @@ OBJ = os.path.join(ROOT, "_build", "obj")
 ARCH = "gfx950"
 
 SOURCES = ["status.cpp", "cache.cpp", "route.hip", "permute.hip", "ffn.hip", "combine.hip",
-           "decode.hip", "probe.hip", "shared.hip"]
+           "decode.hip", "shared.hip"]
+# measurement helpers: a library of their own (include/moe_measure.h)
+MEASURE_SOURCES = ["measure/hbm_read.hip"]
+MEASURE_OUT = os.path.join(PKG, "libmoe_measure.so")
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -38,7 +41,7 @@ def hipcc() -> str:
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, src + ".o")
+    obj = os.path.join(OBJ, src.replace("/", "_") + ".o")
     cmd = [hipcc()] + COMMON + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
@@ -52,10 +55,22 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _link(objs: list[str], out: str, libs: list[str]) -> None:
+    tmp = out + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs + libs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, out)
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    srcs = SOURCES + MEASURE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), 8)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[len(SOURCES):], MEASURE_OUT, [])
+    objs = objs[:len(SOURCES)]
     tmp = OUT + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs + [
         "-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]

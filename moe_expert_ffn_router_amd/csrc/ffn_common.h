@@ -88,8 +88,12 @@ __device__ __forceinline__ void e4m3_hi_lo(float a0, float a1, float a2, float a
 // in A order ([rows][K] each) and one E8M0 scale per 32 consecutive K
 // ([rows][K/32]), by NT threads (thread index `tid`).  The block scale 2^e
 // puts the block's largest magnitude in [128, 256); hi = RNE_e4m3(x / 2^e)
-// and lo = RNE_e4m3(x / 2^e - hi), so hi + lo carries the bf16 value (its 8
-// significant bits: hi takes 4, the residual at most 4 more).  Work goes in
+// and lo = RNE_e4m3(x / 2^e - hi).  hi takes the top 4 significant bits of
+// the bf16 value and the residual at most 4 more, so hi + lo equals x / 2^e
+// whenever that residual is a multiple of 2^-9 (the E4M3 subnormal step),
+// i.e. for |x / 2^e| >= 1/4; smaller elements (more than 2^9 below the block
+// maximum) lose the bits under 2^-9, an error of at most 2^-10 * 2^e, at most
+// 2^-17 of the block's largest magnitude.  Work goes in
 // rounds of NT*4 16-byte pieces: prep_a_mx_load issues one round's loads,
 // prep_a_mx_store converts and stores them, so the loads of the first round
 // can be issued early and other loads issued behind them.

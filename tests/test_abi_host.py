@@ -22,26 +22,41 @@ from oracle import lru as OL
 m = pytest.importorskip("moe_expert_ffn_router_amd")
 
 
-def _declared_functions():
+def _declared_functions(header: str):
     names = set()
-    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
-        src = open(h).read()
-        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-        for mm in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(",
-                              src, flags=re.M):
-            name = mm.group(1)
-            if name not in ("if", "sizeof", "defined"):
-                names.add(name)
+    src = open(os.path.join(ROOT, "include", header)).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    for mm in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(",
+                          src, flags=re.M):
+        name = mm.group(1)
+        if name not in ("if", "sizeof", "defined"):
+            names.add(name)
     return sorted(names)
 
 
+def test_every_header_is_checked():
+    assert sorted(os.path.basename(h) for h in glob.glob(os.path.join(ROOT, "include", "*.h"))) \
+        == ["moe_layer.h", "moe_measure.h"]
+
+
 def test_every_declared_symbol_is_exported():
-    declared = _declared_functions()
+    declared = _declared_functions("moe_layer.h")
     assert len(declared) >= 14, declared
     lib = ctypes.CDLL(m.LIB_PATH)
     missing = [n for n in declared if not hasattr(lib, n)]
     assert not missing, missing
     assert set(declared) == set(m.exported_symbols())
+
+
+def test_measure_library_exports_its_header():
+    from moe_expert_ffn_router_amd import measure
+    declared = _declared_functions("moe_measure.h")
+    lib = ctypes.CDLL(measure.LIB_PATH)
+    assert declared and all(hasattr(lib, n) for n in declared)
+    assert set(declared) == set(measure.exported_symbols())
+    # the layer's library carries no measurement helper
+    assert not hasattr(ctypes.CDLL(m.LIB_PATH), "moe_measure_hbm_read")
+    assert measure._lib.moe_measure_hbm_read(None, 16, 1, None, None) == 1
 
 
 @pytest.mark.parametrize("fmt", synth.FORMATS)

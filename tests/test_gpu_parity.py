@@ -343,15 +343,16 @@ def test_layer_empty_batch():
 
 
 def test_hbm_read_probe_reads_every_word():
-    """The read calibration reads each 16-byte piece exactly once: the XOR of all
-    threads' folds is the XOR of every 32-bit word of the region."""
+    """The read calibration (measurement library) reads each 16-byte piece exactly once:
+    the XOR of all threads' folds is the XOR of every 32-bit word of the region."""
+    from moe_expert_ffn_router_amd import measure
     rng = np.random.default_rng(7)
     n = (3 << 20) + 16 * 37  # not a multiple of the grid's stride
     host = rng.integers(0, 2**32, size=n // 4, dtype=np.uint32)
     src = torch.from_numpy(host.view(np.int32)).to("cuda")
     for grid in (1, 300, 2048):
         sink = torch.zeros(grid * 256, dtype=torch.int32, device="cuda")
-        moe.moe_hbm_read_probe(src, n, grid, sink)
+        measure.moe_measure_hbm_read(src, n, grid, sink)
         torch.cuda.synchronize()
         got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
         assert got == np.bitwise_xor.reduce(host), grid
