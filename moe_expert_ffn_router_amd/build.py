@@ -70,14 +70,7 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(len(srcs), 8)) as ex:
         objs = list(ex.map(_compile, srcs))
     _link(objs[len(SOURCES):], MEASURE_OUT, [])
-    objs = objs[:len(SOURCES)]
-    tmp = OUT + ".tmp"
-    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs + [
-        "-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    _link(objs[:len(SOURCES)], OUT, [])
     if verbose:
         print(f"[build] wrote {OUT}")
     return OUT

@@ -29,6 +29,7 @@
 //    tiles on 8 waves whose operands are copied into LDS by the memory path
 //    itself (no registers hold loads in flight), three K chunks deep.
 #include "ffn_common.h"
+#include "lds_copy.h"
 
 namespace moe {
 
@@ -943,12 +944,6 @@ __global__ __launch_bounds__(256) void ffn_down_mx_kernel(FfnArgs a) {
 // ---------------------------------------------------------------------------
 // m-tiles per super-tile (8, 16, 32 and 64 measured within 4 %; 8 best)
 constexpr int kDmaSuperM = 8;
-// Swizzles of the 16-byte units of a row, chosen so that the 16-byte
-// fragment reads hit distinct banks both per 8 lanes (32 banks) and per
-// 16 lanes (64 banks): 16 consecutive rows reading the same unit spread over
-// all banks.  A rows are 128 B (8 units), weight rows 64 B (4 units).
-__device__ __forceinline__ int a_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-__device__ __forceinline__ int b_swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 template <int BM, int BN>
 struct MxDmaStage {
   uint8_t ah[BM * 128];  // A hi [row][128 B]: 16-byte unit u stored at u ^ a_swz(row)
@@ -961,33 +956,6 @@ struct MxDmaStage {
   __attribute__((aligned(16))) uint32_t as[BM];
   __attribute__((aligned(16))) uint32_t bs[BN];
 };
-
-// Copies of 16 bytes (4 bytes) per lane from base + off into LDS at lds +
-// 16 * lane (4 * lane).  Issued as inline assembly: the compiler then sees no
-// pending LDS write (it would otherwise wait for every copy in flight before
-// any LDS read it cannot prove disjoint), and every wait on these copies is
-// the explicit one in MOE_DMA_SYNC.  No register receives data (the address
-// registers are read at issue).
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, const void* lds) {
-  const uint32_t l = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(off), "s"(base), "s"(l) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const uint8_t* base, uint32_t off, const void* lds) {
-  const uint32_t l = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
-               :: "v"(off), "s"(base), "s"(l) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-// s_waitcnt vmcnt(N) lgkmcnt(0) (expcnt not waited), then a barrier that the
-// compiler moves no memory access across
-#define MOE_DMA_SYNC(N)                                  \
-  do {                                                   \
-    __builtin_amdgcn_s_waitcnt((N) | 0x070);             \
-    asm volatile("s_barrier" ::: "memory");              \
-  } while (0)
 
 template <bool GATED, int MB, int WAVES, int BN>
 __device__ __forceinline__ void ffn_mx_dma_body(const FfnArgs& a, MxDmaStage<MB * 64, BN>& s0,

@@ -1,88 +1,204 @@
 // The always-on shared expert: a dense SwiGLU FFN over every token, with no
-// routing or permutation, so its two products are plain bf16 GEMMs and go to
-// hipBLASLt (fp32 accumulation); the SiLU(gate)*up step between them is the
-// one kernel of this file.
-//   gate/up:  G[T][2I] fp32 = x[T][H] * W13^T    (W13 [2I][H]: gate rows, then up rows)
-//   h:        h[T][I] = bf16( SiLU(G[:, i]) * G[:, I + i] )
-//   down:     y[T][H] = bf16( h * W2^T )          (W2 [H][I])
-// In hipBLASLt's column-major terms each product is D = op(A) * B with A the
-// weight matrix (stored K-major, so op = transpose) and B the activations.
-#include <hipblaslt/hipblaslt.h>
-
-#include <mutex>
-
+// routing or permutation — two dense bf16 products on the 32x32x16 bf16 MFMA
+// with fp32 accumulation:
+//   gate/up:  h[T][I] = bf16( SiLU(x W_gate^T) * (x W_up^T) )   (fused epilogue)
+//   down:     y[T][H] = bf16( h W2^T )
+// x [T][H], W13 [2I][H] (gate rows, then up rows), W2 [H][I]: every operand is
+// K-major, so both GEMMs are C[M][N] = A[M][K] . B[N][K]^T.
+//
+// Tiling (gfx950, 160 KB LDS per CU): 256 output rows x 256 weight rows per
+// workgroup of 4 waves (2 x 2), each wave 128 x 128 outputs as 4 x 4 blocks of
+// 32 x 32 (16 accumulators of 16 fp32, kept in AGPRs: one wave per SIMD).
+// Operands are copied from global memory straight into LDS
+// (global_load_lds_dwordx4) in K steps of 32 (64-byte rows, 32 KB per stage),
+// four stages: chunks c+1 .. c+3 are in flight while chunk c is computed, one
+// barrier per chunk.  Gate/up tiles take 128 h columns: the 256 weight rows
+// are, per wave half, 64 gate rows followed by the matching 64 up rows, so
+// SiLU(gate) * up is formed in registers.  Workgroups are mapped to
+// rectangles of tiles per XCD (consecutive workgroups of one XCD share their
+// A rows or weight rows in its L2).
+//   32x32x16 operands: lane l holds row (A) / column (B) l % 32 and the 8
+//   consecutive K at 8 * (l / 32) of the step's 16; result value v of lane l
+//   is C[8 * (v / 4) + 4 * (l / 32) + v % 4][l % 32].
+#include "lds_copy.h"
 #include "moe_internal.h"
 
 namespace moe {
-
-__global__ __launch_bounds__(256) void swiglu_rows_kernel(const float* __restrict__ g, int T, int I,
-                                                          uint16_t* __restrict__ h) {
-  const size_t n = (size_t)T * I;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
-    const size_t t = i / I, c = i - t * I;
-    const float gv = g[t * 2 * I + c], uv = g[t * 2 * I + I + c];
-    h[i] = f32_to_bf16_rne(gv / (1.0f + expf(-gv)) * uv);
-  }
-}
-
 namespace {
 
-constexpr size_t kLtWorkspace = 64u << 20;  // hipBLASLt's own scratch inside the caller's workspace
-constexpr int kMaxDevices = 64;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-std::mutex g_mu;
-hipblasLtHandle_t g_handle[kMaxDevices] = {};
+constexpr int kSgBM = 256;     // output rows per workgroup
+constexpr int kSgBN = 256;     // weight rows per workgroup
+constexpr int kSgBK = 32;      // K per stage (64-byte rows)
+constexpr int kSgStages = 4;
+constexpr int kSgCopies = kSgBM * kSgBK * 2 / 1024 / 4;  // 1 KB copies of A (and of B) per wave
 
-hipblasLtHandle_t handle_for_device() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  std::lock_guard<std::mutex> lk(g_mu);
-  if (!g_handle[dev] && hipblasLtCreate(&g_handle[dev]) != HIPBLAS_STATUS_SUCCESS)
-    g_handle[dev] = nullptr;
-  return g_handle[dev];
+struct SgStage {
+  uint8_t a[kSgBM * kSgBK * 2];  // [row][64 B], 16-byte unit u stored at u ^ b_swz(row)
+  uint8_t b[kSgBN * kSgBK * 2];
+};
+
+struct SgArgs {
+  const uint8_t* a;  // bf16 [M][K]
+  const uint8_t* w;  // bf16 [N][K]
+  uint16_t* out;     // bf16: gated h [M][I], else y [M][N]
+  int M, K, N, I;    // N: weight rows (gated: 2I)
+  int tm, tn;        // tiles along M and along the output columns
+  int rm, rn, nrn;   // tile rectangle worked on by one XCD at a time; rectangles along N
+};
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void pin_acc(f32x16& acc) { asm volatile("" : "+a"(acc)); }
+
+template <bool GATED>
+__global__ __launch_bounds__(256, 1) void shared_gemm_kernel(SgArgs p) {
+  __shared__ SgStage st[kSgStages];
+  // block -> (XCD-contiguous index) -> rectangle -> tile
+  const int G = (int)gridDim.x, b = (int)blockIdx.x;
+  const int v = (b & 7) * (G >> 3) + (b >> 3);  // G is a multiple of 8
+  const int per = p.rm * p.rn;
+  const int rect = v / per, pos = v - rect * per;
+  const int rect_m = rect / p.nrn, rect_n = rect - rect_m * p.nrn;
+  const int tmi = rect_m * p.rm + pos / p.rn, tni = rect_n * p.rn + pos % p.rn;
+  if (tmi >= p.tm || tni >= p.tn) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int mh = wave >> 1, nh = wave & 1;
+  const int K = p.K, nch = K / kSgBK;
+  const int m0 = tmi * kSgBM;
+
+  // this wave's copies: local rows 16n + lane/4 (n = wave*kSgCopies + q), unit lane%4
+  const uint8_t* abase = p.a + (size_t)m0 * K * 2;
+  const uint8_t* wbase = GATED ? p.w : p.w + (size_t)tni * kSgBN * K * 2;
+  const int last_row = p.M - 1 - m0;  // rows past M read the last row (outputs discarded)
+  uint32_t ao[kSgCopies], wo[kSgCopies];
+#pragma unroll
+  for (int q = 0; q < kSgCopies; ++q) {
+    const int lr = (wave * kSgCopies + q) * 16 + (lane >> 2);
+    const int ar = lr < last_row ? lr : last_row;
+    ao[q] = (uint32_t)ar * (uint32_t)(K * 2) + (uint32_t)(((lane & 3) ^ b_swz(lr)) * 16);
+    int wr;
+    if constexpr (GATED) {
+      // per wave half: 64 gate rows, then the matching 64 up rows
+      const int half = lr >> 7, j = (lr >> 5) & 3, l = lr & 31;
+      const int col = tni * 128 + half * 64 + (j & 1) * 32 + l;
+      wr = j < 2 ? col : p.I + col;
+    } else {
+      const int rows_left = p.N - 1 - tni * kSgBN;
+      wr = lr < rows_left ? lr : rows_left;
+    }
+    wo[q] = (uint32_t)wr * (uint32_t)(K * 2) + (uint32_t)(((lane & 3) ^ b_swz(lr)) * 16);
+  }
+  auto issue = [&](int c, SgStage& S) {
+    const uint32_t kb = (uint32_t)(c * kSgBK * 2);
+#pragma unroll
+    for (int q = 0; q < kSgCopies; ++q) {
+      const int n = wave * kSgCopies + q;
+      dma16(abase, ao[q] + kb, S.a + n * 1024);
+      dma16(wbase, wo[q] + kb, S.b + n * 1024);
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  auto compute = [&](const SgStage& S) {
+#pragma unroll
+    for (int s = 0; s < kSgBK / 16; ++s) {
+      const int u = 2 * s + hh;
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = mh * 128 + i * 32 + l32;
+        af[i] = *reinterpret_cast<const bf16x8*>(S.a + r * 64 + ((u ^ b_swz(r)) * 16));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = nh * 128 + j * 32 + l32;
+        bfr[j] = *reinterpret_cast<const bf16x8*>(S.b + r * 64 + ((u ^ b_swz(r)) * 16));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+          pin_acc(acc[i][j]);
+        }
+    }
+  };
+
+  // prologue: chunks 0..2 in flight
+#pragma unroll
+  for (int c = 0; c < kSgStages - 1; ++c)
+    if (c < nch) issue(c, st[c]);
+  for (int c = 0; c < nch; ++c) {
+    // chunk c's copies done (the later in-flight chunks may still be pending),
+    // every wave's reads of chunk c-1 done
+    const int ahead = nch - 1 - c;
+    if (ahead >= 2) MOE_DMA_SYNC(4 * kSgCopies);
+    else if (ahead == 1) MOE_DMA_SYNC(2 * kSgCopies);
+    else MOE_DMA_SYNC(0);
+    if (c + kSgStages - 1 < nch) issue(c + kSgStages - 1, st[(c + kSgStages - 1) % kSgStages]);
+    compute(st[c % kSgStages]);
+  }
+
+  const int row0 = m0 + mh * 128 + 4 * hh;
+  if constexpr (GATED) {
+    const int col0 = tni * 128 + nh * 64 + l32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = row0 + i * 32 + 8 * (r >> 2) + (r & 3);
+          if (row < p.M) {
+            const float g = acc[i][jj][r], uv = acc[i][jj + 2][r];
+            p.out[(size_t)row * p.I + col0 + jj * 32] = f32_to_bf16_rne(g / (1.0f + expf(-g)) * uv);
+          }
+        }
+  } else {
+    const int col0 = tni * kSgBN + nh * 128 + l32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = row0 + i * 32 + 8 * (r >> 2) + (r & 3);
+          const int col = col0 + j * 32;
+          if (row < p.M && col < p.N) p.out[(size_t)row * p.N + col] = f32_to_bf16_rne(acc[i][j][r]);
+        }
+  }
 }
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
-// D[n_out][T] (column-major, ld n_out) = op_T(Wt: K x n_out, ld K) * X (K x T, ld K)
-int lt_gemm(hipblasLtHandle_t h, const void* w, const void* x, void* d, hipDataType d_type,
-            int n_out, int T, int K, void* lt_ws, hipStream_t s, const char* what) {
-  hipblasLtMatmulDesc_t desc = nullptr;
-  hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, ld = nullptr;
-  hipblasLtMatmulPreference_t pref = nullptr;
-  int st = MOE_OK;
-  const hipblasOperation_t opT = HIPBLAS_OP_T, opN = HIPBLAS_OP_N;
-  const uint64_t wsb = kLtWorkspace;
-  const float alpha = 1.0f, beta = 0.0f;
-  hipblasLtMatmulHeuristicResult_t res{};
-  int n_res = 0;
-  if (hipblasLtMatmulDescCreate(&desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS ||
-      hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opT, sizeof(opT)) !=
-          HIPBLAS_STATUS_SUCCESS ||
-      hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opN, sizeof(opN)) !=
-          HIPBLAS_STATUS_SUCCESS ||
-      hipblasLtMatrixLayoutCreate(&la, HIP_R_16BF, K, n_out, K) != HIPBLAS_STATUS_SUCCESS ||
-      hipblasLtMatrixLayoutCreate(&lb, HIP_R_16BF, K, T, K) != HIPBLAS_STATUS_SUCCESS ||
-      hipblasLtMatrixLayoutCreate(&ld, d_type, n_out, T, n_out) != HIPBLAS_STATUS_SUCCESS ||
-      hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS ||
-      hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb,
-                                            sizeof(wsb)) != HIPBLAS_STATUS_SUCCESS) {
-    st = set_error(MOE_ERR_HIP, "%s: hipBLASLt descriptor set-up failed", what);
-  } else if (hipblasLtMatmulAlgoGetHeuristic(h, desc, la, lb, ld, ld, pref, 1, &res, &n_res) !=
-                 HIPBLAS_STATUS_SUCCESS ||
-             n_res < 1) {
-    st = set_error(MOE_ERR_UNSUPPORTED, "%s: hipBLASLt has no algorithm for %d x %d x %d", what,
-                   n_out, T, K);
-  } else if (hipblasLtMatmul(h, desc, &alpha, w, la, x, lb, &beta, d, ld, d, ld, &res.algo, lt_ws,
-                             kLtWorkspace, s) != HIPBLAS_STATUS_SUCCESS) {
-    st = set_error(MOE_ERR_HIP, "%s: hipblasLtMatmul failed", what);
-  }
-  if (pref) hipblasLtMatmulPreferenceDestroy(pref);
-  if (ld) hipblasLtMatrixLayoutDestroy(ld);
-  if (lb) hipblasLtMatrixLayoutDestroy(lb);
-  if (la) hipblasLtMatrixLayoutDestroy(la);
-  if (desc) hipblasLtMatmulDescDestroy(desc);
-  return st;
+// Launch one dense product: tiles (tm x tn) walked as rectangles of up to 32
+// tiles per XCD round (rn tiles along N).
+template <bool GATED>
+int launch_gemm(SgArgs p, hipStream_t s, const char* what) {
+  p.tm = (p.M + kSgBM - 1) / kSgBM;
+  p.tn = GATED ? p.I / 128 : (p.N + kSgBN - 1) / kSgBN;
+  p.rn = p.tn >= 8 ? 8 : p.tn >= 4 ? 4 : p.tn >= 2 ? 2 : 1;
+  while (p.rn > 1 && p.tn % p.rn && p.tn % (p.rn / 2) == 0) p.rn /= 2;
+  p.rm = 32 / p.rn;
+  p.nrn = (p.tn + p.rn - 1) / p.rn;
+  const int nrm = (p.tm + p.rm - 1) / p.rm;
+  const int64_t blocks = (int64_t)nrm * p.nrn * p.rm * p.rn;
+  const int64_t grid = (blocks + 7) / 8 * 8;
+  if (grid > (int64_t)1 << 30) return set_error(MOE_ERR_UNSUPPORTED, "%s: too many tiles", what);
+  shared_gemm_kernel<GATED><<<(unsigned)grid, 256, 0, s>>>(p);
+  return check_launch(what);
 }
 
 }  // namespace
@@ -90,10 +206,10 @@ int lt_gemm(hipblasLtHandle_t h, const void* w, const void* x, void* d, hipDataT
 
 using namespace moe;
 
-// Workspace: G fp32 [T][2I] | h bf16 [T][I] | hipBLASLt scratch (64 MiB).
+// Workspace: h bf16 [T][I].
 extern "C" size_t moe_shared_ffn_workspace(const moe_experts* W, int32_t T) {
   if (!W || T < 0) return 0;
-  return align256((size_t)T * 2 * W->I * 4) + align256((size_t)T * W->I * 2) + kLtWorkspace;
+  return align256((size_t)T * W->I * 2);
 }
 
 extern "C" int moe_shared_ffn(const moe_experts* W, const uint16_t* x, int32_t T, uint16_t* y,
@@ -110,20 +226,24 @@ extern "C" int moe_shared_ffn(const moe_experts* W, const uint16_t* x, int32_t T
     return set_error(MOE_ERR_INVALID_ARG, "moe_shared_ffn: null or misaligned pointer");
   if (ws_bytes < moe_shared_ffn_workspace(W, T))
     return set_error(MOE_ERR_WORKSPACE, "moe_shared_ffn: workspace %zu too small", ws_bytes);
-  hipblasLtHandle_t h = handle_for_device();
-  if (!h) return set_error(MOE_ERR_HIP, "moe_shared_ffn: hipblasLtCreate failed");
   const int H = W->H, I = W->I;
+  // offsets inside one 256-row tile and inside a weight matrix are 32-bit
+  if ((int64_t)2 * I * H * 2 >= ((int64_t)1 << 32))
+    return set_error(MOE_ERR_UNSUPPORTED, "moe_shared_ffn: weights of %d x %d too large", H, I);
   const uint8_t* rec = static_cast<const uint8_t*>(W->base);  // expert 0
-  uint8_t* wsb = static_cast<uint8_t*>(ws);
-  float* g = reinterpret_cast<float*>(wsb);
-  uint16_t* hb = reinterpret_cast<uint16_t*>(wsb + align256((size_t)T * 2 * I * 4));
-  void* lt_ws = wsb + align256((size_t)T * 2 * I * 4) + align256((size_t)T * I * 2);
+  uint16_t* hb = static_cast<uint16_t*>(ws);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  int st = lt_gemm(h, rec + Lo.w13, x, g, HIP_R_32F, 2 * I, T, H, lt_ws, s, "moe_shared_ffn gate/up");
+  SgArgs g{};
+  g.a = reinterpret_cast<const uint8_t*>(x);
+  g.w = rec + Lo.w13;
+  g.out = hb;
+  g.M = T; g.K = H; g.N = 2 * I; g.I = I;
+  int st = launch_gemm<true>(g, s, "moe_shared_ffn gate/up");
   if (st) return st;
-  const size_t n = (size_t)T * I;
-  const unsigned grid = (unsigned)std::min<size_t>((n + 255) / 256, 65536);
-  swiglu_rows_kernel<<<grid, 256, 0, s>>>(g, T, I, hb);
-  if ((st = check_launch("moe_shared_ffn"))) return st;
-  return lt_gemm(h, rec + Lo.w2, hb, y, HIP_R_16BF, H, T, I, lt_ws, s, "moe_shared_ffn down");
+  SgArgs d{};
+  d.a = reinterpret_cast<const uint8_t*>(hb);
+  d.w = rec + Lo.w2;
+  d.out = y;
+  d.M = T; d.K = I; d.N = H; d.I = I;
+  return launch_gemm<false>(d, s, "moe_shared_ffn down");
 }

@@ -358,10 +358,14 @@ def test_hbm_read_probe_reads_every_word():
         assert got == np.bitwise_xor.reduce(host), grid
 
 
-@pytest.mark.parametrize("T,H,I", [(1, 512, 256), (37, 512, 256), (300, 1024, 512)])
+@pytest.mark.parametrize("T,H,I", [(1, 512, 256), (37, 512, 256), (300, 1024, 512),
+                                   (257, 384, 128), (600, 768, 384), (1030, 1280, 640),
+                                   (513, 2048, 1024)])
 def test_shared_ffn_dense(T, H, I):
-    """moe_shared_ffn (dense bf16 GEMMs) against the oracle's SwiGLU and against the
-    routed-expert kernels run as one expert with k = 1 over every token."""
+    """moe_shared_ffn (dense bf16 GEMMs, 256-row tiles: ragged row tails, column tails
+    of the down product when H is not a multiple of 256, one or several gate/up
+    column tiles) against the oracle's SwiGLU and against the routed-expert kernels
+    run as one expert with k = 1 over every token."""
     from oracle import ffn as OFF
     flush(f"[shared-ffn] T={T} H={H} I={I}")
     rec = synth.make_shared_record(81, H, I, device="cuda")
