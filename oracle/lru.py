@@ -27,7 +27,20 @@ residents with the latest recency (ties: lower slot), drop the rest, and place
 the kept ones, in ascending order of their old slot, into slots 0, 1, ...;
 recencies and the clock are unchanged.
 
-Parity: pinned by a hand-worked trace (tests/golden), by the textbook LRU
+Waves (a step that needs more experts than the pool holds; README feature
+list, "full-layer double-buffered prefill streaming"; the feature article's
+two-buffer mechanism: one buffer is computed on while the next is filled).
+The pages give no rule; the reading taken is: when |needed| > S the step runs
+in waves of at most floor(S/2) experts (two staging sets) — the experts
+already resident first, then the others, each class ascending — and each wave
+is one step of the policy above (one clock tick).  A wave's slots then carry
+the newest recency, and the next wave never lacks older victims (it needs at
+most floor(S/2) slots besides them), so its fills never evict an expert the
+wave before it reads: wave w+1 can be copied while wave w computes.  With
+S = 1 the waves hold one expert each and follow one another.  A step with
+|needed| <= S is a single wave (the step above).
+
+Parity: pinned by hand-worked traces (tests/golden), by the textbook LRU
 stack-distance rule on single-expert steps, by a textbook recency-list LRU
 whose capacity changes between steps, and by invariants.
 """
@@ -79,6 +92,27 @@ class LruSlots:
             "hits": len(needed) - len(misses),
             "misses": len(misses),
         }
+
+    def waves(self, layer: int, counts) -> list:
+        """The experts of one step, split into the waves described above."""
+        counts = np.asarray(counts)
+        needed = [int(e) for e in np.nonzero(counts > 0)[0]]
+        if len(needed) <= self.S:
+            return [needed] if needed else []
+        size = max(1, self.S // 2)
+        order = ([e for e in needed if (layer, e) in self.where]
+                 + [e for e in needed if (layer, e) not in self.where])
+        return [order[i:i + size] for i in range(0, len(order), size)]
+
+    def step_waves(self, layer: int, counts) -> list:
+        """One step in waves: the per-wave results of step(), in wave order."""
+        counts = np.asarray(counts)
+        out = []
+        for wave in self.waves(layer, counts):
+            cw = np.zeros_like(counts)
+            cw[wave] = counts[wave]
+            out.append(self.step(layer, cw))
+        return out
 
     def resize(self, new_S: int) -> list:
         """New pool size; returns the (old slot, new slot) of every kept resident."""

@@ -189,3 +189,71 @@ def test_resize_invariants_multi_expert(seed):
         counts[rng.permutation(E)[:n]] = 1
         r = c.step(layer, counts)
         assert len(set(r["slot_of"].values())) == n and all(0 <= s < c.S for s in r["slot_of"].values())
+
+
+# ---- waves (a step needing more experts than the pool holds) --------------
+def _wave_trace():
+    rows = []
+    with open(os.path.join(GOLDEN, "lru_waves_trace.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            S, layer, needed, waves, fills = [p.strip() for p in line.split("|")]
+            waves = [[int(v) for v in w.split()] for w in waves.split(";")]
+            fills = [[] if fw.strip() == "-" else
+                     [tuple(int(v) for v in f_.split(":")) for f_ in fw.split()]
+                     for fw in fills.split(";")]
+            rows.append((int(S), int(layer), [int(v) for v in needed.split()], waves, fills))
+    return rows
+
+
+def test_waves_hand_worked_trace():
+    caches = {}
+    for S, layer, needed, waves, fills in _wave_trace():
+        c = caches.setdefault(S, lru.LruSlots(S))
+        counts = np.zeros(8, np.int32)
+        counts[needed] = 1 + np.arange(len(needed))
+        assert c.waves(layer, counts) == waves, (S, needed)
+        res = c.step_waves(layer, counts)
+        assert [r["fills"] for r in res] == fills, (S, needed)
+        assert [r["needed"] for r in res] == waves
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_waves_invariants(seed):
+    rng = np.random.default_rng(100 + seed)
+    S, E = int(rng.integers(1, 12)), int(rng.integers(8, 40))
+    c = lru.LruSlots(S)
+    for t in range(60):
+        layer = int(rng.integers(0, 2))
+        counts = (rng.random(E) < rng.uniform(0.05, 0.8)) * rng.integers(1, 9, E)
+        needed = [int(e) for e in np.nonzero(counts)[0]]
+        resident = {e for e in needed if (layer, e) in c.where}
+        if len(needed) <= S:
+            ref = lru.LruSlots(S)
+            ref.owner, ref.recency = list(c.owner), list(c.recency)
+            ref.where, ref.clock = dict(c.where), c.clock
+            one = ref.step(layer, counts)
+        waves = c.waves(layer, counts)
+        res = c.step_waves(layer, counts)
+        assert sorted(e for w in waves for e in w) == needed
+        if len(needed) > S:
+            assert all(len(w) <= max(1, S // 2) for w in waves)
+        else:
+            assert len(res) == (1 if needed else 0)
+            if needed:
+                assert res[0]["fills"] == one["fills"]
+        flat = [e for w in waves for e in w]
+        n_res = sum(1 for e in flat if e in resident)
+        if len(needed) > S:
+            assert set(flat[:n_res]) == resident             # resident experts first
+        prev = set()
+        for w, r in zip(waves, res):
+            assert r["needed"] == sorted(w)
+            if S >= 2:                                        # never evicts the wave before
+                assert not {s for _, s in r["fills"]} & prev
+            assert sorted(r["slot_of"]) == sorted(w)
+            assert len(set(r["slot_of"].values())) == len(w)
+            prev = set(r["slot_of"].values())
+        for e in waves[-1] if waves else []:
+            assert (layer, e) in c.where

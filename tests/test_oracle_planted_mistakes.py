@@ -161,6 +161,26 @@ class _LruResizeNoPacking(LR.LruSlots):
         return moves
 
 
+class _LruWavesOfS(LR.LruSlots):
+    def waves(self, layer, counts):
+        # one staging set: waves as large as the pool
+        counts = np.asarray(counts)
+        needed = [int(e) for e in np.nonzero(counts > 0)[0]]
+        order = ([e for e in needed if (layer, e) in self.where]
+                 + [e for e in needed if (layer, e) not in self.where])
+        return [order[i:i + self.S] for i in range(0, len(order), self.S)]
+
+
+class _LruWavesNotResidentFirst(LR.LruSlots):
+    def waves(self, layer, counts):
+        counts = np.asarray(counts)
+        needed = [int(e) for e in np.nonzero(counts > 0)[0]]
+        if len(needed) <= self.S:
+            return [needed] if needed else []
+        size = max(1, self.S // 2)
+        return [needed[i:i + size] for i in range(0, len(needed), size)]
+
+
 CASES = [
     ("e2m1 exponent bias", F, "e2m1_value", _e2m1_wrong_bias, lambda: T_fmt.test_e2m1_published_table()),
     ("nibble order", F, "unpack_e2m1", _unpack_swapped, lambda: T_fmt.test_nibble_order_low_first()),
@@ -176,6 +196,10 @@ CASES = [
      lambda: [T_lru.test_resize_single_expert_steps_match_textbook_lru(s) for s in range(8)]),
     ("resize does not pack", LR, "LruSlots", _LruResizeNoPacking,
      lambda: T_lru.test_resize_hand_worked()),
+    ("waves as large as the pool", LR, "LruSlots", _LruWavesOfS,
+     lambda: T_lru.test_waves_hand_worked_trace()),
+    ("waves not resident-first", LR, "LruSlots", _LruWavesNotResidentFirst,
+     lambda: T_lru.test_waves_hand_worked_trace()),
 ]
 
 
