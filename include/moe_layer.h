@@ -215,6 +215,27 @@ int moe_forward_decode(const moe_experts* W, const int32_t* slot_of_expert, cons
                        size_t ws_bytes, moe_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_forward_decode_noalloc — for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): moe_forward_decode with the same arguments and results but no
+ * workspace argument.  Its scratch (h, y_perm and the one-stream path's fp32
+ * partials) lives in a fixed array of moe_forward_decode_noalloc_max_scratch()
+ * = 8 MiB of device memory that each GPU the library runs on holds until the
+ * process ends; its device address is looked up on the first call on each
+ * device (hipGetSymbolAddress; nothing is allocated by this library).  A call
+ * whose moe_forward_decode_workspace(W, T, k) exceeds that size returns
+ * MOE_ERR_WORKSPACE before enqueueing anything.  Every call on one GPU shares
+ * that GPU's array (its contents on entry are ignored, nothing needs
+ * clearing): calls that overlap on one GPU (other streams, or other threads)
+ * race and give undefined results; serialise them.                        */
+size_t moe_forward_decode_noalloc_max_scratch(void);
+int moe_forward_decode_noalloc(const moe_experts* W, const int32_t* slot_of_expert,
+                               const float* logits, const uint16_t* x, int32_t T, int32_t k,
+                               int32_t renorm, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                               int32_t* offsets, int32_t* sorted_idx, int32_t* inv_idx,
+                               const uint16_t* y_shared, uint16_t* y, moe_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * moe_dequant_expert — decode one expert record to fp32 with the same device
  * decoders the FFN kernels use (for checking every code on the device).
  *   w13 device fp32 [2I][H] (out), w2 device fp32 [H][I] (out); the NVFP4

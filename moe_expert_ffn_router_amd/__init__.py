@@ -64,6 +64,9 @@ _SIGS = {
     "moe_forward_decode_workspace": (_sz, [ctypes.POINTER(Experts), _i32, _i32]),
     "moe_forward_decode": (ctypes.c_int, [ctypes.POINTER(Experts), _p, _p, _p, _i32, _i32, _i32, _p,
                                           _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_forward_decode_noalloc_max_scratch": (_sz, []),
+    "moe_forward_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(Experts), _p, _p, _p, _i32, _i32,
+                                                  _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "moe_dequant_expert": (ctypes.c_int, [ctypes.POINTER(Experts), _i32, _p, _p, _p]),
     "moe_cache_create": (ctypes.c_int, [ctypes.POINTER(_p), _i32, _i32, _i32, _i64, _p, _p, _p]),
     "moe_cache_destroy": (None, [_p]),
@@ -206,6 +209,24 @@ def moe_forward_decode(W: Experts, slot_of_expert, logits, x, k: int, topk_ids, 
                                    _ptr(offsets), _ptr(sorted_idx), _ptr(inv_idx), _ptr(y_shared),
                                    _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
                                    _stream(stream)), "moe_forward_decode")
+
+
+def moe_forward_decode_noalloc_max_scratch() -> int:
+    return int(_lib.moe_forward_decode_noalloc_max_scratch())
+
+
+def moe_forward_decode_noalloc(W: Experts, slot_of_expert, logits, x, k: int, topk_ids, topk_w,
+                               counts, offsets, sorted_idx, inv_idx, y_shared, y,
+                               renorm: bool = True, stream=None) -> None:
+    """moe_forward_decode with the library's fixed per-device scratch (no workspace)."""
+    _dev_check(slot_of_expert, logits, x, topk_ids, topk_w, counts, offsets, sorted_idx, inv_idx,
+               y_shared, y)
+    T = logits.shape[0]
+    _check(_lib.moe_forward_decode_noalloc(ctypes.byref(W), _ptr(slot_of_expert), _ptr(logits),
+                                           _ptr(x), T, k, int(renorm), _ptr(topk_ids),
+                                           _ptr(topk_w), _ptr(counts), _ptr(offsets),
+                                           _ptr(sorted_idx), _ptr(inv_idx), _ptr(y_shared),
+                                           _ptr(y), _stream(stream)), "moe_forward_decode_noalloc")
 
 
 def moe_dequant_expert(W: Experts, expert: int, w13, w2, stream=None) -> None:

@@ -1306,3 +1306,61 @@ extern "C" int moe_forward_decode_supported(int32_t H, int32_t I, int32_t T, int
                         sizeof(int) * kDA;
   return gu_lds <= 160 * 1024;  // the token-major down's h rows (k <= 16) always fit
 }
+
+// ---------------------------------------------------------------------------
+// moe_forward_decode_noalloc: the same layer call with its scratch (h, y_perm
+// and the one-stream path's fp32 partials) in a fixed array of device memory
+// that every GPU holds for the life of the process, for callers that cannot
+// allocate (graph capture, tight serving loops).  The array's host-side name
+// is only a stand-in: its device address is looked up once per device with
+// hipGetSymbolAddress and that pointer is what the kernels receive.
+// ---------------------------------------------------------------------------
+#include <mutex>
+
+static constexpr size_t kNoAllocScratchBytes = 8u << 20;
+static constexpr int kNoAllocMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+static std::mutex g_scratch_mu;
+static void* g_scratch_dev[kNoAllocMaxDevices] = {};
+
+static int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoAllocMaxDevices)
+    return set_error(MOE_ERR_HIP, "moe_forward_decode_noalloc: no current device (or index >= %d)",
+                     kNoAllocMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return set_error(MOE_ERR_HIP, "moe_forward_decode_noalloc: hipGetSymbolAddress: %s",
+                       hipGetErrorString(e));
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return MOE_OK;
+}
+
+extern "C" size_t moe_forward_decode_noalloc_max_scratch(void) { return kNoAllocScratchBytes; }
+
+extern "C" int moe_forward_decode_noalloc(const moe_experts* W, const int32_t* slot_of_expert,
+                                          const float* logits, const uint16_t* x, int32_t T,
+                                          int32_t k, int32_t renorm, int32_t* topk_ids,
+                                          float* topk_w, int32_t* counts, int32_t* offsets,
+                                          int32_t* sorted_idx, int32_t* inv_idx,
+                                          const uint16_t* y_shared, uint16_t* y,
+                                          moe_stream_t stream) {
+  if (!W) return set_error(MOE_ERR_INVALID_ARG, "moe_forward_decode_noalloc: W is NULL");
+  const size_t need = moe_forward_decode_workspace(W, T, k);
+  if (need > kNoAllocScratchBytes)
+    return set_error(MOE_ERR_WORKSPACE,
+                     "moe_forward_decode_noalloc: T=%d k=%d H=%d I=%d needs %zu bytes of scratch; "
+                     "the static scratch holds %zu (use moe_forward_decode with a workspace)",
+                     T, k, W->H, W->I, need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  const int st = scratch_of_current_device(&ws);
+  if (st) return st;
+  return moe_forward_decode(W, slot_of_expert, logits, x, T, k, renorm, topk_ids, topk_w, counts,
+                            offsets, sorted_idx, inv_idx, y_shared, y, ws, kNoAllocScratchBytes,
+                            stream);
+}
