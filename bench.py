@@ -528,30 +528,62 @@ def bench_cached(args, wl, steps, warmup, want_cpu: bool):
     # to host) replayed through the same policy on host-only handles, waves as above
     sweep = None
     if args.slot_sweep:
-        from moe_expert_ffn_router_amd.layer import plan_waves
         counts = {}
         for li in range(L):
             for b in range(nb):
                 layer.route_permute(logits[li][b])
-                counts[li, b] = layer.counts[:E].cpu().numpy().copy()
+                counts[li, b] = layer.counts[:E].cpu().clone()
         sweep = []
         for S_s in [int(v) for v in args.slot_sweep.split(",")]:
             h = moe.ExpertCache(L, E, S_s, stride)
             m_t = n_t = w_t = 0
             for i in range(warmup + steps):
                 for li in range(L):
-                    c = counts[li, i % nb]
-                    for wave in plan_waves(c, S_s, h.expert_cache_row(li).numpy()):
-                        cw = np.zeros(E, dtype=np.int32)
-                        cw[wave] = c[wave]
-                        _, _, nm, nh, _ = h.expert_cache_lookup(li, torch.from_numpy(cw))
-                        if i >= warmup:
-                            m_t, n_t, w_t = m_t + nm, n_t + nm + nh, w_t + 1
+                    r = h.expert_cache_plan(li, counts[li, i % nb])
+                    if i >= warmup:
+                        m_t, n_t = m_t + r["misses"], n_t + r["misses"] + r["hits"]
+                        w_t += r["n_waves"]
             h.close()
             sweep.append({"slots": S_s, "misses_per_layer_step": round(m_t / (steps * L), 2),
                           "hit_rate": round(1 - m_t / max(1, n_t), 4),
                           "waves_per_layer_step": round(w_t / (steps * L), 2),
                           "fill_gb_per_layer_step": round(m_t * payload / (steps * L) / 1e9, 3)})
+
+    # waves: a pool smaller than one step's experts (two staging sets of S/2 slots:
+    # each wave's copies overlap the FFN of the wave before), same bank and batches,
+    # timed against the fill floor of its own copies
+    wave_case = None
+    if L == 1 and args.slots is None:
+        S_w = 48
+        pool_w = torch.empty((S_w, stride), dtype=torch.uint8, device=dev)
+        table_w = torch.full((E,), -1, dtype=torch.int32, device=dev)
+        cache_w = moe.ExpertCache(1, E, S_w, stride, pool_w, bank, table_w)
+        pool_Ww = moe.experts(wl.fmt, E, wl.H, wl.I, pool_w, stride)
+        n_w = 6
+        layer.forward_streamed(logits[0][0], xs[0], 0, cache_w, pool_Ww, table_w, side=side,
+                               groups=args.fill_groups or 1)
+        torch.cuda.synchronize()
+        s0 = cache_w.stats()
+        w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        wv = []
+        w0.record()
+        for i in range(n_w):
+            _, info = layer.forward_streamed(logits[0][(1 + i) % nb], xs[(1 + i) % nb], 0,
+                                             cache_w, pool_Ww, table_w, side=side,
+                                             groups=args.fill_groups or 1)
+            wv.append(info["waves"])
+        w1.record()
+        torch.cuda.synchronize()
+        wms = w0.elapsed_time(w1) / n_w
+        wbytes = (cache_w.stats()["bytes_filled"] - s0["bytes_filled"]) / n_w
+        wave_case = {"pool_slots": S_w, "steps": n_w, "ms_per_step": round(wms, 3),
+                     "waves_per_step": round(float(np.mean(wv)), 2),
+                     "fill_gb_per_step": round(wbytes / 1e9, 3),
+                     "fill_floor_ms_per_step": round(wbytes / (h2d_gbs_probe(torch, pool_w, bank, side)
+                                                               * 1e9) * 1e3, 3)}
+        wave_case["frac_of_fill_floor"] = round(wave_case["fill_floor_ms_per_step"] / wms, 4)
+        cache_w.close()
+        del cache_w, pool_w, table_w
 
     # elastic resize of the live pool (in place): halve it, keeping the most recently
     # used residents, then grow back; wall time of each host-synchronous call
@@ -653,6 +685,7 @@ def bench_cached(args, wl, steps, warmup, want_cpu: bool):
                   "resize_ms": {"to_%d" % max(1, S // 2): round(shrink_ms, 2),
                                 "to_%d" % S: round(grow_ms, 2)},
                   "slot_sweep": sweep},
+        "waves": wave_case,
         "roofline": roof,
     }
     if want_cpu:
@@ -662,6 +695,18 @@ def bench_cached(args, wl, steps, warmup, want_cpu: bool):
     gc.collect()
     torch.cuda.empty_cache()
     return res
+
+
+def h2d_gbs_probe(torch, pool, bank, side) -> float:
+    """Pinned host -> HBM copy rate of whole expert records on `side` (GB/s)."""
+    n = min(16, pool.shape[0])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(side)
+    with torch.cuda.stream(side):
+        pool[:n].copy_(bank[:n], non_blocking=True)
+    e1.record(side)
+    torch.cuda.synchronize()
+    return n * pool.shape[1] / (e0.elapsed_time(e1) / 1e3) / 1e9
 
 
 # ---------------------------------------------------------------------------
@@ -785,10 +830,9 @@ def main():
         "roofline": hr["roofline"],
         "cpu_baseline": hr.get("cpu_baseline"),
     }
-    for key in ("cpu_baseline_1thread", "end_to_end", "fill_path", "hit_path", "cache",
-                "shared_expert", "layer_roofline"):
-        if key in hr:
-            out[key] = hr[key]
+    for key, val in hr.items():
+        if key not in out and key not in ("workload", "unit", "steps", "warmup", "dtype_note"):
+            out[key] = val
     if per:
         out["per_workload"] = per
     out["host"] = {"cpu": cpu_info(), "affinity_cores": len(os.sched_getaffinity(0))}

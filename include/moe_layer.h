@@ -348,6 +348,62 @@ int expert_cache_fill_groups(moe_cache_t cache, int32_t layer, const int32_t* mi
  * n_groups names an older, already recorded group). */
 int expert_cache_wait_group(moe_cache_t cache, int32_t group, moe_stream_t compute);
 
+/* expert_cache_plan — the policy for one (layer-)step that may need more
+ * distinct experts than the pool holds (README feature list, "full-layer
+ * double-buffered prefill streaming"; feature article, its two-buffer
+ * mechanism: one buffer computed on while the next is filled).  The pages give
+ * no rule; read here as: if the step's experts fit (|needed| <= S) they form
+ * one wave, otherwise waves of at most floor(S/2) experts (at least one),
+ * resident experts first, then the others, each ascending.  Each wave is one
+ * lookup (the policy above, one clock tick).  Under that policy a wave never
+ * evicts an expert the wave before it reads (S >= 2), so the next wave's
+ * copies can overlap the current wave's FFN.  Never refuses for capacity.
+ *   counts_host     host int32 [E]
+ *   wave_of_expert  host int32 [E] (out, may be NULL): wave of each needed
+ *                   expert, -1 for the others
+ *   fill_expert, fill_slot  host int32 [E] (out, may be NULL): all fills, wave
+ *                   by wave, each wave's in lookup order
+ *   wave_fill_end   host int32 [E] (out, may be NULL): wave w's fills are
+ *                   [wave_fill_end[w-1], wave_fill_end[w]) (0 for w = 0)
+ *   n_waves, n_hit  host (out; n_hit may be NULL)
+ * Host-only; touches no device memory. */
+int expert_cache_plan(moe_cache_t cache, int32_t layer, const int32_t* counts_host,
+                      int32_t* wave_of_expert, int32_t* fill_expert, int32_t* fill_slot,
+                      int32_t* wave_fill_end, int32_t* n_waves, int32_t* n_hit);
+
+/* moe_expert_ffn_streamed — moe_expert_ffn for one (layer-)step through the
+ * cache's pool, with the fills streamed under the computation (README feature
+ * list, "full-layer double-buffered prefill streaming"; guide, "MoE
+ * strategies" offload):
+ *   the step is planned as in expert_cache_plan; for each wave, the layer's
+ *   slot-table row is published on `compute`, the wave's misses are copied
+ *   host->device on `side` in min(n_groups, misses) groups of equal size (to
+ *   within one), the expert FFN runs on `compute` over the wave's hit experts
+ *   at once and over each group's experts once that group has landed.  Wave
+ *   w's copies wait only for the FFN work of wave w-2 (and everything enqueued
+ *   on `compute` before the call): two staging sets.  y_perm rows of every
+ *   needed expert are written exactly as by one moe_expert_ffn call (same
+ *   tiles; bit-identical).
+ *   pool_W          the cache's pool as experts: E = the cache's E, base = its
+ *                   pool, stride = its slot_bytes
+ *   x, T, k, offsets, sorted_idx, y_perm   as for moe_expert_ffn (device)
+ *   counts_host     host int32 [E]: the caller's copy of moe_permute's counts
+ *   n_groups        1..16
+ *   ws              device, >= moe_expert_ffn_streamed_workspace(pool_W, T, k)
+ *   fill_expert, fill_slot, wave_fill_end, n_waves, n_hit   as for
+ *                   expert_cache_plan (host out, each may be NULL)
+ * Returns without waiting; the slot-table row for `layer` on the device is the
+ * one after the last wave once `compute` reaches the end of the call's work.
+ * Allocates nothing (the handle's pinned per-wave records are reused; the host
+ * blocks only when a record's previous copy is still pending). */
+size_t moe_expert_ffn_streamed_workspace(const moe_experts* pool_W, int32_t T, int32_t k);
+int moe_expert_ffn_streamed(moe_cache_t cache, int32_t layer, const moe_experts* pool_W,
+                            const uint16_t* x, int32_t T, int32_t k, const int32_t* counts_host,
+                            const int32_t* offsets, const int32_t* sorted_idx, uint16_t* y_perm,
+                            int32_t n_groups, void* ws, size_t ws_bytes, moe_stream_t side,
+                            moe_stream_t compute, int32_t* fill_expert, int32_t* fill_slot,
+                            int32_t* wave_fill_end, int32_t* n_waves, int32_t* n_hit);
+
 /* moe_cache_resize — change the pool to new_S slots at run time, without
  * reloading the experts that stay resident (FlashML-org / FreeToken README
  * feature list, elastic VRAM: the expert cache and the KV cache re-split while
@@ -375,6 +431,98 @@ int expert_cache_wait_group(moe_cache_t cache, int32_t group, moe_stream_t compu
 int moe_cache_resize(moe_cache_t cache, int32_t new_S, void* new_pool_dev, int32_t* move_from,
                      int32_t* move_to, int32_t* n_moves, moe_stream_t side,
                      moe_stream_t compute);
+
+/* ---------------------------------------------------------------------------
+ * CPU execution of experts (guide, "MoE strategies": the cpu strategy computes
+ * missed experts on the CPU from host memory; hybrid splits one step's misses
+ * between fetching over PCIe and CPU execution, both at once; "CPU layer
+ * split": the CPU executor serves bf16, nvfp4 and mxfp4 experts — this one
+ * also serves fp8).  A pool of host threads owned by the handle. */
+typedef struct moe_cpu_pool* moe_cpu_pool_t;
+int moe_cpu_pool_create(moe_cpu_pool_t* out, int32_t threads); /* threads incl. the caller's */
+void moe_cpu_pool_destroy(moe_cpu_pool_t pool);
+
+/* moe_cpu_expert_ffn — the expert FFN of moe_expert_ffn on the CPU, for the
+ * listed experts only, all operands in host memory:
+ *   W          experts whose base is HOST memory (e.g. one layer of the pinned
+ *              bank: record of expert e at base + e * stride)
+ *   experts    host int32 [n_experts] (each once, in [0, E))
+ *   x          host bf16 [T][H];  offsets host int32 [E+1];  sorted_idx host
+ *              int32 [T*k] (as from moe_permute)
+ *   y_perm     host bf16 [T*k][H]: rows [offsets[e], offsets[e+1]) of every
+ *              listed expert are written, others untouched
+ * Weights decode exactly to fp32; products accumulate in fp32 (fixed order);
+ * h = bf16(SiLU(gate) * up) and y are rounded to bf16 as on the GPU path.
+ * Results do not depend on the thread count.  Synchronous; host only. */
+int moe_cpu_expert_ffn(moe_cpu_pool_t pool, const moe_experts* W, const int32_t* experts,
+                       int32_t n_experts, const uint16_t* x, int32_t T, int32_t k,
+                       const int32_t* offsets, const int32_t* sorted_idx, uint16_t* y_perm);
+
+/* moe_bench_bw — calibrate this machine (guide, "use ft bench bw to calibrate";
+ * "hybrid's automatic decision"): the fetch path's rate (pinned host -> device
+ * copies of n_records expert records of bank_W into pool_dev on `stream`) and
+ * the CPU executor's rate (each of those records as an expert with one token
+ * row), both in record payload bytes per second.  hybrid_recommended is set
+ * when the CPU rate is at least `threshold` times the copy rate (the pages'
+ * default threshold is 2.0); fetch_fraction = h2d / (h2d + cpu) is the share
+ * of a step's misses to fetch so that fetching and CPU execution take equal
+ * time (the q* split).  Synchronous; pool_dev holds n_records records. */
+typedef struct {
+  double h2d_bytes_per_s, cpu_bytes_per_s, threshold, fetch_fraction;
+  int32_t hybrid_recommended;
+} moe_bw_profile;
+int moe_bench_bw(moe_cpu_pool_t pool, const moe_experts* bank_W, void* pool_dev,
+                 int32_t n_records, moe_stream_t stream, double threshold, moe_bw_profile* out);
+
+/* expert_cache_plan_hybrid — the policy of one hybrid step (guide, "MoE
+ * strategies": hybrid fetches part of a step's misses over PCIe and computes
+ * the rest on the CPU, overlapped; "expert bank & LRU slot cache": each
+ * (layer, expert)'s most recent active step lets the per-layer fetch cap take
+ * the most active misses first).  The pages fix no rule; read here as:
+ *   misses   = needed experts not resident, ordered by their last active
+ *              step, latest first (never active last; ties lower expert first)
+ *   n_fetch  = ceil(fetch_fraction * |misses|), at most max_fetch when
+ *              max_fetch >= 0 (fetch_fraction 1 = offload, 0 = cpu strategy)
+ *   the first n_fetch misses are fetched: with the hits they form the GPU step
+ *   (planned as expert_cache_plan); the other misses run on the CPU and take
+ *   no slot; their last active step is the step's clock (a step with no GPU
+ *   expert still advances the clock).
+ *   cpu_expert  host int32 [E] (out, may be NULL): the CPU experts, ascending
+ *   n_cpu       host (out);  other outputs as for expert_cache_plan
+ * Host-only; touches no device memory. */
+int expert_cache_plan_hybrid(moe_cache_t cache, int32_t layer, const int32_t* counts_host,
+                             double fetch_fraction, int32_t max_fetch, int32_t* cpu_expert,
+                             int32_t* n_cpu, int32_t* fill_expert, int32_t* fill_slot,
+                             int32_t* wave_fill_end, int32_t* n_waves, int32_t* n_hit);
+
+/* moe_expert_ffn_hybrid — one hybrid step of the expert FFN: the policy of
+ * expert_cache_plan_hybrid; the GPU step runs as in moe_expert_ffn_streamed
+ * (grouped fills on `side`, the FFN behind them on `compute`), and while it
+ * runs the calling thread computes the CPU experts with moe_cpu_expert_ffn
+ * from the cache's bank (x, offsets and sorted_idx are first copied down into
+ * host_stage on `compute`), then copies their y_perm rows up on `compute`.
+ * Returns once the CPU share is done and its rows' copies are enqueued;
+ * `compute` then holds every y_perm row of the step.
+ *   cpu_pool       moe_cpu_pool_create handle
+ *   host_stage     PINNED host memory, >= moe_expert_ffn_hybrid_host_bytes
+ *                  (x, offsets, sorted_idx and the CPU rows); reused by the
+ *                  next call once its copies are done (the call waits)
+ *   fetch_fraction, max_fetch   as for expert_cache_plan_hybrid
+ *   the other arguments and outputs as for moe_expert_ffn_streamed, plus
+ *   cpu_expert / n_cpu (host out) as for expert_cache_plan_hybrid.
+ * CPU experts' y_perm rows are the CPU executor's (fp32 accumulation in
+ * another order: equal to the GPU's within the parity tolerance, not
+ * bit-identical).  Allocates no device memory. */
+size_t moe_expert_ffn_hybrid_host_bytes(const moe_experts* pool_W, int32_t T, int32_t k);
+int moe_expert_ffn_hybrid(moe_cache_t cache, int32_t layer, const moe_experts* pool_W,
+                          moe_cpu_pool_t cpu_pool, const uint16_t* x, int32_t T, int32_t k,
+                          const int32_t* counts_host, const int32_t* offsets,
+                          const int32_t* sorted_idx, uint16_t* y_perm, double fetch_fraction,
+                          int32_t max_fetch, int32_t n_groups, void* ws, size_t ws_bytes,
+                          void* host_stage, size_t host_bytes, moe_stream_t side,
+                          moe_stream_t compute, int32_t* cpu_expert, int32_t* n_cpu,
+                          int32_t* fill_expert, int32_t* fill_slot, int32_t* wave_fill_end,
+                          int32_t* n_waves, int32_t* n_hit);
 
 /* Counters since creation: steps, hits, misses, bytes copied host->device. */
 int moe_cache_stats(moe_cache_t cache, int64_t* steps, int64_t* hits, int64_t* misses,

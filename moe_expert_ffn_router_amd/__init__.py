@@ -44,6 +44,12 @@ class ExpertLayout(ctypes.Structure):
                 ("tensor_scale", _i64), ("payload_bytes", _i64), ("stride", _i64)]
 
 
+class BwProfile(ctypes.Structure):
+    _fields_ = [("h2d_bytes_per_s", ctypes.c_double), ("cpu_bytes_per_s", ctypes.c_double),
+                ("threshold", ctypes.c_double), ("fetch_fraction", ctypes.c_double),
+                ("hybrid_recommended", ctypes.c_int32)]
+
+
 class Experts(ctypes.Structure):
     _fields_ = [("fmt", _i32), ("E", _i32), ("H", _i32), ("I", _i32), ("base", _p),
                 ("stride", _i64)]
@@ -75,8 +81,25 @@ _SIGS = {
     "expert_cache_fill": (ctypes.c_int, [_p, _i32, _p, _p, _i32, _p, _p]),
     "expert_cache_fill_groups": (ctypes.c_int, [_p, _i32, _p, _p, _i32, _i32, _p, _p]),
     "expert_cache_wait_group": (ctypes.c_int, [_p, _i32, _p]),
+    "expert_cache_plan": (ctypes.c_int, [_p, _i32, _p, _p, _p, _p, _p, _p, _p]),
+    "moe_expert_ffn_streamed_workspace": (_sz, [ctypes.POINTER(Experts), _i32, _i32]),
+    "moe_expert_ffn_streamed": (ctypes.c_int, [_p, _i32, ctypes.POINTER(Experts), _p, _i32, _i32,
+                                               _p, _p, _p, _p, _i32, _p, _sz, _p, _p, _p, _p, _p,
+                                               _p, _p]),
     "moe_cache_resize": (ctypes.c_int, [_p, _i32, _p, _p, _p, _p, _p, _p]),
     "moe_cache_stats": (ctypes.c_int, [_p, _p, _p, _p, _p]),
+    "moe_cpu_pool_create": (ctypes.c_int, [ctypes.POINTER(_p), _i32]),
+    "moe_cpu_pool_destroy": (None, [_p]),
+    "moe_cpu_expert_ffn": (ctypes.c_int, [_p, ctypes.POINTER(Experts), _p, _i32, _p, _i32, _i32,
+                                          _p, _p, _p]),
+    "expert_cache_plan_hybrid": (ctypes.c_int, [_p, _i32, _p, ctypes.c_double, _i32, _p, _p, _p,
+                                                _p, _p, _p, _p]),
+    "moe_expert_ffn_hybrid_host_bytes": (_sz, [ctypes.POINTER(Experts), _i32, _i32]),
+    "moe_expert_ffn_hybrid": (ctypes.c_int, [_p, _i32, ctypes.POINTER(Experts), _p, _p, _i32, _i32,
+                                             _p, _p, _p, _p, ctypes.c_double, _i32, _i32, _p, _sz,
+                                             _p, _sz, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "moe_bench_bw": (ctypes.c_int, [_p, ctypes.POINTER(Experts), _p, _i32, _p, ctypes.c_double,
+                                    ctypes.POINTER(BwProfile)]),
     "moe_shared_ffn_workspace": (_sz, [ctypes.POINTER(Experts), _i32]),
     "moe_shared_ffn": (ctypes.c_int, [ctypes.POINTER(Experts), _p, _i32, _p, _p, _sz, _p]),
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -293,6 +316,77 @@ class ExpertCache:
         _check(_lib.expert_cache_wait_group(self._h, group, _stream(compute)),
                "expert_cache_wait_group")
 
+    def expert_cache_plan(self, layer: int, counts_host: torch.Tensor):
+        """The step's waves and fills (host-only policy; advances the cache state)."""
+        c = counts_host.to(torch.int32).contiguous()
+        E = self.E
+        wave_of = torch.zeros(E, dtype=torch.int32)
+        fe, fs, we = (torch.zeros(E, dtype=torch.int32) for _ in range(3))
+        nw, nh = ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib.expert_cache_plan(self._h, layer, _ptr(c), _ptr(wave_of), _ptr(fe), _ptr(fs),
+                                      _ptr(we), ctypes.byref(nw), ctypes.byref(nh)),
+               "expert_cache_plan")
+        return _plan_result(wave_of, fe, fs, we, nw.value, nh.value)
+
+    def moe_expert_ffn_streamed(self, layer: int, pool_W: Experts, x, T: int, k: int,
+                                counts_host: torch.Tensor, offsets, sorted_idx, y_perm,
+                                n_groups: int, ws, side=None, compute=None, out=None):
+        """One step's expert FFN through the pool with streamed fills.  `out` (optional):
+        three host int32 [E] tensors that receive the fills' experts, their slots and each
+        wave's fill end (reused across calls).  Returns (n_waves, n_hit)."""
+        E = self.E
+        if out is None:
+            out = tuple(torch.zeros(E, dtype=torch.int32) for _ in range(3))
+        fe, fs, we = out
+        nw, nh = ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib.moe_expert_ffn_streamed(self._h, layer, ctypes.byref(pool_W), _ptr(x), T, k,
+                                            _ptr(counts_host), _ptr(offsets), _ptr(sorted_idx),
+                                            _ptr(y_perm), n_groups, _ptr(ws),
+                                            ws.numel() * ws.element_size(), _stream(side),
+                                            _stream(compute), _ptr(fe), _ptr(fs), _ptr(we),
+                                            ctypes.byref(nw), ctypes.byref(nh)),
+               "moe_expert_ffn_streamed")
+        return nw.value, nh.value
+
+    def expert_cache_plan_hybrid(self, layer: int, counts_host: torch.Tensor,
+                                 fetch_fraction: float, max_fetch: int = -1) -> dict:
+        """One hybrid step's policy (host only; advances the cache state)."""
+        c = counts_host.to(torch.int32).contiguous()
+        E = self.E
+        cpu, fe, fs, we = (torch.zeros(E, dtype=torch.int32) for _ in range(4))
+        nc, nw, nh = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib.expert_cache_plan_hybrid(self._h, layer, _ptr(c), fetch_fraction, max_fetch,
+                                             _ptr(cpu), ctypes.byref(nc), _ptr(fe), _ptr(fs),
+                                             _ptr(we), ctypes.byref(nw), ctypes.byref(nh)),
+               "expert_cache_plan_hybrid")
+        r = _plan_result(torch.full((E,), -1, dtype=torch.int32), fe, fs, we, nw.value, nh.value)
+        r["cpu"] = cpu[:nc.value].tolist()
+        return r
+
+    def moe_expert_ffn_hybrid(self, layer: int, pool_W: Experts, cpu_pool, x, T: int, k: int,
+                              counts_host: torch.Tensor, offsets, sorted_idx, y_perm,
+                              fetch_fraction: float, max_fetch: int, n_groups: int, ws,
+                              host_stage, side=None, compute=None, out=None):
+        """One hybrid step (see the header).  `out`: four host int32 [E] tensors reused
+        across calls (CPU experts, fills' experts, their slots, wave ends).  Returns
+        (n_cpu, n_waves, n_hit)."""
+        E = self.E
+        if out is None:
+            out = tuple(torch.zeros(E, dtype=torch.int32) for _ in range(4))
+        ce, fe, fs, we = out
+        nc, nw, nh = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib.moe_expert_ffn_hybrid(self._h, layer, ctypes.byref(pool_W), cpu_pool._h,
+                                          _ptr(x), T, k, _ptr(counts_host), _ptr(offsets),
+                                          _ptr(sorted_idx), _ptr(y_perm), fetch_fraction,
+                                          max_fetch, n_groups, _ptr(ws),
+                                          ws.numel() * ws.element_size(), _ptr(host_stage),
+                                          host_stage.numel() * host_stage.element_size(),
+                                          _stream(side), _stream(compute), _ptr(ce),
+                                          ctypes.byref(nc), _ptr(fe), _ptr(fs), _ptr(we),
+                                          ctypes.byref(nw), ctypes.byref(nh)),
+               "moe_expert_ffn_hybrid")
+        return nc.value, nw.value, nh.value
+
     def moe_cache_resize(self, new_S: int, pool=None, side=None, compute=None):
         """Resize to new_S slots (into `pool` if given, else in place); returns the
         (old slot, new slot) pairs of the kept residents as two int32 tensors."""
@@ -312,6 +406,71 @@ class ExpertCache:
         v = [ctypes.c_int64() for _ in range(4)]
         _check(_lib.moe_cache_stats(self._h, *[ctypes.byref(x) for x in v]), "moe_cache_stats")
         return dict(zip(("steps", "hits", "misses", "bytes_filled"), (x.value for x in v)))
+
+
+class CpuPool:
+    """Owner of a moe_cpu_pool_t (host threads of the CPU expert executor)."""
+
+    def __init__(self, threads: int):
+        h = ctypes.c_void_p()
+        _check(_lib.moe_cpu_pool_create(ctypes.byref(h), threads), "moe_cpu_pool_create")
+        self._h = h
+        self.threads = threads
+
+    def close(self):
+        if self._h:
+            _lib.moe_cpu_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _host_check(*ts):
+    for t in ts:
+        if isinstance(t, torch.Tensor) and t.numel() and t.is_cuda:
+            raise ValueError("host tensor expected")
+
+
+def moe_cpu_expert_ffn(pool: CpuPool, W: Experts, experts, x, T: int, k: int, offsets, sorted_idx,
+                       y_perm) -> None:
+    """The listed experts' FFN on the CPU (host tensors throughout; W.base is host memory)."""
+    _host_check(experts, x, offsets, sorted_idx, y_perm)
+    ex = experts.to(torch.int32).contiguous()
+    _check(_lib.moe_cpu_expert_ffn(pool._h, ctypes.byref(W), _ptr(ex), int(ex.numel()), _ptr(x), T,
+                                   k, _ptr(offsets), _ptr(sorted_idx), _ptr(y_perm)),
+           "moe_cpu_expert_ffn")
+
+
+def moe_bench_bw(pool: CpuPool, bank_W: Experts, pool_dev, n_records: int, threshold: float = 2.0,
+                 stream=None) -> dict:
+    out = BwProfile()
+    _check(_lib.moe_bench_bw(pool._h, ctypes.byref(bank_W), _ptr(pool_dev), n_records,
+                             _stream(stream), threshold, ctypes.byref(out)), "moe_bench_bw")
+    return {f: getattr(out, f) for f, _ in BwProfile._fields_}
+
+
+def _plan_result(wave_of, fe, fs, we, n_waves: int, n_hit: int) -> dict:
+    ends = we[:n_waves].tolist()
+    starts = [0] + ends[:-1]
+    fills = list(zip(fe[:ends[-1] if ends else 0].tolist(), fs[:ends[-1] if ends else 0].tolist()))
+    waves = [[] for _ in range(n_waves)]
+    for e, w in enumerate(wave_of.tolist()):
+        if w >= 0:
+            waves[w].append(e)
+    return {"waves": waves, "fills": [fills[a:b] for a, b in zip(starts, ends)],
+            "n_waves": n_waves, "hits": n_hit, "misses": len(fills)}
+
+
+def moe_expert_ffn_hybrid_host_bytes(W: Experts, T: int, k: int) -> int:
+    return int(_lib.moe_expert_ffn_hybrid_host_bytes(ctypes.byref(W), T, k))
+
+
+def moe_expert_ffn_streamed_workspace(W: Experts, T: int, k: int) -> int:
+    return int(_lib.moe_expert_ffn_streamed_workspace(ctypes.byref(W), T, k))
 
 
 def moe_shared_ffn_workspace(W: Experts, T: int) -> int:

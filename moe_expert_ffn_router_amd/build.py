@@ -18,7 +18,7 @@ OUT = os.path.join(PKG, "libmoe_mi355x.so")
 OBJ = os.path.join(ROOT, "_build", "obj")
 ARCH = "gfx950"
 
-SOURCES = ["status.cpp", "cache.cpp", "route.hip", "permute.hip", "ffn.hip", "combine.hip",
+SOURCES = ["status.cpp", "cache.cpp", "cpu_expert.cpp", "route.hip", "permute.hip", "ffn.hip", "combine.hip",
            "decode.hip", "shared.hip"]
 # measurement helpers: a library of their own (include/moe_measure.h)
 MEASURE_SOURCES = ["measure/hbm_read.hip"]

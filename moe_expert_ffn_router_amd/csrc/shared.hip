@@ -10,16 +10,18 @@
 // workgroup of 4 waves (2 x 2), each wave 128 x 128 outputs as 4 x 4 blocks of
 // 32 x 32 (16 accumulators of 16 fp32, kept in AGPRs: one wave per SIMD).
 // Operands are copied from global memory straight into LDS
-// (global_load_lds_dwordx4) in K steps of 32 (64-byte rows, 32 KB per stage),
-// four stages: chunks c+1 .. c+3 are in flight while chunk c is computed, one
-// barrier per chunk.  Gate/up tiles take 128 h columns: the 256 weight rows
+// (global_load_lds_dwordx4) in K steps of kSgBK (kSgStages stages: the next
+// kSgStages-1 chunks are in flight while one is computed), one barrier per
+// chunk.  Gate/up tiles take 128 h columns: the 256 weight rows
 // are, per wave half, 64 gate rows followed by the matching 64 up rows, so
 // SiLU(gate) * up is formed in registers.  Workgroups are mapped to
 // rectangles of tiles per XCD (consecutive workgroups of one XCD share their
 // A rows or weight rows in its L2).
 //   32x32x16 operands: lane l holds row (A) / column (B) l % 32 and the 8
 //   consecutive K at 8 * (l / 32) of the step's 16; result value v of lane l
-//   is C[8 * (v / 4) + 4 * (l / 32) + v % 4][l % 32].
+//   is D[8 * (v / 4) + 4 * (l / 32) + v % 4][l % 32].  The weights are the
+//   first operand (D = W X^T): a lane's values are output columns of one
+//   token row, four consecutive per group (one 8-byte store).
 #include "lds_copy.h"
 #include "moe_internal.h"
 
@@ -30,13 +32,25 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kSgBM = 256;     // output rows per workgroup
 constexpr int kSgBN = 256;     // weight rows per workgroup
-constexpr int kSgBK = 32;      // K per stage (64-byte rows)
-constexpr int kSgStages = 4;
-constexpr int kSgCopies = kSgBM * kSgBK * 2 / 1024 / 4;  // 1 KB copies of A (and of B) per wave
+#ifndef MOE_SG_BK
+#define MOE_SG_BK 32
+#endif
+#ifndef MOE_SG_STAGES
+#define MOE_SG_STAGES 4
+#endif
+constexpr int kSgBK = MOE_SG_BK;          // K per stage (32: 64-byte rows, 64: 128-byte rows)
+constexpr int kSgStages = MOE_SG_STAGES;  // kSgStages * (kSgBM + kSgBN) * kSgBK * 2 <= 160 KB
+constexpr int kSgRowB = kSgBK * 2;        // bytes of one row of a stage
+constexpr int kSgUnits = kSgRowB / 16;    // 16-byte units per row
+constexpr int kSgCopies = kSgBM * kSgRowB / 1024 / 4;  // 1 KB copies of A (and of B) per wave
+static_assert(kSgStages * (kSgBM + kSgBN) * kSgRowB <= 160 * 1024, "LDS");
+
+// unit swizzle of a stage row (64-byte rows: b_swz, 128-byte rows: a_swz)
+__device__ __forceinline__ int sg_swz(int r) { return kSgUnits == 4 ? b_swz(r) : a_swz(r); }
 
 struct SgStage {
-  uint8_t a[kSgBM * kSgBK * 2];  // [row][64 B], 16-byte unit u stored at u ^ b_swz(row)
-  uint8_t b[kSgBN * kSgBK * 2];
+  uint8_t a[kSgBM * kSgRowB];  // [row][kSgRowB], 16-byte unit u stored at u ^ sg_swz(row)
+  uint8_t b[kSgBN * kSgRowB];
 };
 
 struct SgArgs {
@@ -71,16 +85,18 @@ __global__ __launch_bounds__(256, 1) void shared_gemm_kernel(SgArgs p) {
   const int K = p.K, nch = K / kSgBK;
   const int m0 = tmi * kSgBM;
 
-  // this wave's copies: local rows 16n + lane/4 (n = wave*kSgCopies + q), unit lane%4
+  // this wave's copies: 1 KB each, local rows (1024 / kSgRowB) n + lane / kSgUnits
+  // (n = wave*kSgCopies + q), unit lane % kSgUnits
   const uint8_t* abase = p.a + (size_t)m0 * K * 2;
   const uint8_t* wbase = GATED ? p.w : p.w + (size_t)tni * kSgBN * K * 2;
   const int last_row = p.M - 1 - m0;  // rows past M read the last row (outputs discarded)
   uint32_t ao[kSgCopies], wo[kSgCopies];
 #pragma unroll
   for (int q = 0; q < kSgCopies; ++q) {
-    const int lr = (wave * kSgCopies + q) * 16 + (lane >> 2);
+    const int lr = (wave * kSgCopies + q) * (1024 / kSgRowB) + lane / kSgUnits;
     const int ar = lr < last_row ? lr : last_row;
-    ao[q] = (uint32_t)ar * (uint32_t)(K * 2) + (uint32_t)(((lane & 3) ^ b_swz(lr)) * 16);
+    const uint32_t unit = (uint32_t)(((lane % kSgUnits) ^ sg_swz(lr)) * 16);
+    ao[q] = (uint32_t)ar * (uint32_t)(K * 2) + unit;
     int wr;
     if constexpr (GATED) {
       // per wave half: 64 gate rows, then the matching 64 up rows
@@ -91,10 +107,10 @@ __global__ __launch_bounds__(256, 1) void shared_gemm_kernel(SgArgs p) {
       const int rows_left = p.N - 1 - tni * kSgBN;
       wr = lr < rows_left ? lr : rows_left;
     }
-    wo[q] = (uint32_t)wr * (uint32_t)(K * 2) + (uint32_t)(((lane & 3) ^ b_swz(lr)) * 16);
+    wo[q] = (uint32_t)wr * (uint32_t)(K * 2) + unit;
   }
   auto issue = [&](int c, SgStage& S) {
-    const uint32_t kb = (uint32_t)(c * kSgBK * 2);
+    const uint32_t kb = (uint32_t)(c * kSgRowB);
 #pragma unroll
     for (int q = 0; q < kSgCopies; ++q) {
       const int n = wave * kSgCopies + q;
@@ -119,18 +135,20 @@ __global__ __launch_bounds__(256, 1) void shared_gemm_kernel(SgArgs p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = mh * 128 + i * 32 + l32;
-        af[i] = *reinterpret_cast<const bf16x8*>(S.a + r * 64 + ((u ^ b_swz(r)) * 16));
+        af[i] = *reinterpret_cast<const bf16x8*>(S.a + r * kSgRowB + ((u ^ sg_swz(r)) * 16));
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = nh * 128 + j * 32 + l32;
-        bfr[j] = *reinterpret_cast<const bf16x8*>(S.b + r * 64 + ((u ^ b_swz(r)) * 16));
+        bfr[j] = *reinterpret_cast<const bf16x8*>(S.b + r * kSgRowB + ((u ^ sg_swz(r)) * 16));
       }
+      // weights as the MFMA's first operand: the result's rows are output columns,
+      // so each lane ends with 4 consecutive columns of one row per value group
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+          acc[i][j] = mfma32(bfr[j], af[i], acc[i][j]);
           pin_acc(acc[i][j]);
         }
     }
@@ -144,40 +162,64 @@ __global__ __launch_bounds__(256, 1) void shared_gemm_kernel(SgArgs p) {
     // chunk c's copies done (the later in-flight chunks may still be pending),
     // every wave's reads of chunk c-1 done
     const int ahead = nch - 1 - c;
-    if (ahead >= 2) MOE_DMA_SYNC(4 * kSgCopies);
-    else if (ahead == 1) MOE_DMA_SYNC(2 * kSgCopies);
-    else MOE_DMA_SYNC(0);
+    if constexpr (kSgStages >= 4) {
+      if (ahead >= 2) MOE_DMA_SYNC(4 * kSgCopies);
+      else if (ahead == 1) MOE_DMA_SYNC(2 * kSgCopies);
+      else MOE_DMA_SYNC(0);
+    } else if constexpr (kSgStages == 3) {
+      if (ahead >= 1) MOE_DMA_SYNC(2 * kSgCopies);
+      else MOE_DMA_SYNC(0);
+    } else {
+      MOE_DMA_SYNC(0);
+    }
     if (c + kSgStages - 1 < nch) issue(c + kSgStages - 1, st[(c + kSgStages - 1) % kSgStages]);
     compute(st[c % kSgStages]);
   }
 
-  const int row0 = m0 + mh * 128 + 4 * hh;
+  // lane: row m0 + mh*128 + 32i + l32; value v of block j: column 32j + 8(v/4) + 4hh + v%4
+  // of the wave's 128 weight rows, so values 4q..4q+3 are 4 consecutive columns
+  const int row_l = m0 + mh * 128 + l32;
   if constexpr (GATED) {
-    const int col0 = tni * 128 + nh * 64 + l32;
+    const int col0 = tni * 128 + nh * 64 + 4 * hh;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      const int row = row_l + i * 32;
+      if (row >= p.M) continue;
+      uint16_t* dst = p.out + (size_t)row * p.I + col0;
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = row0 + i * 32 + 8 * (r >> 2) + (r & 3);
-          if (row < p.M) {
-            const float g = acc[i][jj][r], uv = acc[i][jj + 2][r];
-            p.out[(size_t)row * p.I + col0 + jj * 32] = f32_to_bf16_rne(g / (1.0f + expf(-g)) * uv);
-          }
-        }
-  } else {
-    const int col0 = tni * kSgBN + nh * 128 + l32;
+        for (int q = 0; q < 4; ++q) {
+          uint16_t hv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+          for (int r = 0; r < 4; ++r) {
+            const float g = acc[i][jj][4 * q + r], uv = acc[i][jj + 2][4 * q + r];
+            hv[r] = f32_to_bf16_rne(g / (1.0f + expf(-g)) * uv);
+          }
+          *reinterpret_cast<uint2*>(dst + jj * 32 + 8 * q) =
+              uint2{(uint32_t)hv[0] | ((uint32_t)hv[1] << 16), (uint32_t)hv[2] | ((uint32_t)hv[3] << 16)};
+        }
+    }
+  } else {
+    const int col0 = tni * kSgBN + nh * 128 + 4 * hh;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = row_l + i * 32;
+      if (row >= p.M) continue;
+      uint16_t* dst = p.out + (size_t)row * p.N + col0;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = row0 + i * 32 + 8 * (r >> 2) + (r & 3);
-          const int col = col0 + j * 32;
-          if (row < p.M && col < p.N) p.out[(size_t)row * p.N + col] = f32_to_bf16_rne(acc[i][j][r]);
+        for (int q = 0; q < 4; ++q) {
+          const int col = col0 + j * 32 + 8 * q;  // the 4 columns lie on one side of N (N % 128 == 0)
+          if (col >= p.N) continue;
+          const uint32_t b0 = f32_to_bf16_rne(acc[i][j][4 * q]);
+          const uint32_t b1 = f32_to_bf16_rne(acc[i][j][4 * q + 1]);
+          const uint32_t b2 = f32_to_bf16_rne(acc[i][j][4 * q + 2]);
+          const uint32_t b3 = f32_to_bf16_rne(acc[i][j][4 * q + 3]);
+          *reinterpret_cast<uint2*>(dst + j * 32 + 8 * q) = uint2{b0 | (b1 << 16), b2 | (b3 << 16)};
         }
+    }
   }
 }
 

@@ -4,11 +4,10 @@ Owns the device buffers of one layer (routing results, permutation,
 workspaces, outputs) and issues route -> permute -> expert_ffn -> combine on
 one stream through the C ABI.  With an expert cache, the slot-table path is
 route -> permute -> counts to host -> expert_cache_lookup -> expert_cache_fill
--> expert_ffn (through the slot table) -> combine; the streamed variant
-computes the hit experts while the misses are copied, each group of misses
-as soon as it lands, and takes a step that needs more experts than the pool
-has slots in waves.  No arithmetic happens here; it only sequences library
-calls.
+-> expert_ffn (through the slot table) -> combine; the streamed variant hands
+the whole step to moe_expert_ffn_streamed (waves, grouped fills on a side
+stream, the FFN behind them).  No arithmetic happens here; it only sequences
+library calls.
 """
 from __future__ import annotations
 
@@ -16,6 +15,7 @@ import numpy as np
 import torch
 
 from . import (Experts, experts, moe_combine, moe_expert_ffn, moe_expert_ffn_workspace,
+               moe_expert_ffn_streamed_workspace,
                moe_forward_decode, moe_forward_decode_supported, moe_forward_decode_workspace,
                moe_shared_ffn, moe_shared_ffn_workspace,
                moe_permute, moe_permute_workspace, moe_route, moe_route_permute)
@@ -23,26 +23,6 @@ from . import (Experts, experts, moe_combine, moe_expert_ffn, moe_expert_ffn_wor
 
 def _i32(n, dev):
     return torch.empty(max(int(n), 1), dtype=torch.int32, device=dev)
-
-
-def plan_waves(counts_host, S: int, resident=None) -> list[list[int]]:
-    """The experts one step needs (counts > 0) in waves of at most S: resident
-    experts first (resident[e] >= 0), each class ascending, so that a wave's
-    fills never evict an expert a later wave of the same step could have hit."""
-    c = np.asarray(counts_host).reshape(-1)
-    needed = [int(e) for e in np.nonzero(c > 0)[0]]
-    if resident is not None:
-        r = np.asarray(resident).reshape(-1)
-        needed = [e for e in needed if r[e] >= 0] + [e for e in needed if r[e] < 0]
-    if not needed:
-        return []
-    return [needed[i:i + S] for i in range(0, len(needed), S)]
-
-
-def split_groups(n: int, groups: int) -> list[tuple[int, int]]:
-    """[i0, i1) of each of `groups` consecutive groups of n items, equal to within one (the
-    split expert_cache_fill_groups makes)."""
-    return [(n * g // groups, n * (g + 1) // groups) for g in range(groups)]
 
 
 class MoELayer:
@@ -67,6 +47,10 @@ class MoELayer:
         probe.fmt = FMT[fmt]
         self.ffn_ws = torch.empty(max(moe_expert_ffn_workspace(probe, T_max, k), 256),
                                   dtype=torch.uint8, device=dev)
+        self._probe = probe
+        self.stream_ws = None                 # streamed cache path: made on first use
+        self.counts_host = torch.zeros(E, dtype=torch.int32).pin_memory()
+        self.plan_out = tuple(torch.zeros(E, dtype=torch.int32) for _ in range(3))
         self.y_perm = torch.empty((max(A, 1), H), dtype=torch.bfloat16, device=dev)
         self.y = torch.empty((max(T_max, 1), H), dtype=torch.bfloat16, device=dev)
         self.shared_I = shared_I
@@ -153,46 +137,27 @@ class MoELayer:
     def forward_streamed(self, logits: torch.Tensor, x: torch.Tensor, layer: int, cache,
                          pool_W: Experts, slot_table: torch.Tensor, side=None, groups: int = 4,
                          variant="auto", stream=None) -> tuple[torch.Tensor, dict]:
-        """Slot-table path with the FFN behind the fills.  Per wave (plan_waves: at most
-        S experts): lookup, then expert_cache_fill_groups (the misses in `groups` copy
-        groups on `side`), the expert FFN over the wave's hit experts at once, and over
-        each group's experts once the group has landed (expert_cache_wait_group).  Every
-        FFN call is moe_expert_ffn with the counts of the other experts zeroed: the same
-        tiles, so y is bit-identical to forward_cached whenever that one fits."""
+        """Slot-table path with the FFN behind the fills (moe_expert_ffn_streamed): waves of
+        at most S (or S/2 when the step needs more than S experts), each wave's misses in
+        `groups` copy groups on `side`, the FFN over the hits at once and over each group as
+        it lands.  y is bit-identical to forward_cached whenever that one fits."""
         T = logits.shape[0]
         E = self.E
         cs = stream if stream is not None else torch.cuda.current_stream()
+        if self.stream_ws is None:
+            self.stream_ws = torch.empty(
+                max(moe_expert_ffn_streamed_workspace(self._probe, self.T_max, self.k), 256),
+                dtype=torch.uint8, device=self.device)
         self.route_permute(logits, cs)
-        counts_host = self.counts[:E].to("cpu")          # the one host sync of the step
-        ch = counts_host.numpy()
-        row_dev = slot_table[layer * E:(layer + 1) * E]
-        waves = plan_waves(ch, cache.S, cache.expert_cache_row(layer).numpy())
-        n_hit_all = n_miss_all = 0
-        fills = []
-        for wave in waves:
-            cw = np.zeros(E, dtype=np.int32)
-            cw[wave] = ch[wave]
-            me, ms, n_miss, n_hit, row = cache.expert_cache_lookup(layer, torch.from_numpy(cw))
-            G = min(groups, n_miss)
-            miss = me.tolist()
-            masks = np.zeros((1 + G, (E + 3) // 4 * 4), dtype=np.int32)  # rows 16-byte aligned
-            hit = sorted(set(wave) - set(miss))
-            masks[0, hit] = ch[hit]
-            for g, (i0, i1) in enumerate(split_groups(n_miss, G)):
-                masks[1 + g, miss[i0:i1]] = ch[miss[i0:i1]]
-            with torch.cuda.stream(cs):
-                dm = torch.from_numpy(masks).pin_memory().to(self.device, non_blocking=True)
-            cache.expert_cache_fill_groups(layer, me, ms, G, side=side, compute=cs)
-            if hit:
-                moe_expert_ffn(pool_W, row_dev, x, T, self.k, dm[0], self.offsets, self.sorted_idx,
-                               self.y_perm, self.ffn_ws, variant, cs)
-            for g in range(G):
-                cache.expert_cache_wait_group(g, cs)
-                moe_expert_ffn(pool_W, row_dev, x, T, self.k, dm[1 + g], self.offsets,
-                               self.sorted_idx, self.y_perm, self.ffn_ws, variant, cs)
-            n_hit_all += n_hit
-            n_miss_all += n_miss
-            fills += list(zip(me.tolist(), ms.tolist()))
+        with torch.cuda.stream(cs):
+            self.counts_host.copy_(self.counts[:E], non_blocking=True)
+        cs.synchronize()                                 # the one host sync of the step
+        nw, nh = cache.moe_expert_ffn_streamed(layer, pool_W, x, T, self.k, self.counts_host,
+                                               self.offsets, self.sorted_idx, self.y_perm,
+                                               groups, self.stream_ws, side=side, compute=cs,
+                                               out=self.plan_out)
+        fe, fs, we = self.plan_out
+        n_fill = int(we[nw - 1]) if nw else 0
+        fills = list(zip(fe[:n_fill].tolist(), fs[:n_fill].tolist()))
         self.combine(T, False, cs)
-        return self.y[:T], {"misses": n_miss_all, "hits": n_hit_all, "waves": len(waves),
-                            "fills": fills}
+        return self.y[:T], {"misses": n_fill, "hits": nh, "waves": nw, "fills": fills}

@@ -40,6 +40,20 @@ wave before it reads: wave w+1 can be copied while wave w computes.  With
 S = 1 the waves hold one expert each and follow one another.  A step with
 |needed| <= S is a single wave (the step above).
 
+Hybrid execution (guide, "MoE strategies": in a hybrid step part of the misses
+is fetched over PCIe and the rest computed on the CPU, at the same time; the
+cpu strategy computes every miss on the CPU; "expert bank & LRU slot cache":
+the cache keeps each (layer, expert)'s most recent active step so that the
+per-layer fetch cap takes the most active misses first).  Reading taken:
+every (layer, expert) remembers the step it was last needed in, resident or
+not; a hybrid step fetches n_fetch = ceil(q * misses) of its misses (q the
+fetch fraction: 1 = offload, 0 = cpu; at most max_fetch when that is >= 0),
+the misses ordered by last active step, latest first (never active last; ties
+lower expert first); the rest run on the CPU and take no slot.  The fetched
+misses and the hits form the GPU step (waves as above; a step with no GPU
+expert still advances the clock); CPU experts' last active step is that
+step's clock.
+
 Parity: pinned by hand-worked traces (tests/golden), by the textbook LRU
 stack-distance rule on single-expert steps, by a textbook recency-list LRU
 whose capacity changes between steps, and by invariants.
@@ -62,6 +76,7 @@ class LruSlots:
         self.recency = [-1] * S
         self.where = {}                   # (layer, expert) -> slot
         self.clock = 0
+        self.last_active = {}             # (layer, expert) -> last step it was needed
 
     def step(self, layer: int, counts) -> dict:
         counts = np.asarray(counts)
@@ -84,6 +99,7 @@ class LruSlots:
             fills.append((e, s))
         for e in needed:
             self.recency[self.where[(layer, e)]] = self.clock
+            self.last_active[(layer, e)] = self.clock
         self.clock += 1
         return {
             "needed": needed,
@@ -113,6 +129,33 @@ class LruSlots:
             cw[wave] = counts[wave]
             out.append(self.step(layer, cw))
         return out
+
+    def split_hybrid(self, layer: int, counts, fetch_fraction: float, max_fetch: int = -1):
+        """(fetched misses, CPU misses) of one hybrid step, each in the order taken."""
+        counts = np.asarray(counts)
+        needed = [int(e) for e in np.nonzero(counts > 0)[0]]
+        misses = [e for e in needed if (layer, e) not in self.where]
+        order = sorted(misses, key=lambda e: (-self.last_active.get((layer, e), -1), e))
+        n_fetch = int(np.ceil(fetch_fraction * len(misses)))
+        if max_fetch >= 0:
+            n_fetch = min(n_fetch, max_fetch)
+        return order[:n_fetch], order[n_fetch:]
+
+    def step_hybrid(self, layer: int, counts, fetch_fraction: float, max_fetch: int = -1) -> dict:
+        counts = np.asarray(counts)
+        fetch, cpu = self.split_hybrid(layer, counts, fetch_fraction, max_fetch)
+        gpu_counts = counts.copy()
+        gpu_counts[cpu] = 0
+        if np.any(gpu_counts > 0):
+            waves = self.step_waves(layer, gpu_counts)
+        else:
+            waves = []
+            self.clock += 1
+        for e in cpu:
+            self.last_active[(layer, e)] = self.clock - 1
+        return {"fetch": fetch, "cpu": sorted(cpu), "waves": waves,
+                "fills": [f for r in waves for f in r["fills"]],
+                "hits": sum(r["hits"] for r in waves)}
 
     def resize(self, new_S: int) -> list:
         """New pool size; returns the (old slot, new slot) of every kept resident."""

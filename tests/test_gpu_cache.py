@@ -203,15 +203,15 @@ def test_streamed_matches_cached(fmt, groups):
 @pytest.mark.parametrize("fmt", ["fp8_b128", "mxfp4"])
 def test_streamed_waves_exceed_pool(fmt):
     """A pool smaller than one step's experts: the streamed path runs the step
-    in waves; fills follow the oracle LRU applied wave by wave, every slot holds
-    its bank record, and y is bit-identical to the all-resident run."""
+    in waves of at most S/2 (two staging sets, each wave's copies overlapping the
+    wave before); fills follow the oracle's waves, every slot holds its bank
+    record, y is bit-identical to the all-resident run and matches the oracle."""
     wl = synth.Workload("stream_waves", T=96, H=512, E=32, I=256, k=4, fmt=fmt, seed=48, zipf=1.0,
                         domains=3, batches=6)
     S = 6
     d = _pool_set(wl, S)
     ora = OL.LruSlots(S)
     side = torch.cuda.Stream()
-    resident = None
     for b in range(6):
         lg, x = _batch(wl, b)
         y_s, info = d["layer"].forward_streamed(lg, x, 0, d["cache"], d["pool_W"], d["table"],
@@ -221,15 +221,10 @@ def test_streamed_waves_exceed_pool(fmt):
         ids, _ = OR.route(synth.make_logits(wl, b), wl.k)
         counts, *_ = OP.permute(ids, wl.E)
         assert int((counts > 0).sum()) > S
-        fills = []
-        from moe_expert_ffn_router_amd.layer import plan_waves
-        waves = plan_waves(counts, S, resident)
-        for wave in waves:
-            cw = np.zeros(wl.E, dtype=np.int64)
-            cw[wave] = counts[wave]
-            fills += ora.step(0, cw)["fills"]
-            resident = ora.slot_table(0, wl.E)
-        assert info["waves"] == len(waves) and info["fills"] == fills, b
+        res = ora.step_waves(0, counts)
+        fills = [f for r in res for f in r["fills"]]
+        assert all(len(r["needed"]) <= S // 2 for r in res)     # two staging sets
+        assert info["waves"] == len(res) and info["fills"] == fills, b
         # all-resident run through the same separate calls
         lay = d["layer"]
         lay.route_permute(lg)
@@ -238,6 +233,11 @@ def test_streamed_waves_exceed_pool(fmt):
         y_r = lay.y[:wl.T].clone()
         torch.cuda.synchronize()
         assert torch.equal(y_s.view(torch.int16), y_r.view(torch.int16)), f"batch {b}"
+        if b == 0:
+            ex = OLY.ExpertSet(wl.fmt, wl.H, wl.I, lambda e: d["bank"][e].numpy())
+            toks = [0, 7, 50, wl.T - 1]
+            out = OLY.forward_tokens(synth.make_logits(wl, b), synth.make_x(wl, b), wl.k, ex, toks)
+            assert rel_err(bf16_to_np(y_s[toks]), out["y"]) <= TOL
         flush(f"   batch {b}: waves {info['waves']} hits {info['hits']} misses {info['misses']}")
     tab = d["table"].cpu().numpy()
     pool_h = d["pool"].cpu()
@@ -270,7 +270,6 @@ def test_shared_pool_layers_with_resizes():
     pool_W = moe.experts(wl.fmt, wl.E, wl.H, wl.I, pool, stride)
     ora = OL.LruSlots(S0)
     side = torch.cuda.Stream()
-    from moe_expert_ffn_router_amd.layer import plan_waves
     plan = {4: ("shrink", 9), 8: ("grow", 30), 12: ("move", 48), 16: ("shrink", 16)}
     flush(f"[pool-resize] L={L} S0={S0}")
     hits_after_resize = 0
@@ -304,11 +303,7 @@ def test_shared_pool_layers_with_resizes():
         lg, x = _batch(wl, b)
         ids, _ = OR.route(synth.make_logits(wl, b), wl.k)
         counts, *_ = OP.permute(ids, wl.E)
-        fills = []
-        for wave in plan_waves(counts, ora.S, ora.slot_table(li, wl.E)):
-            cw = np.zeros(wl.E, dtype=np.int64)
-            cw[wave] = counts[wave]
-            fills += ora.step(li, cw)["fills"]
+        fills = [f for r in ora.step_waves(li, counts) for f in r["fills"]]
         y_s, info = layer.forward_streamed(lg, x, li, cache, pool_W, table, side=side, groups=2)
         y_s = y_s.clone()
         torch.cuda.synchronize()

@@ -257,3 +257,46 @@ def test_waves_invariants(seed):
             prev = set(r["slot_of"].values())
         for e in waves[-1] if waves else []:
             assert (layer, e) in c.where
+
+
+# ---- hybrid steps (part of the misses on the CPU) -------------------------
+def test_hybrid_hand_worked_trace():
+    c = lru.LruSlots(4)
+    with open(os.path.join(GOLDEN, "lru_hybrid_trace.txt")) as f:
+        rows = [l for l in f if l.strip() and not l.startswith("#")]
+    assert len(rows) == 5
+    for line in rows:
+        needed, q, mf, fills, cpu, hits = [p.strip() for p in line.split("|")]
+        counts = np.zeros(8, np.int32)
+        counts[[int(v) for v in needed.split()]] = 3
+        r = c.step_hybrid(0, counts, float(q), int(mf))
+        exp_f = [] if fills == "-" else [tuple(int(v) for v in x.split(":")) for x in fills.split()]
+        exp_c = [] if cpu == "-" else [int(v) for v in cpu.split()]
+        assert (r["fills"], r["cpu"], r["hits"]) == (exp_f, exp_c, int(hits)), line
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_hybrid_invariants_and_extremes(seed):
+    rng = np.random.default_rng(700 + seed)
+    S, E = int(rng.integers(2, 10)), int(rng.integers(8, 30))
+    a, b, c = lru.LruSlots(S), lru.LruSlots(S), lru.LruSlots(S)
+    for t in range(50):
+        counts = ((rng.random(E) < 0.4) * rng.integers(1, 4, E)).astype(np.int32)
+        needed = set(np.nonzero(counts)[0].tolist())
+        # q = 1 with no cap is the offload step (waves included)
+        ra = a.step_hybrid(0, counts, 1.0)
+        rb = b.step_waves(0, counts)
+        assert ra["cpu"] == [] and ra["fills"] == [f for r in rb for f in r["fills"]]
+        # any q: CPU experts are misses, take no slot, fetched + cpu = misses
+        misses = {e for e in needed if (0, e) not in c.where}
+        q = float(rng.choice([0.0, 0.3, 0.5, 1.0]))
+        c0 = c.clock
+        rc = c.step_hybrid(0, counts, q, int(rng.integers(-1, 4)))
+        assert set(rc["cpu"]) | set(rc["fetch"]) == misses
+        assert not set(rc["cpu"]) & set(rc["fetch"])
+        assert all((0, e) not in c.where for e in rc["cpu"])
+        assert {e for e, _ in rc["fills"]} == set(rc["fetch"])
+        for e in needed:
+            assert c0 <= c.last_active[(0, e)] <= c.clock - 1
+        for e in rc["cpu"]:
+            assert c.last_active[(0, e)] == c.clock - 1

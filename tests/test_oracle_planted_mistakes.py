@@ -181,6 +181,19 @@ class _LruWavesNotResidentFirst(LR.LruSlots):
         return [needed[i:i + size] for i in range(0, len(needed), size)]
 
 
+class _LruHybridFetchesOldest(LR.LruSlots):
+    def split_hybrid(self, layer, counts, fetch_fraction, max_fetch=-1):
+        # fetch cap filled with the LEAST recently active misses
+        counts = np.asarray(counts)
+        needed = [int(e) for e in np.nonzero(counts > 0)[0]]
+        misses = [e for e in needed if (layer, e) not in self.where]
+        order = sorted(misses, key=lambda e: (self.last_active.get((layer, e), -1), e))
+        n = int(np.ceil(fetch_fraction * len(misses)))
+        if max_fetch >= 0:
+            n = min(n, max_fetch)
+        return order[:n], order[n:]
+
+
 CASES = [
     ("e2m1 exponent bias", F, "e2m1_value", _e2m1_wrong_bias, lambda: T_fmt.test_e2m1_published_table()),
     ("nibble order", F, "unpack_e2m1", _unpack_swapped, lambda: T_fmt.test_nibble_order_low_first()),
@@ -200,6 +213,8 @@ CASES = [
      lambda: T_lru.test_waves_hand_worked_trace()),
     ("waves not resident-first", LR, "LruSlots", _LruWavesNotResidentFirst,
      lambda: T_lru.test_waves_hand_worked_trace()),
+    ("hybrid fetches least active", LR, "LruSlots", _LruHybridFetchesOldest,
+     lambda: T_lru.test_hybrid_hand_worked_trace()),
 ]
 
 
