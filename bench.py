@@ -585,6 +585,55 @@ def bench_cached(args, wl, steps, warmup, want_cpu: bool):
         cache_w.close()
         del cache_w, pool_w, table_w
 
+    # hybrid steps (part of each step's misses on the CPU, from the bank): calibrate the
+    # host-memory and PCIe rates with the real kernels, split at the calibrated fetch
+    # fraction (q*), and time steps on a fresh pool of the same size
+    hybrid = None
+    if L == 1 and args.slots is None:
+        threads = max(1, len(os.sched_getaffinity(0)))
+        cpu_pool = moe.CpuPool(threads)
+        pool_h = torch.empty((S, stride), dtype=torch.uint8, device=dev)
+        bank_W = moe.experts(wl.fmt, E, wl.H, wl.I, bank.data_ptr(), stride)
+        prof = moe.moe_bench_bw(cpu_pool, bank_W, pool_h, 16, 2.0, stream=side)
+        table_h = torch.full((E,), -1, dtype=torch.int32, device=dev)
+        cache_h = moe.ExpertCache(1, E, S, stride, pool_h, bank, table_h)
+        pool_Wh = moe.experts(wl.fmt, E, wl.H, wl.I, pool_h, stride)
+        q = float(prof["fetch_fraction"])
+        n_h = 4
+        for i in range(2):   # fill the pool, as the offload run did in its warm-up
+            layer.forward_hybrid(logits[0][i % nb], xs[i % nb], 0, cache_h, pool_Wh, table_h,
+                                 cpu_pool, q, side=side, groups=args.fill_groups or 1)
+        torch.cuda.synchronize()
+        h0, h1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n_cpu, n_fetch = [], []
+        t_h = time.time()
+        h0.record()
+        for i in range(n_h):
+            _, info = layer.forward_hybrid(logits[0][(2 + i) % nb], xs[(2 + i) % nb], 0, cache_h,
+                                           pool_Wh, table_h, cpu_pool, q, side=side,
+                                           groups=args.fill_groups or 1)
+            n_cpu.append(len(info["cpu"]))
+            n_fetch.append(info["fetched"])
+        h1.record()
+        torch.cuda.synchronize()
+        hybrid = {"calibration": {"h2d_gbs": round(prof["h2d_bytes_per_s"] / 1e9, 2),
+                                  "cpu_gbs": round(prof["cpu_bytes_per_s"] / 1e9, 2),
+                                  "cpu_threads": threads, "threshold": prof["threshold"],
+                                  "hybrid_recommended": bool(prof["hybrid_recommended"]),
+                                  "fetch_fraction_q": round(q, 4)},
+                  "steps": n_h, "ms_per_step": round(h0.elapsed_time(h1) / n_h, 3),
+                  "wall_ms_per_step": round((time.time() - t_h) * 1e3 / n_h, 3),
+                  "cpu_experts_per_step": round(float(np.mean(n_cpu)), 1),
+                  "fetched_per_step": round(float(np.mean(n_fetch)), 1),
+                  "tokens_per_s": round(wl.T * n_h / (h0.elapsed_time(h1) / 1e3), 1),
+                  "offload_ms_per_step": round(total_ms / steps, 3),
+                  "note": ("auto would " + ("choose hybrid" if prof["hybrid_recommended"]
+                                            else "stay on offload") +
+                           " (CPU rate vs threshold x PCIe rate); timed at the calibrated split")}
+        cache_h.close()
+        cpu_pool.close()
+        del cache_h, pool_h, table_h
+
     # elastic resize of the live pool (in place): halve it, keeping the most recently
     # used residents, then grow back; wall time of each host-synchronous call
     t_r = time.time()
@@ -686,6 +735,7 @@ def bench_cached(args, wl, steps, warmup, want_cpu: bool):
                                 "to_%d" % S: round(grow_ms, 2)},
                   "slot_sweep": sweep},
         "waves": wave_case,
+        "hybrid": hybrid,
         "roofline": roof,
     }
     if want_cpu:

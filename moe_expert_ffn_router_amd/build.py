@@ -40,9 +40,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, src.replace("/", "_") + ".o")
-    cmd = [hipcc()] + COMMON + ["-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, obj_dir: str = OBJ, extra: tuple = ()) -> str:
+    obj = os.path.join(obj_dir, src.replace("/", "_") + ".o")
+    cmd = [hipcc()] + COMMON + list(extra) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -76,5 +76,37 @@ def build(verbose: bool = False) -> str:
     return OUT
 
 
+# Host-sanitizer build: the same sources with AddressSanitizer and
+# UndefinedBehaviorSanitizer on the host side only (device code unchanged), as
+# a separate library; the CPU tests load it through MOE_LIB_PATH with the ASan
+# runtime preloaded.
+ASAN_OUT = os.path.join(ROOT, "_build", "asan", "libmoe_mi355x_asan.so")
+ASAN_FLAGS = ("-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+              "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host",
+              "-fno-omit-frame-pointer", "-g")
+
+
+def asan_runtime() -> str:
+    import glob
+    c = sorted(glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not c:
+        raise RuntimeError("ASan runtime not found")
+    return c[-1]
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    obj_dir = os.path.join(ROOT, "_build", "asan")
+    os.makedirs(obj_dir, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
+        objs = list(ex.map(lambda src: _compile(src, obj_dir, ASAN_FLAGS), SOURCES))
+    _link(objs, ASAN_OUT, ["-fsanitize=address", "-fsanitize=undefined", "-shared-libsan"])
+    if verbose:
+        print(f"[build] wrote {ASAN_OUT}")
+    return ASAN_OUT
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if "asan" in sys.argv[1:]:
+        build_host_sanitized(verbose=True)
+    else:
+        build(verbose=True)

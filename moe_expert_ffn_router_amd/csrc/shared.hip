@@ -33,17 +33,27 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kSgBM = 256;     // output rows per workgroup
 constexpr int kSgBN = 256;     // weight rows per workgroup
 #ifndef MOE_SG_BK
-#define MOE_SG_BK 32
+#define MOE_SG_BK 64
 #endif
 #ifndef MOE_SG_STAGES
-#define MOE_SG_STAGES 4
+#define MOE_SG_STAGES 2
 #endif
 constexpr int kSgBK = MOE_SG_BK;          // K per stage (32: 64-byte rows, 64: 128-byte rows)
 constexpr int kSgStages = MOE_SG_STAGES;  // kSgStages * (kSgBM + kSgBN) * kSgBK * 2 <= 160 KB
 constexpr int kSgRowB = kSgBK * 2;        // bytes of one row of a stage
 constexpr int kSgUnits = kSgRowB / 16;    // 16-byte units per row
-constexpr int kSgCopies = kSgBM * kSgRowB / 1024 / 4;  // 1 KB copies of A (and of B) per wave
+#ifndef MOE_SG_WAVES
+#define MOE_SG_WAVES 8
+#endif
+#ifndef MOE_SG_SCHED
+#define MOE_SG_SCHED 1
+#endif
+constexpr int kSgWaves = MOE_SG_WAVES;     // 4: one wave per SIMD; 8: two
+constexpr int kSgWN = kSgWaves / 2;        // waves along the weight rows (2 along M)
+constexpr int kSgNJ = kSgBN / kSgWN / 32;  // 32-column blocks per wave (4 or 2)
+constexpr int kSgCopies = kSgBM * kSgRowB / 1024 / kSgWaves;  // 1 KB copies of A (and of B) per wave
 static_assert(kSgStages * (kSgBM + kSgBN) * kSgRowB <= 160 * 1024, "LDS");
+static_assert(kSgStages >= 2 && kSgStages <= 5, "waits are written for 2..5 stages");
 
 // unit swizzle of a stage row (64-byte rows: b_swz, 128-byte rows: a_swz)
 __device__ __forceinline__ int sg_swz(int r) { return kSgUnits == 4 ? b_swz(r) : a_swz(r); }
@@ -68,7 +78,7 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ void pin_acc(f32x16& acc) { asm volatile("" : "+a"(acc)); }
 
 template <bool GATED>
-__global__ __launch_bounds__(256, 1) void shared_gemm_kernel(SgArgs p) {
+__global__ __launch_bounds__(64 * kSgWaves) void shared_gemm_kernel(SgArgs p) {
   __shared__ SgStage st[kSgStages];
   // block -> (XCD-contiguous index) -> rectangle -> tile
   const int G = (int)gridDim.x, b = (int)blockIdx.x;
@@ -81,7 +91,7 @@ __global__ __launch_bounds__(256, 1) void shared_gemm_kernel(SgArgs p) {
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int mh = wave >> 1, nh = wave & 1;
+  const int mh = wave / kSgWN, nh = wave % kSgWN;
   const int K = p.K, nch = K / kSgBK;
   const int m0 = tmi * kSgBM;
 
@@ -99,10 +109,10 @@ __global__ __launch_bounds__(256, 1) void shared_gemm_kernel(SgArgs p) {
     ao[q] = (uint32_t)ar * (uint32_t)(K * 2) + unit;
     int wr;
     if constexpr (GATED) {
-      // per wave half: 64 gate rows, then the matching 64 up rows
-      const int half = lr >> 7, j = (lr >> 5) & 3, l = lr & 31;
-      const int col = tni * 128 + half * 64 + (j & 1) * 32 + l;
-      wr = j < 2 ? col : p.I + col;
+      // per wave column group: 16*NJ gate rows, then the matching 16*NJ up rows
+      const int grp = lr / (32 * kSgNJ), j = (lr >> 5) % kSgNJ, l = lr & 31;
+      const int col = tni * 128 + grp * (16 * kSgNJ) + (j % (kSgNJ / 2)) * 32 + l;
+      wr = j < kSgNJ / 2 ? col : p.I + col;
     } else {
       const int rows_left = p.N - 1 - tni * kSgBN;
       wr = lr < rows_left ? lr : rows_left;
@@ -119,40 +129,53 @@ __global__ __launch_bounds__(256, 1) void shared_gemm_kernel(SgArgs p) {
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][kSgNJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kSgNJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // fragments of K step s (16 K: unit 2s + hh of each row)
+  auto load_frags = [&](const SgStage& S, int s, bf16x8 (&af)[4], bf16x8 (&bfr)[kSgNJ]) {
+    const int u = 2 * s + hh;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = mh * 128 + i * 32 + l32;
+      af[i] = *reinterpret_cast<const bf16x8*>(S.a + r * kSgRowB + ((u ^ sg_swz(r)) * 16));
+    }
+#pragma unroll
+    for (int j = 0; j < kSgNJ; ++j) {
+      const int r = nh * (32 * kSgNJ) + j * 32 + l32;
+      bfr[j] = *reinterpret_cast<const bf16x8*>(S.b + r * kSgRowB + ((u ^ sg_swz(r)) * 16));
+    }
+  };
+  // Per K step: the next step's fragments are read while this step's MFMAs
+  // issue (one LDS read between consecutive MFMAs), so the LDS latency hides
+  // behind MFMA work instead of stalling before each group.
   auto compute = [&](const SgStage& S) {
+    constexpr int NSTEP = kSgBK / 16;
+    bf16x8 af[2][4], bfr[2][kSgNJ];
+    load_frags(S, 0, af[0], bfr[0]);
 #pragma unroll
-    for (int s = 0; s < kSgBK / 16; ++s) {
-      const int u = 2 * s + hh;
-      bf16x8 af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = mh * 128 + i * 32 + l32;
-        af[i] = *reinterpret_cast<const bf16x8*>(S.a + r * kSgRowB + ((u ^ sg_swz(r)) * 16));
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = nh * 128 + j * 32 + l32;
-        bfr[j] = *reinterpret_cast<const bf16x8*>(S.b + r * kSgRowB + ((u ^ sg_swz(r)) * 16));
-      }
+    for (int s = 0; s < NSTEP; ++s) {
+      if (s + 1 < NSTEP) load_frags(S, s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
+#if MOE_SG_SCHED
+      __builtin_amdgcn_sched_barrier(0);  // the reads stay ahead of this step's MFMAs
+#endif
       // weights as the MFMA's first operand: the result's rows are output columns,
       // so each lane ends with 4 consecutive columns of one row per value group
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[i][j] = mfma32(bfr[j], af[i], acc[i][j]);
-          pin_acc(acc[i][j]);
-        }
+        for (int j = 0; j < kSgNJ; ++j) acc[i][j] = mfma32(bfr[s & 1][j], af[s & 1][i], acc[i][j]);
+#if MOE_SG_SCHED
+      __builtin_amdgcn_sched_barrier(0);
+#endif
     }
   };
+
 
   // prologue: chunks 0..2 in flight
 #pragma unroll
@@ -161,17 +184,12 @@ __global__ __launch_bounds__(256, 1) void shared_gemm_kernel(SgArgs p) {
   for (int c = 0; c < nch; ++c) {
     // chunk c's copies done (the later in-flight chunks may still be pending),
     // every wave's reads of chunk c-1 done
-    const int ahead = nch - 1 - c;
-    if constexpr (kSgStages >= 4) {
-      if (ahead >= 2) MOE_DMA_SYNC(4 * kSgCopies);
-      else if (ahead == 1) MOE_DMA_SYNC(2 * kSgCopies);
-      else MOE_DMA_SYNC(0);
-    } else if constexpr (kSgStages == 3) {
-      if (ahead >= 1) MOE_DMA_SYNC(2 * kSgCopies);
-      else MOE_DMA_SYNC(0);
-    } else {
-      MOE_DMA_SYNC(0);
-    }
+    // chunks issued after chunk c that may still be in flight: min(stages - 2, nch - 1 - c)
+    const int ahead = nch - 1 - c < kSgStages - 2 ? nch - 1 - c : kSgStages - 2;
+    if (ahead >= 3) MOE_DMA_SYNC(6 * kSgCopies);
+    else if (ahead == 2) MOE_DMA_SYNC(4 * kSgCopies);
+    else if (ahead == 1) MOE_DMA_SYNC(2 * kSgCopies);
+    else MOE_DMA_SYNC(0);
     if (c + kSgStages - 1 < nch) issue(c + kSgStages - 1, st[(c + kSgStages - 1) % kSgStages]);
     compute(st[c % kSgStages]);
   }
@@ -180,20 +198,20 @@ __global__ __launch_bounds__(256, 1) void shared_gemm_kernel(SgArgs p) {
   // of the wave's 128 weight rows, so values 4q..4q+3 are 4 consecutive columns
   const int row_l = m0 + mh * 128 + l32;
   if constexpr (GATED) {
-    const int col0 = tni * 128 + nh * 64 + 4 * hh;
+    const int col0 = tni * 128 + nh * (16 * kSgNJ) + 4 * hh;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = row_l + i * 32;
       if (row >= p.M) continue;
       uint16_t* dst = p.out + (size_t)row * p.I + col0;
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
+      for (int jj = 0; jj < kSgNJ / 2; ++jj)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           uint16_t hv[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float g = acc[i][jj][4 * q + r], uv = acc[i][jj + 2][4 * q + r];
+            const float g = acc[i][jj][4 * q + r], uv = acc[i][jj + kSgNJ / 2][4 * q + r];
             hv[r] = f32_to_bf16_rne(g / (1.0f + expf(-g)) * uv);
           }
           *reinterpret_cast<uint2*>(dst + jj * 32 + 8 * q) =
@@ -201,14 +219,14 @@ __global__ __launch_bounds__(256, 1) void shared_gemm_kernel(SgArgs p) {
         }
     }
   } else {
-    const int col0 = tni * kSgBN + nh * 128 + 4 * hh;
+    const int col0 = tni * kSgBN + nh * (32 * kSgNJ) + 4 * hh;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = row_l + i * 32;
       if (row >= p.M) continue;
       uint16_t* dst = p.out + (size_t)row * p.N + col0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < kSgNJ; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int col = col0 + j * 32 + 8 * q;  // the 4 columns lie on one side of N (N % 128 == 0)
@@ -239,7 +257,7 @@ int launch_gemm(SgArgs p, hipStream_t s, const char* what) {
   const int64_t blocks = (int64_t)nrm * p.nrn * p.rm * p.rn;
   const int64_t grid = (blocks + 7) / 8 * 8;
   if (grid > (int64_t)1 << 30) return set_error(MOE_ERR_UNSUPPORTED, "%s: too many tiles", what);
-  shared_gemm_kernel<GATED><<<(unsigned)grid, 256, 0, s>>>(p);
+  shared_gemm_kernel<GATED><<<(unsigned)grid, 64 * kSgWaves, 0, s>>>(p);
   return check_launch(what);
 }
 

@@ -15,7 +15,7 @@ import numpy as np
 import torch
 
 from . import (Experts, experts, moe_combine, moe_expert_ffn, moe_expert_ffn_workspace,
-               moe_expert_ffn_streamed_workspace,
+               moe_expert_ffn_hybrid_host_bytes, moe_expert_ffn_streamed_workspace,
                moe_forward_decode, moe_forward_decode_supported, moe_forward_decode_workspace,
                moe_shared_ffn, moe_shared_ffn_workspace,
                moe_permute, moe_permute_workspace, moe_route, moe_route_permute)
@@ -51,6 +51,8 @@ class MoELayer:
         self.stream_ws = None                 # streamed cache path: made on first use
         self.counts_host = torch.zeros(E, dtype=torch.int32).pin_memory()
         self.plan_out = tuple(torch.zeros(E, dtype=torch.int32) for _ in range(3))
+        self.hybrid_out = tuple(torch.zeros(E, dtype=torch.int32) for _ in range(4))
+        self.host_stage = None                # hybrid path: pinned staging, made on first use
         self.y_perm = torch.empty((max(A, 1), H), dtype=torch.bfloat16, device=dev)
         self.y = torch.empty((max(T_max, 1), H), dtype=torch.bfloat16, device=dev)
         self.shared_I = shared_I
@@ -161,3 +163,37 @@ class MoELayer:
         fills = list(zip(fe[:n_fill].tolist(), fs[:n_fill].tolist()))
         self.combine(T, False, cs)
         return self.y[:T], {"misses": n_fill, "hits": nh, "waves": nw, "fills": fills}
+
+    def forward_hybrid(self, logits: torch.Tensor, x: torch.Tensor, layer: int, cache, pool_W: Experts,
+                       slot_table: torch.Tensor, cpu_pool, fetch_fraction: float,
+                       max_fetch: int = -1, side=None, groups: int = 4,
+                       stream=None) -> tuple[torch.Tensor, dict]:
+        """Hybrid step (moe_expert_ffn_hybrid): ceil(fetch_fraction * misses) of the misses
+        (the most recently active) are fetched and computed on the GPU behind their copies,
+        the others computed on the CPU from the bank while the GPU runs; then combine."""
+        T = logits.shape[0]
+        E = self.E
+        cs = stream if stream is not None else torch.cuda.current_stream()
+        if self.stream_ws is None:
+            self.stream_ws = torch.empty(
+                max(moe_expert_ffn_streamed_workspace(self._probe, self.T_max, self.k), 256),
+                dtype=torch.uint8, device=self.device)
+        if self.host_stage is None:
+            self.host_stage = torch.empty(
+                moe_expert_ffn_hybrid_host_bytes(self._probe, self.T_max, self.k),
+                dtype=torch.uint8).pin_memory()
+        self.route_permute(logits, cs)
+        with torch.cuda.stream(cs):
+            self.counts_host.copy_(self.counts[:E], non_blocking=True)
+        cs.synchronize()                                 # the one host sync of the step
+        nc, nw, nh = cache.moe_expert_ffn_hybrid(layer, pool_W, cpu_pool, x, T, self.k,
+                                                 self.counts_host, self.offsets, self.sorted_idx,
+                                                 self.y_perm, fetch_fraction, max_fetch, groups,
+                                                 self.stream_ws, self.host_stage, side=side,
+                                                 compute=cs, out=self.hybrid_out)
+        ce, fe, fs, we = self.hybrid_out
+        n_fill = int(we[nw - 1]) if nw else 0
+        fills = list(zip(fe[:n_fill].tolist(), fs[:n_fill].tolist()))
+        self.combine(T, False, cs)
+        return self.y[:T], {"misses": n_fill + nc, "fetched": n_fill, "cpu": ce[:nc].tolist(),
+                            "hits": nh, "waves": nw, "fills": fills}

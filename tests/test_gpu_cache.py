@@ -344,3 +344,79 @@ def test_fill_groups_argument_checks():
     for i, e in enumerate(me.tolist()):
         assert torch.equal(d["pool"][ms[i]].cpu(), d["bank"][e])
     cache.close()
+
+
+# ---------------------------------------------------------------------------
+# hybrid: part of each step's misses computed on the CPU
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("fmt,q,max_fetch,S", [("mxfp4", 0.5, -1, 10), ("nvfp4", 0.3, 2, 12),
+                                               ("fp8_b128", 0.0, -1, 8), ("bf16", 0.6, -1, 6)])
+def test_hybrid_matches_oracle(fmt, q, max_fetch, S):
+    """Hybrid steps: the CPU experts and the fills follow the oracle's hybrid policy (the
+    most recently active misses fetched, the rest on the CPU, waves when the GPU share
+    exceeds the pool); GPU experts' y_perm rows are bit-identical to the all-resident
+    run's, the CPU experts' rows and y match the oracle within tolerance."""
+    wl = synth.Workload("hybrid", T=64, H=512, E=24, I=256, k=4, fmt=fmt, seed=52, zipf=1.0,
+                        domains=3, batches=6)
+    flush(f"[hybrid] {fmt} q={q} max_fetch={max_fetch} S={S}")
+    d = _pool_set(wl, S)
+    ora = OL.LruSlots(S)
+    cpu_pool = moe.CpuPool(4)
+    side = torch.cuda.Stream()
+    lay = d["layer"]
+    ref_layer = moe.MoELayer(wl.fmt, wl.E, wl.H, wl.I, wl.k, wl.T, d["stride"])
+    n_cpu_total = 0
+    for b in range(6):
+        lg, x = _batch(wl, b)
+        y_h, info = lay.forward_hybrid(lg, x, 0, d["cache"], d["pool_W"], d["table"], cpu_pool,
+                                       q, max_fetch, side=side, groups=2)
+        y_h = y_h.clone()
+        yp = lay.y_perm[:wl.T * wl.k].clone()
+        torch.cuda.synchronize()
+        ids, w = OR.route(synth.make_logits(wl, b), wl.k)
+        counts, offsets, sidx, inv = OP.permute(ids, wl.E)
+        r = ora.step_hybrid(0, counts, q, max_fetch)
+        assert info["cpu"] == r["cpu"] and info["fills"] == r["fills"], b
+        assert info["hits"] == r["hits"]
+        n_cpu_total += len(r["cpu"])
+        # all-resident run: GPU experts' rows bit-identical
+        ref_layer.route_permute(lg)
+        ref_layer.expert_ffn(ref_layer.weights(d["dev"]), x, wl.T)
+        ref_yp = ref_layer.y_perm[:wl.T * wl.k].clone()
+        torch.cuda.synchronize()
+        cpu_rows = np.zeros(wl.T * wl.k, bool)
+        for e in r["cpu"]:
+            cpu_rows[offsets[e]:offsets[e + 1]] = True
+        g = torch.from_numpy(~cpu_rows).to(DEV)
+        assert torch.equal(yp[g].view(torch.int16), ref_yp[g].view(torch.int16)), b
+        # the CPU rows and the output against the oracle
+        ex = OLY.ExpertSet(wl.fmt, wl.H, wl.I, lambda e: d["bank"][e].numpy())
+        ref = OLY.forward(synth.make_logits(wl, b), synth.make_x(wl, b), wl.k, ex)
+        if cpu_rows.any():
+            assert rel_err(bf16_to_np(yp)[cpu_rows], ref["y_perm"][cpu_rows]) <= TOL
+        assert rel_err(bf16_to_np(y_h), ref["y"]) <= TOL
+        flush(f"   batch {b}: cpu {len(r['cpu'])} fetched {len(r['fetch'])} hits {r['hits']}")
+    assert n_cpu_total > 0 or q == 1.0
+    tab = d["table"].cpu().numpy()
+    pool_h = d["pool"].cpu()
+    for (L, e), s in ora.where.items():
+        assert tab[e] == s and torch.equal(pool_h[s], d["bank"][e]), (e, s)
+    cpu_pool.close()
+    d["cache"].close()
+
+
+def test_bench_bw_profile():
+    """moe_bench_bw: both rates positive, the recommendation follows the threshold, and
+    the fetch fraction is h2d / (h2d + cpu)."""
+    wl = synth.Workload("bw", T=8, H=2048, E=16, I=512, k=8, fmt="mxfp4", seed=53)
+    d = _pool_set(wl, 8)
+    pool = moe.CpuPool(4)
+    bank_W = moe.experts(wl.fmt, wl.E, wl.H, wl.I, d["bank"].data_ptr(), d["stride"])
+    p = moe.moe_bench_bw(pool, bank_W, d["pool"], 8, 2.0)
+    assert p["h2d_bytes_per_s"] > 0 and p["cpu_bytes_per_s"] > 0
+    assert p["hybrid_recommended"] == int(p["cpu_bytes_per_s"] >= 2.0 * p["h2d_bytes_per_s"])
+    assert abs(p["fetch_fraction"] - p["h2d_bytes_per_s"] /
+               (p["h2d_bytes_per_s"] + p["cpu_bytes_per_s"])) < 1e-12
+    flush(f"   h2d {p['h2d_bytes_per_s'] / 1e9:.1f} GB/s, cpu {p['cpu_bytes_per_s'] / 1e9:.1f} GB/s")
+    pool.close()
+    d["cache"].close()
