@@ -438,13 +438,31 @@ __global__ __launch_bounds__(256) void ffn_down_tile_kernel(FfnArgs a) {
 // chunk stays raw in registers (two named buffers used alternately, so no
 // register holding a pending load is copied).  While chunk c is computed the
 // loads of chunk c+1 are in flight; one barrier per chunk.  K/128 must be
-// even (the last prefetch re-reads the last chunk).  Blocks are numbered so
-// that consecutive logical blocks land on one XCD (hardware block b runs on
-// XCD b % 8), and logical blocks walk super-tiles of 8 m-tiles column block
-// by column block: the blocks an XCD runs at a time share the A rows of a few
-// m-tiles and the weights of a few column blocks in its L2.
+// even (the last prefetch re-reads the last chunk).  Blocks walk super-tiles
+// of 8 m-tiles column block by column block, each super-tile on one XCD
+// (tile_of_block).
 // ----------------------------------------------------------------------------
 constexpr int kSuperM = 8;  // m-tiles per super-tile (prefill block order)
+
+// Block b -> (m-tile, column block) for the prefill grids.  The grid holds
+// whole super-tiles (SM m-tiles x nnb column blocks, walked column block by
+// column block, so that the blocks an XCD runs at a time share the A rows of
+// a few m-tiles and the weights of a few column blocks in its L2), a multiple
+// of 8 of them.  Hardware block b runs on XCD b % 8, and super-tile s is
+// served by XCD s % 8: the grid is sized from an upper bound on the m-tiles,
+// the ones that hold rows come first, and this keeps them spread over all
+// eight XCDs (a contiguous range of super-tiles per XCD would leave most
+// XCDs with only empty tiles when the bound is loose).
+template <int SM>
+__device__ __forceinline__ void tile_of_block(int b, int nnb, int& tile, int& nb) {
+  const int S = SM * nnb;                  // blocks per super-tile
+  const int x = b & 7, j = b >> 3;         // XCD, index among that XCD's blocks
+  const int sl = j / S, gi = j - sl * S;   // super-tile of this XCD, block inside it
+  tile = (sl * 8 + x) * SM + gi % SM;
+  nb = gi / SM;
+}
+// m-tiles of a grid: the bound rounded up to whole groups of 8 super-tiles
+static int64_t grid_m_tiles(int64_t bound) { return (bound + 8 * kSuperM - 1) / (8 * kSuperM) * (8 * kSuperM); }
 
 template <int FMT, bool GATED, int MSUB, int MH>
 __device__ __forceinline__ void ffn_pipe_body(const FfnArgs& a) {
@@ -454,12 +472,11 @@ __device__ __forceinline__ void ffn_pipe_body(const FfnArgs& a) {
   const int N_out = GATED ? a.I : a.H;
   const int K = GATED ? a.H : a.I, nch = K / KC;
   const int nnb = N_out / NCOLB;
-  const int G = (int)gridDim.x, b = (int)blockIdx.x;
-  const int lid = (b & 7) * (G >> 3) + (b >> 3);  // G is a multiple of 8
+  const int b = (int)blockIdx.x;
   // super-tiles of kSuperM m-tiles, walked column block by column block (as
   // in the block-scaled kernels)
-  const int grp = lid / (kSuperM * nnb), gi = lid - grp * (kSuperM * nnb);
-  const int tile = grp * kSuperM + gi % kSuperM, nb = gi / kSuperM;
+  int tile, nb;
+  tile_of_block<kSuperM>(b, nnb, tile, nb);
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const int wave = (tid >> 6) & 3, mh = tid >> 8;  // column quarter, row group
 
@@ -688,13 +705,12 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
   const int N_out = GATED ? a.I : a.H;
   const int K = GATED ? a.H : a.I, nch = K / KC;
   const int nnb = N_out / NCOLB;
-  const int G = (int)gridDim.x, b = (int)blockIdx.x;
-  const int lid = (b & 7) * (G >> 3) + (b >> 3);  // G is a multiple of 8
+  const int b = (int)blockIdx.x;
   // super-tiles of kSuperM m-tiles x all column blocks, walked column block
   // by column block: the blocks one XCD runs at a time share both the A rows
   // of a few m-tiles and the weights of a few column blocks in its L2
-  const int grp = lid / (kSuperM * nnb), gi = lid - grp * (kSuperM * nnb);
-  const int tile = grp * kSuperM + gi % kSuperM, nb = gi / kSuperM;
+  int tile, nb;
+  tile_of_block<kSuperM>(b, nnb, tile, nb);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
 
   __shared__ __attribute__((aligned(16))) uint8_t Sh[2][BM * QP];
@@ -818,7 +834,9 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
   };
   // one m-subtile's A fragments at a time (hi, lo: 16 registers), the next
   // subtile's read from LDS while these are used, against the chunk's 4 raw
-  // B subtiles; accumulators pinned after each step
+  // B subtiles; accumulators pinned after each step.  Row subtiles past the
+  // tile's rows are skipped.
+  const int nact = min(MSUB, (rows + 15) >> 4);
   auto compute = [&](int buf, const QRaw<FMT> (&r)[NSUB]) {
     auto frag = [&](int i, i32x8& h, i32x8& l, int& sa) {
       const int o = (i * 16 + l16) * QP + g * 32;
@@ -842,9 +860,10 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
     }
 #pragma unroll
     for (int i = 0; i < MSUB; ++i) {
+      if (i >= nact) break;
       i32x8 nh, nl;
       int ns = 0;
-      if (i + 1 < MSUB) frag(i + 1, nh, nl, ns);
+      if (i + 1 < nact) frag(i + 1, nh, nl, ns);
 #pragma unroll
       for (int j = 0; j < NSUB; ++j) {
         if constexpr (FMT == MOE_W_MXFP4) {
@@ -864,7 +883,7 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
           pin(acc[i][j]);  // the block-scale FMA reads it as a VALU operand
         }
       }
-      if (i + 1 < MSUB) {
+      if (i + 1 < nact) {
         ah = nh;
         al = nl;
         sa = ns;
@@ -937,13 +956,13 @@ __global__ __launch_bounds__(256) void ffn_down_mx_kernel(FfnArgs a) {
 // 8 waves (2 row halves x 4 column quarters, 64 x 64 outputs per wave).
 // Every operand byte goes from global memory straight into LDS
 // (global_load_lds_dwordx4: lane l of one instruction writes 16 bytes at
-// base + 16 l), three K chunks deep, so no registers hold loads in flight.
+// base + 16 l), two K chunks deep, so no registers hold loads in flight.
 // Waits are explicit: at chunk c a wave waits for its own copies of chunk c
 // (vmcnt) and for its LDS reads of chunk c-1 (lgkmcnt), then one barrier
-// makes all copies visible and frees chunk c-1's stage for chunk c+2.
+// makes all copies visible and frees chunk c-1's stage for chunk c+1.
 // ---------------------------------------------------------------------------
 // m-tiles per super-tile (8, 16, 32 and 64 measured within 4 %; 8 best)
-constexpr int kDmaSuperM = 8;
+constexpr int kDmaSuperM = kSuperM;
 template <int BM, int BN>
 struct MxDmaStage {
   uint8_t ah[BM * 128];  // A hi [row][128 B]: 16-byte unit u stored at u ^ a_swz(row)
@@ -972,10 +991,9 @@ __device__ __forceinline__ void ffn_mx_dma_body(const FfnArgs& a, MxDmaStage<MB 
   const int N_out = GATED ? a.I : a.H;
   const int K = GATED ? a.H : a.I, nch = K / KC, KS = K / 32;
   const int nnb = N_out / NCOLB;
-  const int G = (int)gridDim.x, b = (int)blockIdx.x;
-  const int lid = (b & 7) * (G >> 3) + (b >> 3);  // G is a multiple of 8
-  const int grp = lid / (kDmaSuperM * nnb), gi = lid - grp * (kDmaSuperM * nnb);
-  const int tile = grp * kDmaSuperM + gi % kDmaSuperM, nb = gi / kDmaSuperM;
+  const int b = (int)blockIdx.x;
+  int tile, nb;
+  tile_of_block<kDmaSuperM>(b, nnb, tile, nb);
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int mh = wave / WN, nw = wave % WN;
@@ -1062,8 +1080,11 @@ __device__ __forceinline__ void ffn_mx_dma_body(const FfnArgs& a, MxDmaStage<MB 
     for (int j = 0; j < NSUB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // the wave's weight subtiles, then its 4 row subtiles (the next one's A
-  // fragments read while the current one's MFMAs run)
+  // fragments read while the current one's MFMAs run); row subtiles past the
+  // tile's rows are skipped (a wave whose half holds none skips the chunk)
+  const int nact = min(MSUB, max(0, (rows - mh * 64 + 15) >> 4));
   auto compute = [&](const MxDmaStage<BM, BN>& S) {
+    if (nact == 0) return;
     i32x4 bq[NSUB];
     int sb[NSUB];
 #pragma unroll
@@ -1097,16 +1118,17 @@ __device__ __forceinline__ void ffn_mx_dma_body(const FfnArgs& a, MxDmaStage<MB 
     frag(0, ah, al, sa);
 #pragma unroll
     for (int i = 0; i < MSUB; ++i) {
+      if (i >= nact) break;
       i32x8 nh, nl;
       int ns = 0;
-      if (i + 1 < MSUB) frag(i + 1, nh, nl, ns);
+      if (i + 1 < nact) frag(i + 1, nh, nl, ns);
 #pragma unroll
       for (int j = 0; j < NSUB; ++j) {
         acc[i][j] = mfma_mx(ah, bq[j], sa, sb[j], acc[i][j]);
         acc[i][j] = mfma_mx(al, bq[j], sa, sb[j], acc[i][j]);
         if constexpr (NSUB > 4) pin_a(acc[i][j]);  // accumulators in AGPRs
       }
-      if (i + 1 < MSUB) {
+      if (i + 1 < nact) {
         ah = nh;
         al = nl;
         sa = ns;
@@ -1222,10 +1244,9 @@ __device__ __forceinline__ void ffn_nv_dma_body(const FfnArgs& a, NvDmaStage<MB 
   const int N_out = GATED ? a.I : a.H;
   const int K = GATED ? a.H : a.I, nch = K / KC;
   const int nnb = N_out / NCOLB;
-  const int G = (int)gridDim.x, b = (int)blockIdx.x;
-  const int lid = (b & 7) * (G >> 3) + (b >> 3);  // G is a multiple of 8
-  const int grp = lid / (kDmaSuperM * nnb), gi = lid - grp * (kDmaSuperM * nnb);
-  const int tile = grp * kDmaSuperM + gi % kDmaSuperM, nb = gi / kDmaSuperM;
+  const int b = (int)blockIdx.x;
+  int tile, nb;
+  tile_of_block<kDmaSuperM>(b, nnb, tile, nb);
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int mh = wave / NWG, nw = wave % NWG;
@@ -1480,7 +1501,7 @@ static void fill_args(FfnArgs& a, const moe_experts* W, const Layout& L) {
 template <int MSUB, int MH, typename K1, typename K2>
 static void launch_pipe(const FfnArgs& a, K1 k1, K2 k2, hipStream_t s) {
   // whole super-tiles: the grid is then a multiple of 8 as well
-  const int64_t mt = (max_tiles_for(a.A, a.E, MSUB * 16 * MH) + kSuperM - 1) / kSuperM * kSuperM;
+  const int64_t mt = grid_m_tiles(max_tiles_for(a.A, a.E, MSUB * 16 * MH));
   k1<<<(unsigned)(mt * (a.I / 128)), 256 * MH, 0, s>>>(a);
   k2<<<(unsigned)(mt * (a.H / 256)), 256 * MH, 0, s>>>(a);
 }
@@ -1531,18 +1552,18 @@ static void launch_ffn(const FfnArgs& a, bool decode, hipStream_t s) {
       d.aq_hi = ws + L.hq_hi; d.aq_lo = ws + L.hq_lo; d.aq_sc = ws + L.hq_sc;
       quant_rows_kernel<<<(unsigned)((T + 7) / 8), 256, 0, s>>>(
           a.x, T, a.H, ws + L.xq_hi, ws + L.xq_lo, ws + L.xq_sc);
-      // (FP8 on these kernels, 256 rows per block, measured 2.00 ms against
-      // 1.50 ms on the 64-row kernels for its skewed 2048-token batch)
+      // (FP8 on a 128 x 256 copy-pipeline tile measured 0.91 ms against 0.86 ms on
+      // these 64-row kernels for its skewed 2048-token batch: LDS-bound)
       if (FMT == MOE_W_MXFP4 && a.I % (kDmaBN / 2) == 0 && a.H % kDmaBN == 0) {
         // 128-row tiles on the LDS-DMA pipeline
         const int64_t mt =
-            (max_tiles_for(a.A, a.E, kDmaBM) + kDmaSuperM - 1) / kDmaSuperM * kDmaSuperM;
+            grid_m_tiles(max_tiles_for(a.A, a.E, kDmaBM));
         ffn_gateup_mxd_kernel<<<(unsigned)(mt * (a.I / (kDmaBN / 2))), kDmaWaves * 64, 0, s>>>(g);
         quant_rows_kernel<<<(unsigned)((a.A + 7) / 8), 256, 0, s>>>(
             a.hbuf, a.A, a.I, ws + L.hq_hi, ws + L.hq_lo, ws + L.hq_sc);
         ffn_down_mxd_kernel<<<(unsigned)(mt * (a.H / kDmaBN)), kDmaWaves * 64, 0, s>>>(d);
       } else {
-        const int64_t mt = (max_tiles_for(a.A, a.E, 64) + kSuperM - 1) / kSuperM * kSuperM;
+        const int64_t mt = grid_m_tiles(max_tiles_for(a.A, a.E, 64));
         ffn_gateup_mx_kernel<FMT><<<(unsigned)(mt * (a.I / 128)), 256, 0, s>>>(g);
         quant_rows_kernel<<<(unsigned)((a.A + 7) / 8), 256, 0, s>>>(
             a.hbuf, a.A, a.I, ws + L.hq_hi, ws + L.hq_lo, ws + L.hq_sc);
@@ -1562,7 +1583,7 @@ static void launch_ffn(const FfnArgs& a, bool decode, hipStream_t s) {
                         (int64_t)a.A * a.I * 2 < (1ll << 32);
       if (fits && a.I % (kNvBN / 2) == 0 && a.H % kNvBN == 0) {
         const int64_t mt =
-            (max_tiles_for(a.A, a.E, kNvMB * 64) + kDmaSuperM - 1) / kDmaSuperM * kDmaSuperM;
+            grid_m_tiles(max_tiles_for(a.A, a.E, kNvMB * 64));
         ffn_gateup_nvd_kernel<<<(unsigned)(mt * (a.I / (kNvBN / 2))), kNvWaves * 64, 0, s>>>(a);
         ffn_down_nvd_kernel<<<(unsigned)(mt * (a.H / kNvBN)), kNvWaves * 64, 0, s>>>(a);
         return;

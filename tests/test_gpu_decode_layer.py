@@ -183,8 +183,10 @@ def test_decode_layer_routing_ties():
     assert rel_err(bf16_to_np(dec["y"][:wl.T]), ref["y"]) <= TOL
 
 
-def test_decode_layer_slot_table():
-    wl = DEC["nvfp4"]
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])   # mxfp4: the one-stream path
+def test_decode_layer_slot_table(fmt):
+    wl = DEC[fmt]
+    flush(f"[decode-layer] slot table {fmt}")
     case = Case(wl)
     layer = _layer(case)
     rng = np.random.default_rng(5)
@@ -196,6 +198,30 @@ def test_decode_layer_slot_table():
     via = _decode(layer, layer.weights(pool), case.logits, case.x, slot=slot)
     _same_routing(direct, via, wl.T, wl.k, wl.E)
     _same_bits(direct, via, wl.T)
+
+
+@pytest.mark.parametrize("T,E", [(8, 256), (16, 256), (16, 16)])
+def test_decode_layer_every_token_same_experts(T, E):
+    """Every token routes to the same k experts (identical logits rows): on the
+    one-stream path each unit then serves all T tokens (the most rows one unit
+    takes) and only k * I/128 units have work."""
+    wl = synth.Workload(f"dec_same_{T}_{E}", T=T, H=2048, E=E, I=512, k=8, fmt="mxfp4",
+                        seed=300 + T + E)
+    flush(f"[decode-layer] same experts T={T} E={E}")
+    case = Case(wl, gen_device="cuda")
+    row = np.random.default_rng(T + E).standard_normal(wl.E).astype(np.float32)
+    lg_np = np.repeat(row[None, :], wl.T, axis=0)
+    lg = torch.from_numpy(lg_np).to(DEV)
+    layer = _layer(case)
+    W = layer.weights(case.records)
+    sep = _separate(layer, W, lg, case.x)
+    dec = _decode(layer, W, lg, case.x)
+    _same_routing(sep, dec, wl.T, wl.k, wl.E)
+    ref = OL.forward(lg_np, case.x_np, wl.k, case.oracle_experts())
+    err = rel_err(bf16_to_np(dec["y"][:wl.T]), ref["y"])
+    flush(f"   rel err vs oracle {err:.2e}")
+    assert err <= TOL
+    assert rel_err(bf16_to_np(dec["y"][:wl.T]), bf16_to_np(sep["y"][:wl.T])) <= 1e-2
 
 
 def test_decode_layer_graph_replays_match_eager():

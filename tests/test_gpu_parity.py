@@ -280,6 +280,41 @@ def test_layer_prefill_pipe(fmt, T, E, H, I):
     assert err <= TOL and dif <= 1e-2
 
 
+# Per-expert row counts on both sides of every 16-row subtile and 64 / 128-row
+# tile boundary (and an expert with no rows), one expert per token (k = 1):
+# the prefill kernels skip the subtiles past an expert's rows.
+BOUNDARY_COUNTS = [1, 15, 16, 17, 0, 63, 64, 65, 127, 128, 129, 2, 300]
+
+
+@pytest.mark.parametrize("fmt", synth.FORMATS)
+def test_layer_prefill_row_boundaries(fmt):
+    E, H, I = len(BOUNDARY_COUNTS), 512, 768
+    T = sum(BOUNDARY_COUNTS)
+    wl = synth.Workload(f"bound_{fmt}", T=T, H=H, E=E, I=I, k=1, fmt=fmt, seed=150)
+    flush(f"[layer-bounds] fmt={fmt} T={T} E={E}")
+    case = Case(wl)
+    rng = np.random.default_rng(151)
+    expert = np.repeat(np.arange(E), BOUNDARY_COUNTS)
+    rng.shuffle(expert)
+    lg = (0.1 * rng.standard_normal((T, E))).astype(np.float32)
+    lg[np.arange(T), expert] = 4.0
+    case.logits_np = lg
+    case.logits = torch.from_numpy(lg).to(DEV)
+    layer, y = _run_layer(case, "prefill")
+    y = y.clone()
+    assert np.array_equal(layer.counts[:E].cpu().numpy(), np.array(BOUNDARY_COUNTS))
+    ref = OL.forward(lg, case.x_np, wl.k, case.oracle_experts())
+    e_perm = rel_err(bf16_to_np(layer.y_perm[:T]), ref["y_perm"])
+    err = rel_err(bf16_to_np(y), ref["y"])
+    flush(f"   rel err y_perm {e_perm:.2e}, y {err:.2e}")
+    assert e_perm <= TOL and err <= TOL
+    # every row on its own: a wrong or skipped subtile shows in its rows even when
+    # the largest row dominates the relative error
+    yp = bf16_to_np(layer.y_perm[:T])
+    row_err = np.max(np.abs(yp - ref["y_perm"]), axis=1) / np.max(np.abs(ref["y_perm"]), axis=1)
+    assert np.all(row_err <= TOL), int(np.argmax(row_err))
+
+
 @pytest.mark.parametrize("fmt", synth.FORMATS)
 def test_variants_agree_and_deterministic(fmt):
     wl = SMALL[fmt]
