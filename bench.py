@@ -115,8 +115,8 @@ def parse():
 # kernel sources the timed launches of each workload are compiled from
 KERNEL_SOURCES = {
     "decode": ("decode.hip", "ffn_common.h", "moe_internal.h", "route_common.h"),
-    "layer": ("ffn.hip", "ffn_common.h", "moe_internal.h", "route.hip", "route_common.h",
-              "permute.hip", "combine.hip"),
+    "layer": ("ffn.hip", "ffn_common.h", "lds_copy.h", "moe_internal.h", "route.hip",
+              "route_common.h", "permute.hip", "combine.hip"),
 }
 
 
