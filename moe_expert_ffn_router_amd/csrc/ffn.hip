@@ -834,9 +834,7 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
   };
   // one m-subtile's A fragments at a time (hi, lo: 16 registers), the next
   // subtile's read from LDS while these are used, against the chunk's 4 raw
-  // B subtiles; accumulators pinned after each step.  Row subtiles past the
-  // tile's rows are skipped.
-  const int nact = min(MSUB, (rows + 15) >> 4);
+  // B subtiles; accumulators pinned after each step
   auto compute = [&](int buf, const QRaw<FMT> (&r)[NSUB]) {
     auto frag = [&](int i, i32x8& h, i32x8& l, int& sa) {
       const int o = (i * 16 + l16) * QP + g * 32;
@@ -860,10 +858,9 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
     }
 #pragma unroll
     for (int i = 0; i < MSUB; ++i) {
-      if (i >= nact) break;
       i32x8 nh, nl;
       int ns = 0;
-      if (i + 1 < nact) frag(i + 1, nh, nl, ns);
+      if (i + 1 < MSUB) frag(i + 1, nh, nl, ns);
 #pragma unroll
       for (int j = 0; j < NSUB; ++j) {
         if constexpr (FMT == MOE_W_MXFP4) {
@@ -883,7 +880,7 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
           pin(acc[i][j]);  // the block-scale FMA reads it as a VALU operand
         }
       }
-      if (i + 1 < nact) {
+      if (i + 1 < MSUB) {
         ah = nh;
         al = nl;
         sa = ns;
@@ -1080,11 +1077,8 @@ __device__ __forceinline__ void ffn_mx_dma_body(const FfnArgs& a, MxDmaStage<MB 
     for (int j = 0; j < NSUB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // the wave's weight subtiles, then its 4 row subtiles (the next one's A
-  // fragments read while the current one's MFMAs run); row subtiles past the
-  // tile's rows are skipped (a wave whose half holds none skips the chunk)
-  const int nact = min(MSUB, max(0, (rows - mh * 64 + 15) >> 4));
+  // fragments read while the current one's MFMAs run)
   auto compute = [&](const MxDmaStage<BM, BN>& S) {
-    if (nact == 0) return;
     i32x4 bq[NSUB];
     int sb[NSUB];
 #pragma unroll
@@ -1118,17 +1112,16 @@ __device__ __forceinline__ void ffn_mx_dma_body(const FfnArgs& a, MxDmaStage<MB 
     frag(0, ah, al, sa);
 #pragma unroll
     for (int i = 0; i < MSUB; ++i) {
-      if (i >= nact) break;
       i32x8 nh, nl;
       int ns = 0;
-      if (i + 1 < nact) frag(i + 1, nh, nl, ns);
+      if (i + 1 < MSUB) frag(i + 1, nh, nl, ns);
 #pragma unroll
       for (int j = 0; j < NSUB; ++j) {
         acc[i][j] = mfma_mx(ah, bq[j], sa, sb[j], acc[i][j]);
         acc[i][j] = mfma_mx(al, bq[j], sa, sb[j], acc[i][j]);
         if constexpr (NSUB > 4) pin_a(acc[i][j]);  // accumulators in AGPRs
       }
-      if (i + 1 < nact) {
+      if (i + 1 < MSUB) {
         ah = nh;
         al = nl;
         sa = ns;
