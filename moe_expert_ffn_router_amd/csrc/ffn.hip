@@ -1195,9 +1195,8 @@ __global__ __launch_bounds__(kDmaWaves * 64) void ffn_down_mxd_kernel(FfnArgs a)
 // with their E4M3 block scales copied straight into LDS (two stages), the
 // codes decoded to bf16 per lane right before the 32x32x16 bf16 MFMAs (that
 // shape runs at twice the rate of 16x16x32 here: 2.5 against 1.3 PFLOP/s
-// measured).  WAVES waves as MB row groups of 32 MR rows x WAVES/MB column
-// groups over BN weight rows; a wave owns MR x NB output blocks of 32 x 32
-// (each decoded weight fragment feeds MR MFMAs).
+// measured).  WAVES waves as MB row groups of 64 rows x WAVES/MB column
+// groups over BN weight rows; a wave owns 2 x NB output blocks of 32 x 32.
 //   32x32x16 operands (checked on the device): lane l holds row (A) or
 //   column (B) l % 32 and 8 consecutive K at 8*(l/32) of the step's 16; result
 //   value v of lane l is C[8*(v/4) + 4*(l/32) + v%4][l % 32].  Within a chunk
@@ -1222,12 +1221,11 @@ struct NvDmaStage {
   __attribute__((aligned(16))) uint2 bs[BN];  // the chunk's 8 E4M3 scale bytes per row
 };
 
-template <bool GATED, int MB, int WAVES, int BN, int MR = 2>
-__device__ __forceinline__ void ffn_nv_dma_body(const FfnArgs& a, NvDmaStage<MB * MR * 32, BN>& s0,
-                                                NvDmaStage<MB * MR * 32, BN>& s1) {
-  static_assert(MB * MR == 2 || MB * MR == 4, "64 or 128 rows per block");
-  constexpr int WM = MR * 32;                    // rows per wave: MR blocks of 32
-  constexpr int BM = MB * WM, NWG = WAVES / MB;  // column groups
+template <bool GATED, int MB, int WAVES, int BN>
+__device__ __forceinline__ void ffn_nv_dma_body(const FfnArgs& a, NvDmaStage<MB * 64, BN>& s0,
+                                                NvDmaStage<MB * 64, BN>& s1) {
+  static_assert(MB == 1 || MB == 2, "64 or 128 rows per block");
+  constexpr int BM = MB * 64, NWG = WAVES / MB;  // column groups
   constexpr int WR = BN / NWG;                   // weight rows per wave
   constexpr int NB = WR / 32;                    // 32-column blocks per wave
   constexpr int NCOLB = GATED ? BN / 2 : BN;     // output columns per block
@@ -1318,9 +1316,9 @@ __device__ __forceinline__ void ffn_nv_dma_body(const FfnArgs& a, NvDmaStage<MB 
     for (int q = 0; q < CPS; ++q) dma4(sc, so[q] + ks, &S.bs[(wave * CPS + q) * 32]);
   };
 
-  f32x16 acc[MR][NB];
+  f32x16 acc[2][NB];
 #pragma unroll
-  for (int i = 0; i < MR; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
 
@@ -1343,10 +1341,10 @@ __device__ __forceinline__ void ffn_nv_dma_body(const FfnArgs& a, NvDmaStage<MB 
     }
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
-      bf16x8 af[MR];
+      bf16x8 af[2];
 #pragma unroll
-      for (int mb = 0; mb < MR; ++mb) {
-        const int r = mh * WM + mb * 32 + l32;
+      for (int mb = 0; mb < 2; ++mb) {
+        const int r = mh * 64 + mb * 32 + l32;
         af[mb] = *reinterpret_cast<const bf16x8*>(ap + r * 128 + ((st ^ a_swz(r)) * 16));
       }
 #pragma unroll
@@ -1355,7 +1353,7 @@ __device__ __forceinline__ void ffn_nv_dma_body(const FfnArgs& a, NvDmaStage<MB 
         const uint32_t d = (st & 3) == 0 ? q.x : (st & 3) == 1 ? q.y : (st & 3) == 2 ? q.z : q.w;
         const bf16x8 bv = fp4x8_to_bf16_mul(d, scl[n][st >> 1]);
 #pragma unroll
-        for (int mb = 0; mb < MR; ++mb) {
+        for (int mb = 0; mb < 2; ++mb) {
           acc[mb][n] = mfma32(af[mb], bv, acc[mb][n]);
           pin_a16(acc[mb][n]);
         }
@@ -1382,10 +1380,10 @@ __device__ __forceinline__ void ffn_nv_dma_body(const FfnArgs& a, NvDmaStage<MB 
     for (int n = 0; n < NB / 2; ++n) {
       const int col = nb * NCOLB + nw * (WR / 2) + n * 32 + l32;
 #pragma unroll
-      for (int mb = 0; mb < MR; ++mb)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int m = mh * WM + mb * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+          const int m = mh * 64 + mb * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
           if (m < rows) {
             const float gv = acc[mb][n][v] * tsg, uv = acc[mb][n + NB / 2][v] * tsu;
             const float hv = gv / (1.0f + expf(-gv)) * uv;
@@ -1399,10 +1397,10 @@ __device__ __forceinline__ void ffn_nv_dma_body(const FfnArgs& a, NvDmaStage<MB 
     for (int n = 0; n < NB; ++n) {
       const int col = nb * NCOLB + nw * WR + n * 32 + l32;
 #pragma unroll
-      for (int mb = 0; mb < MR; ++mb)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int m = mh * WM + mb * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+          const int m = mh * 64 + mb * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
           if (m < rows)
             a.y_perm[(size_t)(seg0 + m) * a.H + col] = f32_to_bf16_rne(acc[mb][n][v] * tsd);
         }
