@@ -534,6 +534,24 @@ const char* moe_status_str(int status);
 const char* moe_last_error(void); /* thread-local; "" when none */
 int moe_version(void);            /* ABI version, currently 1 */
 
+/* Bounds-checked builds (the library compiled with -DMOE_DEBUG; a separate
+ * build, see the package's build script).  There, every index a kernel takes
+ * from a caller's array is range-checked before use: slot-table entries
+ * against [0, E) of the moe_experts they address (the struct carries no
+ * pool size, so with a pool of S < E slots an entry in [S, E) passes),
+ * sorted_idx values against T*k, each expert's row segment (offsets[e],
+ * counts[e]) against [0, T*k), inv_idx values in moe_combine against T*k.
+ * An out-of-range value is replaced by an in-range one (the kernel stays
+ * inside its buffers; its results are then meaningless) and sets a flag:
+ *   1 = slot, 2 = sorted index, 4 = row segment, 8 = inverse index
+ *   (0x80000000: the flags could not be read).
+ * moe_debug_take writes the flags raised since the previous call into *flags
+ * and clears them; it synchronizes the device.  Release builds compile the
+ * checks away and return MOE_ERR_UNSUPPORTED with *flags = 0.  For callers
+ * that want their own inputs checked (the pages' engine states no such
+ * interface). */
+int moe_debug_take(uint32_t* flags);
+
 #ifdef __cplusplus
 }
 #endif

@@ -15,7 +15,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# MOE_LIB_PATH selects another build of the same library (the host-sanitizer build)
+# MOE_LIB_PATH selects another build of the same library (the host-sanitizer build,
+# the bounds-checked build)
 LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(_HERE, "libmoe_mi355x.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP, MOE_ERR_CAPACITY, \
@@ -106,6 +107,7 @@ _SIGS = {
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_version": (ctypes.c_int, []),
+    "moe_debug_take": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint32)]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -486,6 +488,17 @@ def moe_shared_ffn(W: Experts, x: torch.Tensor, T: int, y: torch.Tensor, ws: tor
 
 def moe_version() -> int:
     return int(_lib.moe_version())
+
+
+DBG_SLOT, DBG_SORTED, DBG_SEGMENT, DBG_INV = 1, 2, 4, 8
+
+
+def moe_debug_take() -> int:
+    """Flags raised by a bounds-checked build's range checks since the last call
+    (cleared); raises MoeError (MOE_ERR_UNSUPPORTED) on a release build."""
+    f = ctypes.c_uint32(0)
+    _check(_lib.moe_debug_take(ctypes.byref(f)), "moe_debug_take")
+    return int(f.value)
 
 
 from .layer import MoELayer  # noqa: E402,F401

@@ -64,7 +64,7 @@ def _link(objs: list[str], out: str, libs: list[str]) -> None:
     os.replace(tmp, out)
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, debug: bool = True) -> str:
     os.makedirs(OBJ, exist_ok=True)
     srcs = SOURCES + MEASURE_SOURCES
     with cf.ThreadPoolExecutor(max_workers=min(len(srcs), 8)) as ex:
@@ -73,6 +73,8 @@ def build(verbose: bool = False) -> str:
     _link(objs[:len(SOURCES)], OUT, [])
     if verbose:
         print(f"[build] wrote {OUT}")
+    if debug:
+        build_debug(verbose)
     return OUT
 
 
@@ -105,8 +107,28 @@ def build_host_sanitized(verbose: bool = False) -> str:
     return ASAN_OUT
 
 
+# Bounds-checked build: the same sources with -DMOE_DEBUG (every index taken
+# from a caller's array range-checked and clamped in the kernels, flags read
+# back by moe_debug_take), as a separate library next to the release one,
+# loaded through MOE_LIB_PATH; build() makes both.
+DEBUG_OUT = os.path.join(PKG, "libmoe_mi355x_debug.so")
+
+
+def build_debug(verbose: bool = False) -> str:
+    obj_dir = os.path.join(ROOT, "_build", "debug")
+    os.makedirs(obj_dir, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
+        objs = list(ex.map(lambda src: _compile(src, obj_dir, ("-DMOE_DEBUG",)), SOURCES))
+    _link(objs, DEBUG_OUT, [])
+    if verbose:
+        print(f"[build] wrote {DEBUG_OUT}")
+    return DEBUG_OUT
+
+
 if __name__ == "__main__":
     if "asan" in sys.argv[1:]:
         build_host_sanitized(verbose=True)
+    elif "debug" in sys.argv[1:]:
+        build_debug(verbose=True)
     else:
         build(verbose=True)

@@ -16,7 +16,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   __shared__ int src[kMaxK];
   __shared__ float wt[kMaxK];
   if (threadIdx.x < k) {
-    src[threadIdx.x] = inv_idx[(size_t)t * k + threadIdx.x];
+    src[threadIdx.x] = dbg_clamp(inv_idx[(size_t)t * k + threadIdx.x], T * k, kDbgInv);
     wt[threadIdx.x] = topk_w[(size_t)t * k + threadIdx.x];
   }
   __syncthreads();
@@ -51,6 +51,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     *reinterpret_cast<uint4*>(y + (size_t)t * H + c) = o;
   }
 }
+
+#ifdef MOE_DEBUG
+uint32_t dbg_take_combine() { return dbg_take_unit(); }
+#endif
 
 }  // namespace moe
 

@@ -71,13 +71,14 @@ __device__ __forceinline__ void tiles_load(const FfnArgs& a, TileRegs<NT>& r) {
     if (e < a.E) {
       r.c[i] = a.counts[e];
       r.o[i] = a.offsets[e];
+      dbg_segment(r.o[i], r.c[i], a.A);
     }
   }
   if (a.slot_of) {
 #pragma unroll
     for (int i = 0; i < kMaxE / NT; ++i) {
       const int e = threadIdx.x + i * NT;
-      if (e < a.E) r.s[i] = a.slot_of[e];
+      if (e < a.E) r.s[i] = dbg_clamp(a.slot_of[e], a.E, kDbgSlot);
     }
   }
 }
@@ -361,7 +362,7 @@ __global__ __launch_bounds__(256) void dec_gateup_kernel(DecArgs p) {
   // one round trip: x rows, sorted_idx, counts/offsets/slot table
   uint4 xv[8];
   stage_load<256, 8>(xv, a.x, a.H, T, a.H, 0);
-  const int sid = tid < a.A ? a.sorted_idx[tid] : 0;
+  const int sid = tid < a.A ? dbg_clamp(a.sorted_idx[tid], a.A, kDbgSorted) : 0;
   TileRegs<256> tr;
   tiles_load<256>(a, tr);
   stage_store<256, 8>(xv, xs, xp, T, a.H, 0);
@@ -392,7 +393,7 @@ __global__ __launch_bounds__(256) void dec_down_kernel(FfnArgs a) {
   __shared__ f32x4 red[4][4][64];
   __shared__ int sidx[kDA];
   const int tid = threadIdx.x;
-  const int sid = tid < a.A ? a.sorted_idx[tid] : 0;
+  const int sid = tid < a.A ? dbg_clamp(a.sorted_idx[tid], a.A, kDbgSorted) : 0;
   TileRegs<256> tr;
   tiles_load<256>(a, tr);
   if (tid < a.A) sidx[tid] = sid;
@@ -588,7 +589,7 @@ __global__ __launch_bounds__(256) void dec_gateup_tok_kernel(DecArgs p) {
   if (wave == 0) {
     topk_begin<VPL>(lv, E, lane, st);
     for (int r = 0; r <= jneed; ++r) topk_round<VPL>(st, r, lane);
-    if (lane <= jneed) eslot[lane] = a.slot_of ? a.slot_of[st.id_r] : st.id_r;
+    if (lane <= jneed) eslot[lane] = a.slot_of ? dbg_clamp(a.slot_of[st.id_r], a.E, kDbgSlot) : st.id_r;
   }
   __syncthreads();
   TokRaw<FMT, CPW> ra, rb;
@@ -709,7 +710,7 @@ __global__ __launch_bounds__(256) void dec_down_tok_kernel(DecArgs p) {
   for (int i = 0; i < NJ; ++i) {
     jj[i] = min(wave + 4 * i, k - 1);
     const int id = __builtin_amdgcn_readfirstlane(p.ids[t * k + jj[i]]);
-    const int slot = a.slot_of ? __builtin_amdgcn_readfirstlane(a.slot_of[id]) : id;
+    const int slot = a.slot_of ? __builtin_amdgcn_readfirstlane(dbg_clamp(a.slot_of[id], a.E, kDbgSlot)) : id;
     rec[i] = a.base + (size_t)slot * a.stride;
   }
   const int nchunks = I / KC;
@@ -892,7 +893,7 @@ __global__ __launch_bounds__(1024) void dec_fused_tok_kernel(DecArgs p) {
   if (wave == 0) {
     topk_begin<VPL>(lv, E, lane, st);
     for (int r = 0; r <= j; ++r) topk_round<VPL>(st, r, lane);
-    if (lane == j) eslot[0] = a.slot_of ? a.slot_of[st.id_r] : st.id_r;
+    if (lane == j) eslot[0] = a.slot_of ? dbg_clamp(a.slot_of[st.id_r], a.E, kDbgSlot) : st.id_r;
   }
   __syncthreads();
   const uint8_t* rec = a.base + (size_t)eslot[0] * a.stride;
@@ -1198,6 +1199,10 @@ static int launch_decode(DecArgs& p, hipStream_t s) {
   return moe_combine(p.f.y_perm, p.inv, p.wts, p.T, p.f.k, p.f.H, p.y_shared, p.y,
                      reinterpret_cast<moe_stream_t>(s));
 }
+
+#ifdef MOE_DEBUG
+uint32_t dbg_take_decode() { return dbg_take_unit(); }
+#endif
 
 }  // namespace moe
 

@@ -108,6 +108,7 @@ __device__ __forceinline__ void ffn_decode_body(const FfnArgs& a) {
 
   TileInfo ti;
   if (!find_tile<16>(a.counts, a.offsets, a.E, tile, lane, ti)) return;  // uniform per block
+  dbg_segment(ti.seg0, ti.rows, a.A);
   const uint8_t* rec = record_of(a, ti.e);
   const uint8_t* w = rec + (GATED ? a.off_w13 : a.off_w2);
   const uint8_t* sc = rec + (GATED ? a.off_w13s : a.off_w2s);
@@ -131,7 +132,7 @@ __device__ __forceinline__ void ffn_decode_body(const FfnArgs& a) {
 
   // the row index is requested first: waits on it then leave the weight loads in flight
   int tok = -1;
-  if (l16 < ti.rows) tok = GATED ? a.sorted_idx[ti.seg0 + l16] : ti.seg0 + l16;
+  if (l16 < ti.rows) tok = GATED ? dbg_clamp(a.sorted_idx[ti.seg0 + l16], a.A, kDbgSorted) : ti.seg0 + l16;
   const uint16_t* arow = nullptr;
   bool have_row = false;
   for (int c0 = c_first; c0 < nchunks; c0 += CSTEP * U) {
@@ -300,7 +301,10 @@ __device__ __forceinline__ void ffn_tile_body(const FfnArgs& a) {
     const bool ok = find_tile<BM>(a.counts, a.offsets, a.E, tile, lane, ti);
     if (lane == 0) {
       s_valid = ok;
-      if (ok) s_ti = ti;
+      if (ok) {
+        dbg_segment(ti.seg0, ti.rows, a.A);
+        s_ti = ti;
+      }
     }
   }
   __syncthreads();
@@ -313,7 +317,7 @@ __device__ __forceinline__ void ffn_tile_body(const FfnArgs& a) {
 
   for (int r = tid; r < BM; r += 256) {
     int v = -1;
-    if (r < rows) v = GATED ? a.sorted_idx[seg0 + r] / a.k : seg0 + r;
+    if (r < rows) v = GATED ? dbg_clamp(a.sorted_idx[seg0 + r], a.A, kDbgSorted) / a.k : seg0 + r;
     src_row[r] = v;
   }
   const int ncol0 = nb * NCOL + wave * NCOL_W;
@@ -494,7 +498,10 @@ __device__ __forceinline__ void ffn_pipe_body(const FfnArgs& a) {
     const bool ok = find_tile<BM>(a.counts, a.offsets, a.E, tile, lane, ti);
     if (lane == 0) {
       s_valid = ok;
-      if (ok) s_ti = ti;
+      if (ok) {
+        dbg_segment(ti.seg0, ti.rows, a.A);
+        s_ti = ti;
+      }
     }
   }
   __syncthreads();
@@ -507,7 +514,7 @@ __device__ __forceinline__ void ffn_pipe_body(const FfnArgs& a) {
   // rows past the tile read its first row: valid memory, outputs discarded
   for (int r = tid; r < BM; r += NT) {
     const int rr = r < rows ? r : 0;
-    src_row[r] = GATED ? a.sorted_idx[seg0 + rr] / a.k : seg0 + rr;
+    src_row[r] = GATED ? dbg_clamp(a.sorted_idx[seg0 + rr], a.A, kDbgSorted) / a.k : seg0 + rr;
   }
   const int ncol0 = nb * NCOLB + wave * (NH * 16);
   int brow[NSUB];
@@ -731,7 +738,10 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
     const bool ok = find_tile<BM>(a.counts, a.offsets, a.E, tile, lane, ti);
     if (lane == 0) {
       s_valid = ok;
-      if (ok) s_ti = ti;
+      if (ok) {
+        dbg_segment(ti.seg0, ti.rows, a.A);
+        s_ti = ti;
+      }
     }
   }
   __syncthreads();
@@ -746,7 +756,7 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
   // rows past the tile read its first row: valid memory, outputs discarded
   if (tid < BM) {
     const int rr = tid < rows ? tid : 0;
-    src_row[tid] = GATED ? a.sorted_idx[seg0 + rr] / a.k : seg0 + rr;
+    src_row[tid] = GATED ? dbg_clamp(a.sorted_idx[seg0 + rr], a.A, kDbgSorted) / a.k : seg0 + rr;
   }
   const int ncol0 = nb * NCOLB + wave * (NH * 16);
   // 32-bit byte offsets from the (scalar) weight and scale bases: a weight
@@ -1003,7 +1013,10 @@ __device__ __forceinline__ void ffn_mx_dma_body(const FfnArgs& a, MxDmaStage<MB 
     const bool ok = find_tile<BM>(a.counts, a.offsets, a.E, tile, lane, ti);
     if (lane == 0) {
       s_valid = ok;
-      if (ok) s_ti = ti;
+      if (ok) {
+        dbg_segment(ti.seg0, ti.rows, a.A);
+        s_ti = ti;
+      }
     }
   }
   __syncthreads();
@@ -1017,7 +1030,7 @@ __device__ __forceinline__ void ffn_mx_dma_body(const FfnArgs& a, MxDmaStage<MB 
   // rows past the tile read its first row: valid memory, outputs discarded
   if (tid < BM) {
     const int rr = tid < rows ? tid : 0;
-    src_row[tid] = GATED ? a.sorted_idx[seg0 + rr] / a.k : seg0 + rr;
+    src_row[tid] = GATED ? dbg_clamp(a.sorted_idx[seg0 + rr], a.A, kDbgSorted) / a.k : seg0 + rr;
   }
   __syncthreads();
   // weight row of block-local row br = (group br/64, subtile (br/16)%4,
@@ -1252,7 +1265,10 @@ __device__ __forceinline__ void ffn_nv_dma_body(const FfnArgs& a, NvDmaStage<MB 
     const bool ok = find_tile<BM>(a.counts, a.offsets, a.E, tile, lane, ti);
     if (lane == 0) {
       s_valid = ok;
-      if (ok) s_ti = ti;
+      if (ok) {
+        dbg_segment(ti.seg0, ti.rows, a.A);
+        s_ti = ti;
+      }
     }
   }
   __syncthreads();
@@ -1270,7 +1286,7 @@ __device__ __forceinline__ void ffn_nv_dma_body(const FfnArgs& a, NvDmaStage<MB 
   // rows past the tile read its first row: valid memory, outputs discarded
   if (tid < BM) {
     const int rr = tid < rows ? tid : 0;
-    src_row[tid] = GATED ? a.sorted_idx[seg0 + rr] / a.k : seg0 + rr;
+    src_row[tid] = GATED ? dbg_clamp(a.sorted_idx[seg0 + rr], a.A, kDbgSorted) / a.k : seg0 + rr;
   }
   __syncthreads();
   // weight row of block-local row br = (column group br/WR, 32-row block
@@ -1591,6 +1607,10 @@ static void launch_ffn(const FfnArgs& a, bool decode, hipStream_t s) {
     ffn_down_tile_kernel<FMT><<<(unsigned)(mt * (a.H / 128)), 256, 0, s>>>(a);
   }
 }
+
+#ifdef MOE_DEBUG
+uint32_t dbg_take_ffn() { return dbg_take_unit(); }
+#endif
 
 }  // namespace moe
 

@@ -222,7 +222,7 @@ __device__ __forceinline__ float block_scale(const BRaw<FMT>& r) {
 }
 
 __device__ __forceinline__ const uint8_t* record_of(const FfnArgs& a, int e) {
-  const int slot = a.slot_of ? a.slot_of[e] : e;
+  const int slot = a.slot_of ? dbg_clamp(a.slot_of[e], a.E, kDbgSlot) : e;
   return a.base + (size_t)slot * a.stride;
 }
 

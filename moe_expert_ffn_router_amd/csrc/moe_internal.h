@@ -245,4 +245,48 @@ __device__ __forceinline__ int block_exclusive_scan_1024(int* v, int n, int* wav
   return total;
 }
 
+// ---------------------------------------------------------------------------
+// Bounds-checked build (-DMOE_DEBUG).  Every index a kernel takes from a
+// caller's array — slot table entries, sorted and inverse indices, the row
+// segment an expert's offset and count describe — passes through dbg_clamp /
+// dbg_segment: an out-of-range value sets a bit in this translation unit's
+// flag word and is replaced by an in-range one, so the kernel stays inside
+// its buffers (the results are then meaningless, the flag says so).
+// moe_debug_take() returns and clears the flags of every translation unit.
+// Release builds compile the checks away.
+// ---------------------------------------------------------------------------
+enum : uint32_t { kDbgSlot = 1u, kDbgSorted = 2u, kDbgSegment = 4u, kDbgInv = 8u };
+#ifdef MOE_DEBUG
+static __device__ uint32_t g_dbg_flags;
+__device__ __forceinline__ int dbg_clamp(int v, int hi, uint32_t bit) {  // expects 0 <= v < hi
+  if (v < 0 || v >= hi) {
+    atomicOr(&g_dbg_flags, bit);
+    return v < 0 || hi < 1 ? 0 : hi - 1;
+  }
+  return v;
+}
+// An expert's rows [seg0, seg0 + rows) must lie in [0, A); else no rows.
+__device__ __forceinline__ void dbg_segment(int& seg0, int& rows, int A) {
+  if (seg0 < 0 || rows < 0 || (int64_t)seg0 + rows > A) {
+    atomicOr(&g_dbg_flags, kDbgSegment);
+    seg0 = 0;
+    rows = 0;
+  }
+}
+// The flags of the calling translation unit, cleared (host; synchronizes the device).
+static inline uint32_t dbg_take_unit() {
+  uint32_t v = 0, z = 0;
+  if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_dbg_flags), sizeof(v)) != hipSuccess ||
+      hipMemcpyToSymbol(HIP_SYMBOL(g_dbg_flags), &z, sizeof(z)) != hipSuccess)
+    return 0x80000000u;  // the read failed: reported as a flag of its own
+  return v;
+}
+uint32_t dbg_take_ffn();
+uint32_t dbg_take_decode();
+uint32_t dbg_take_combine();
+#else
+__device__ __forceinline__ int dbg_clamp(int v, int, uint32_t) { return v; }
+__device__ __forceinline__ void dbg_segment(int&, int&, int) {}
+#endif
+
 }  // namespace moe

@@ -74,6 +74,18 @@ const char* moe_last_error(void) { return moe::g_last_error; }
 
 int moe_version(void) { return 1; }
 
+int moe_debug_take(uint32_t* flags) {
+  if (!flags) return moe::set_error(MOE_ERR_INVALID_ARG, "moe_debug_take: flags is NULL");
+#ifdef MOE_DEBUG
+  *flags = moe::dbg_take_ffn() | moe::dbg_take_decode() | moe::dbg_take_combine();
+  return MOE_OK;
+#else
+  *flags = 0;
+  return moe::set_error(MOE_ERR_UNSUPPORTED,
+                        "moe_debug_take: release build (the bounds checks need -DMOE_DEBUG)");
+#endif
+}
+
 int moe_expert_layout_query(int32_t fmt, int32_t H, int32_t I, moe_expert_layout* out) {
   moe::g_last_error[0] = 0;
   if (!out) return moe::set_error(MOE_ERR_INVALID_ARG, "moe_expert_layout_query: out is NULL");
