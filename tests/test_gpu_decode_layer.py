@@ -72,8 +72,8 @@ def _same_bits(r1, r2, T):
     assert torch.equal(r1["y"][:T].view(torch.int16), r2["y"][:T].view(torch.int16)), "y"
 
 
-def _check_case(wl, seed_note=""):
-    case = Case(wl)
+def _check_case(wl, seed_note="", gen_device="cpu"):
+    case = Case(wl, gen_device=gen_device)
     layer = _layer(case)
     assert layer.decode_ws is not None
     W = layer.weights(case.records)
@@ -135,6 +135,16 @@ def test_decode_layer_chunkings(H, I, T, k):
     wl = synth.Workload(f"dec_chunk_{H}_{I}", T=T, H=H, E=32, I=I, k=k, fmt="mxfp4", seed=H + I + T)
     flush(f"[decode-layer] H={H} I={I} T={T} k={k}")
     _check_case(wl, f"H={H} I={I} T={T} k={k}: ")
+
+
+@pytest.mark.parametrize("fmt,T,k", [("nvfp4", 4, 16), ("mxfp4", 4, 16), ("bf16", 20, 8),
+                                      ("fp8_b128", 20, 8)])
+def test_decode_layer_largest_expert_count(fmt, T, k):
+    """E = 1024: the token-major kernels' sixteen logits per lane (T <= 16, k = 16)
+    and the tile-major tile table over 1024 experts (T = 20)."""
+    wl = synth.Workload(f"dec_e1024_{fmt}", T=T, H=512, E=1024, I=512, k=k, fmt=fmt, seed=T + k + 400)
+    flush(f"[decode-layer] E=1024 {fmt} T={T} k={k}")
+    _check_case(wl, f"E=1024 T={T} k={k}: ", gen_device="cuda")
 
 
 def test_decode_layer_full_workload_and_varying_batch():

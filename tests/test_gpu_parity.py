@@ -316,6 +316,32 @@ def test_layer_prefill_row_boundaries(fmt):
     assert np.all(row_err <= TOL), int(np.argmax(row_err))
 
 
+# The ends of the supported range: the largest expert count with the largest k
+# (the tile search holds sixteen experts per lane), the largest hidden and
+# intermediate sizes, and k = E (every token picks every expert).
+EXTREME = [(f, T, E, k, H, I) for f in synth.FORMATS
+           for (T, E, k, H, I) in ((16, 1024, 16, 256, 256), (5, 2, 2, 16384, 256),
+                                   (5, 2, 2, 512, 16384), (5, 2, 2, 16384, 128))]
+
+
+@pytest.mark.parametrize("fmt,T,E,k,H,I", EXTREME)
+def test_layer_extreme_shapes(fmt, T, E, k, H, I):
+    wl = synth.Workload(f"ext_{fmt}_{E}_{H}_{I}", T=T, H=H, E=E, I=I, k=k, fmt=fmt,
+                        seed=160 + E + H // 128 + I // 64)
+    flush(f"[layer-extreme] fmt={fmt} T={T} E={E} k={k} H={H} I={I}")
+    case = Case(wl, gen_device="cuda")
+    ref = OL.forward(case.logits_np, case.x_np, k, case.oracle_experts())
+    A = T * k
+    for variant in ("prefill", "decode"):
+        layer, y = _run_layer(case, variant)
+        assert np.array_equal(layer.counts[:E].cpu().numpy(), ref["counts"])
+        assert np.array_equal(layer.sorted_idx[:A].cpu().numpy(), ref["sorted_idx"])
+        e_perm = rel_err(bf16_to_np(layer.y_perm[:A]), ref["y_perm"])
+        err = rel_err(bf16_to_np(y), ref["y"])
+        flush(f"   {variant}: rel err y_perm {e_perm:.2e}, y {err:.2e}")
+        assert e_perm <= TOL and err <= TOL
+
+
 @pytest.mark.parametrize("fmt", synth.FORMATS)
 def test_variants_agree_and_deterministic(fmt):
     wl = SMALL[fmt]
