@@ -1,8 +1,9 @@
 // Token -> expert permutation: a stable counting sort of the flat assignment
 // index a = t*k + j by expert id, with no order-dependent atomics.
 //
-// The A assignments are cut into chunks of 1024 (one workgroup of 4 waves
-// each); a chunk is 16 segments of 64.  Inside a segment, one wave sorts the
+// The A assignments are cut into chunks (one workgroup of 4 waves each): A <=
+// 1024 is one chunk of up to 16 segments of 64, larger A chunks of 256 (one
+// segment per wave, so that a prefill batch spreads over many workgroups).  Inside a segment, one wave sorts the
 // 64 keys (expert << 6 | lane) with a bitonic network over lane shuffles,
 // which gives every element its rank among equal experts in lower lanes and
 // every group its size.  Per-(segment, expert) sizes are prefix-summed in
@@ -11,23 +12,26 @@
 // chunks' e-count) + (earlier segments' e-count) + rank.
 //
 // A <= 1024 runs as one fused workgroup (one launch, used by decode batches);
-// larger A runs histogram -> scan -> scatter.
+// larger A runs histogram -> scan -> scatter over chunks of 256.
 #include "moe_internal.h"
 
 namespace moe {
 
-constexpr int kSegs = kChunk / 64;  // 16 segments per chunk
 constexpr int kPermThreads = 256;
+constexpr int kBlockChunk = 256;  // assignments per workgroup of the multi-block path
 
+template <int CH>
 struct ChunkLds {
+  static constexpr int kSegs = CH / 64;
   uint16_t segcnt[kSegs][kMaxE];  // per-segment counts, then exclusive prefix
-  int rank[kChunk];               // rank inside its segment, by chunk position
-  int key[kChunk];                // expert of each chunk position (E = invalid)
+  int rank[CH];                   // rank inside its segment, by chunk position
+  int key[CH];                    // expert of each chunk position (E = invalid)
 };
 
 // Sort-based stable ranks of one 64-wide segment.  `key` is the expert id of
 // this lane's element (E for lanes past the end of the input).
-__device__ __forceinline__ void segment_ranks(int key, int lane, int seg, int E, ChunkLds& L) {
+template <int CH>
+__device__ __forceinline__ void segment_ranks(int key, int lane, int seg, int E, ChunkLds<CH>& L) {
   uint32_t v = ((uint32_t)key << 6) | (uint32_t)lane;
 #pragma unroll
   for (int kk = 2; kk <= 64; kk <<= 1) {
@@ -60,14 +64,16 @@ __device__ __forceinline__ void segment_ranks(int key, int lane, int seg, int E,
 // Ranks of one chunk: fills L.key, L.rank and L.segcnt (as exclusive
 // per-expert prefix over segments); returns per-expert chunk totals through
 // `total` (one expert per thread, strided).  Ends with a barrier.
-__device__ void chunk_ranks(const int* __restrict__ ids, int A, int E, int chunk, ChunkLds& L,
+template <int CH>
+__device__ void chunk_ranks(const int* __restrict__ ids, int A, int E, int chunk, ChunkLds<CH>& L,
                             int* __restrict__ total_out /* LDS or null */) {
+  constexpr int kSegs = ChunkLds<CH>::kSegs;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < kSegs * E; i += kPermThreads) L.segcnt[i / E][i % E] = 0;
   __syncthreads();
   for (int seg = wave; seg < kSegs; seg += kPermThreads / 64) {
     const int pos = seg * 64 + lane;
-    const int a = chunk * kChunk + pos;
+    const int a = chunk * CH + pos;
     int key = (a < A) ? ids[a] : E;
     key = (key >= 0 && key < E) ? key : E;  // out-of-range ids are never scattered
     L.key[pos] = key;
@@ -90,10 +96,10 @@ __device__ void chunk_ranks(const int* __restrict__ ids, int A, int E, int chunk
 __global__ __launch_bounds__(kPermThreads) void permute_fused_kernel(
     const int* __restrict__ ids, int A, int E, int* __restrict__ counts, int* __restrict__ offsets,
     int* __restrict__ sorted_idx, int* __restrict__ inv_idx) {
-  __shared__ ChunkLds L;
+  __shared__ ChunkLds<kChunk> L;
   __shared__ int tot[kMaxE];
   __shared__ int wave_tot[4];
-  chunk_ranks(ids, A, E, 0, L, tot);
+  chunk_ranks<kChunk>(ids, A, E, 0, L, tot);
   for (int e = threadIdx.x; e < E; e += kPermThreads) counts[e] = tot[e];
   __syncthreads();
   const int total = block_exclusive_scan_256(tot, E, wave_tot);
@@ -114,8 +120,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_hist_kernel(const int* _
   __shared__ int h[kMaxE];
   for (int e = threadIdx.x; e < E; e += kPermThreads) h[e] = 0;
   __syncthreads();
-  const int base = blockIdx.x * kChunk;
-  for (int i = threadIdx.x; i < kChunk; i += kPermThreads) {
+  const int base = blockIdx.x * kBlockChunk;
+  for (int i = threadIdx.x; i < kBlockChunk; i += kPermThreads) {
     const int a = base + i;
     if (a < A) {
       const int e = ids[a];
@@ -136,10 +142,16 @@ __global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(int nblk, in
   __shared__ int wave_tot[4];
   for (int e = threadIdx.x; e < E; e += kPermThreads) {
     int run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      const int c = blkcnt[(size_t)b * E + e];
-      blkcnt[(size_t)b * E + e] = run;
-      run += c;
+    for (int b0 = 0; b0 < nblk; b0 += 16) {  // 16 loads in flight before their stores
+      int c[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c[i] = b0 + i < nblk ? blkcnt[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (b0 + i < nblk) {
+          blkcnt[(size_t)(b0 + i) * E + e] = run;
+          run += c[i];
+        }
     }
     tot[e] = run;
     counts[e] = run;
@@ -153,13 +165,13 @@ __global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(int nblk, in
 __global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(
     const int* __restrict__ ids, int A, int E, const int* __restrict__ blkbase,
     const int* __restrict__ offsets, int* __restrict__ sorted_idx, int* __restrict__ inv_idx) {
-  __shared__ ChunkLds L;
+  __shared__ ChunkLds<kBlockChunk> L;
   __shared__ int base[kMaxE];
   for (int e = threadIdx.x; e < E; e += kPermThreads)
     base[e] = offsets[e] + blkbase[(size_t)blockIdx.x * E + e];
-  chunk_ranks(ids, A, E, blockIdx.x, L, nullptr);
-  const int c0 = blockIdx.x * kChunk;
-  for (int pos = threadIdx.x; pos < kChunk; pos += kPermThreads) {
+  chunk_ranks<kBlockChunk>(ids, A, E, blockIdx.x, L, nullptr);
+  const int c0 = blockIdx.x * kBlockChunk;
+  for (int pos = threadIdx.x; pos < kBlockChunk; pos += kPermThreads) {
     const int e = L.key[pos];
     if (e >= E) continue;
     const int a = c0 + pos;
@@ -174,7 +186,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(
 extern "C" size_t moe_permute_workspace(int32_t T, int32_t k, int32_t E) {
   if (T <= 0 || k <= 0 || E <= 0) return 256;
   const int64_t A = (int64_t)T * k;
-  const int64_t nblk = (A + moe::kChunk - 1) / moe::kChunk;
+  const int64_t nblk = (A + moe::kBlockChunk - 1) / moe::kBlockChunk;
   return (size_t)(((nblk * E * 4) + 255) / 256 * 256);
 }
 
@@ -200,7 +212,7 @@ extern "C" int moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_
                                                     inv_idx);
     return check_launch("moe_permute(fused)");
   }
-  const int nblk = (A + kChunk - 1) / kChunk;
+  const int nblk = (A + kBlockChunk - 1) / kBlockChunk;
   const size_t need = moe_permute_workspace(T, k, E);
   if (!ws || ws_bytes < need)
     return set_error(MOE_ERR_WORKSPACE, "moe_permute: workspace %zu < %zu bytes", ws_bytes, need);
