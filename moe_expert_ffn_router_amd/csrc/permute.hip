@@ -132,34 +132,57 @@ __global__ __launch_bounds__(kPermThreads) void permute_hist_kernel(const int* _
   for (int e = threadIdx.x; e < E; e += kPermThreads) blkcnt[(size_t)blockIdx.x * E + e] = h[e];
 }
 
-// One workgroup: per expert, exclusive prefix of chunk counts (in place) and
-// the totals; then offsets = exclusive scan of the totals.
-__global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(int nblk, int E,
+// One workgroup of 1024 threads: per expert, exclusive prefix of the chunk
+// counts across chunks (in place) and the totals; then offsets = exclusive scan
+// of the totals.  Thread (part, e) = (tid / E, tid % E) takes the part-th of P
+// contiguous chunk ranges of expert e: it sums its range first (32 loads in
+// flight), the parts' sums meet in LDS, then it reads the range again and
+// overwrites it with running prefixes.
+constexpr int kScanThreads = 1024;
+__global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(int nblk, int E,
                                                                    int* __restrict__ blkcnt,
                                                                    int* __restrict__ counts,
                                                                    int* __restrict__ offsets) {
+  __shared__ int part_sum[kScanThreads];
   __shared__ int tot[kMaxE];
-  __shared__ int wave_tot[4];
-  for (int e = threadIdx.x; e < E; e += kPermThreads) {
-    int run = 0;
-    for (int b0 = 0; b0 < nblk; b0 += 16) {  // 16 loads in flight before their stores
-      int c[16];
+  __shared__ int wave_tot[kScanThreads / 64];
+  const int tid = threadIdx.x;
+  const int P = max(1, min(16, kScanThreads / E));  // parts per expert, P * E <= 1024
+  const int part = tid / E, e = tid - part * E;
+  const bool active = part < P;
+  const int b_lo = active ? (int)((int64_t)part * nblk / P) : 0;
+  const int b_hi = active ? (int)((int64_t)(part + 1) * nblk / P) : 0;
+  int sum = 0;
+  for (int b0 = b_lo; b0 < b_hi; b0 += 32) {
+    int c[32];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) c[i] = b0 + i < nblk ? blkcnt[(size_t)(b0 + i) * E + e] : 0;
+    for (int i = 0; i < 32; ++i) c[i] = b0 + i < b_hi ? blkcnt[(size_t)(b0 + i) * E + e] : 0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (b0 + i < nblk) {
-          blkcnt[(size_t)(b0 + i) * E + e] = run;
-          run += c[i];
-        }
-    }
-    tot[e] = run;
-    counts[e] = run;
+    for (int i = 0; i < 32; ++i) sum += c[i];
+  }
+  part_sum[tid] = sum;
+  __syncthreads();
+  int run = 0;
+  for (int q = 0; q < part && active; ++q) run += part_sum[q * E + e];
+  if (active && part == P - 1) {
+    tot[e] = run + sum;
+    counts[e] = run + sum;
+  }
+  for (int b0 = b_lo; b0 < b_hi; b0 += 32) {
+    int c[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) c[i] = b0 + i < b_hi ? blkcnt[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      if (b0 + i < b_hi) {
+        blkcnt[(size_t)(b0 + i) * E + e] = run;
+        run += c[i];
+      }
   }
   __syncthreads();
-  const int total = block_exclusive_scan_256(tot, E, wave_tot);
-  for (int e = threadIdx.x; e < E; e += kPermThreads) offsets[e] = tot[e];
-  if (threadIdx.x == 0) offsets[E] = total;
+  const int total = block_exclusive_scan<kScanThreads>(tot, E, wave_tot);
+  for (int x = tid; x < E; x += kScanThreads) offsets[x] = tot[x];
+  if (tid == 0) offsets[E] = total;
 }
 
 __global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(
@@ -219,7 +242,7 @@ extern "C" int moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_
   if (!aligned16(ws)) return set_error(MOE_ERR_INVALID_ARG, "moe_permute: ws misaligned");
   int* blk = static_cast<int*>(ws);
   permute_hist_kernel<<<nblk, kPermThreads, 0, s>>>(topk_ids, A, E, blk);
-  permute_scan_kernel<<<1, kPermThreads, 0, s>>>(nblk, E, blk, counts, offsets);
+  permute_scan_kernel<<<1, kScanThreads, 0, s>>>(nblk, E, blk, counts, offsets);
   permute_scatter_kernel<<<nblk, kPermThreads, 0, s>>>(topk_ids, A, E, blk, offsets, sorted_idx,
                                                       inv_idx);
   return check_launch("moe_permute");
