@@ -922,19 +922,23 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
   }
 
   if constexpr (GATED) {
+    // h goes out split for the down GEMM: the wave's 32 columns are one block
+    static_assert(NH == 2, "one 32-column block of h per wave");
 #pragma unroll
     for (int i = 0; i < MSUB; ++i)
 #pragma unroll
-      for (int j = 0; j < NH; ++j)
+      for (int r = 0; r < 4; ++r) {
+        const int m = i * 16 + g * 4 + r;
+        float hv[NH];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = i * 16 + g * 4 + r;
-          if (m < rows) {
-            const float gv = acc[i][j][r], uv = acc[i][j + NH][r];
-            const float hv = gv / (1.0f + expf(-gv)) * uv;
-            a.hbuf[(size_t)(seg0 + m) * a.I + ncol0 + j * 16 + l16] = f32_to_bf16_rne(hv);
-          }
+        for (int j = 0; j < NH; ++j) {
+          const float gv = acc[i][j][r], uv = acc[i][j + NH][r];
+          hv[j] = gv / (1.0f + expf(-gv)) * uv;
         }
+        const size_t row = (size_t)(seg0 + (m < rows ? m : 0));
+        h32_split_store(hv[0], hv[1], m < rows, l16, ncol0, a.hq_hi + row * a.I,
+                        a.hq_lo + row * a.I, a.hq_sc + row * (a.I / 32));
+      }
   } else {
 #pragma unroll
     for (int i = 0; i < MSUB; ++i)
@@ -1157,22 +1161,26 @@ __device__ __forceinline__ void ffn_mx_dma_body(const FfnArgs& a, MxDmaStage<MB 
 
   const int m_base = mh * 64;
   if constexpr (GATED) {
+    // h goes out split for the down GEMM: group qq's 32 columns are one block
+    static_assert(NH == 2, "one 32-column block of h per weight group");
 #pragma unroll
     for (int qq = 0; qq < NQ; ++qq) {
       const int c0 = nb * NCOLB + (nw * NQ + qq) * (NH * 16);
 #pragma unroll
       for (int i = 0; i < MSUB; ++i)
 #pragma unroll
-        for (int jj = 0; jj < NH; ++jj)
+        for (int r = 0; r < 4; ++r) {
+          const int m = m_base + i * 16 + g * 4 + r;
+          float hv[NH];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int m = m_base + i * 16 + g * 4 + r;
-            if (m < rows) {
-              const float gv = acc[i][qq * 4 + jj][r], uv = acc[i][qq * 4 + NH + jj][r];
-              const float hv = gv / (1.0f + expf(-gv)) * uv;
-              a.hbuf[(size_t)(seg0 + m) * a.I + c0 + jj * 16 + l16] = f32_to_bf16_rne(hv);
-            }
+          for (int jj = 0; jj < NH; ++jj) {
+            const float gv = acc[i][qq * 4 + jj][r], uv = acc[i][qq * 4 + NH + jj][r];
+            hv[jj] = gv / (1.0f + expf(-gv)) * uv;
           }
+          const size_t row = (size_t)(seg0 + (m < rows ? m : 0));
+          h32_split_store(hv[0], hv[1], m < rows, l16, c0, a.hq_hi + row * a.I,
+                          a.hq_lo + row * a.I, a.hq_sc + row * (a.I / 32));
+        }
     }
   } else {
     const int ncol0 = nb * NCOLB + nw * (NSUB * 16);
@@ -1552,11 +1560,12 @@ static void launch_ffn(const FfnArgs& a, bool decode, hipStream_t s) {
     // the kernels address the split operands with 32-bit offsets
     const bool fits = (int64_t)T * a.H < (1ll << 32) && (int64_t)a.A * a.I < (1ll << 32);
     if (!decode && pipe_ok(a) && fits) {
-      // split x once, gate/up, split h once, down
+      // split x once; gate/up, whose epilogue writes h split; down
       const FfnWs L = ffn_ws(FMT, T, a.k, a.H, a.I);
       uint8_t* ws = reinterpret_cast<uint8_t*>(a.hbuf);
       FfnArgs g = a;
       g.aq_hi = ws + L.xq_hi; g.aq_lo = ws + L.xq_lo; g.aq_sc = ws + L.xq_sc;
+      g.hq_hi = ws + L.hq_hi; g.hq_lo = ws + L.hq_lo; g.hq_sc = ws + L.hq_sc;  // gate/up writes h split
       FfnArgs d = a;
       d.aq_hi = ws + L.hq_hi; d.aq_lo = ws + L.hq_lo; d.aq_sc = ws + L.hq_sc;
       quant_rows_kernel<<<(unsigned)((T + 7) / 8), 256, 0, s>>>(
@@ -1568,14 +1577,10 @@ static void launch_ffn(const FfnArgs& a, bool decode, hipStream_t s) {
         const int64_t mt =
             grid_m_tiles(max_tiles_for(a.A, a.E, kDmaBM));
         ffn_gateup_mxd_kernel<<<(unsigned)(mt * (a.I / (kDmaBN / 2))), kDmaWaves * 64, 0, s>>>(g);
-        quant_rows_kernel<<<(unsigned)((a.A + 7) / 8), 256, 0, s>>>(
-            a.hbuf, a.A, a.I, ws + L.hq_hi, ws + L.hq_lo, ws + L.hq_sc);
         ffn_down_mxd_kernel<<<(unsigned)(mt * (a.H / kDmaBN)), kDmaWaves * 64, 0, s>>>(d);
       } else {
         const int64_t mt = grid_m_tiles(max_tiles_for(a.A, a.E, 64));
         ffn_gateup_mx_kernel<FMT><<<(unsigned)(mt * (a.I / 128)), 256, 0, s>>>(g);
-        quant_rows_kernel<<<(unsigned)((a.A + 7) / 8), 256, 0, s>>>(
-            a.hbuf, a.A, a.I, ws + L.hq_hi, ws + L.hq_lo, ws + L.hq_sc);
         ffn_down_mx_kernel<FMT><<<(unsigned)(mt * (a.H / 256)), 256, 0, s>>>(d);
       }
       return;

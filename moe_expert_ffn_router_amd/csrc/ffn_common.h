@@ -28,6 +28,11 @@ struct FfnArgs {
   const uint8_t* aq_hi;
   const uint8_t* aq_lo;
   const uint8_t* aq_sc;
+  // block-scaled prefill, gate/up: h written split as the down GEMM's A
+  // operand (same layout as aq_*), in place of bf16 h
+  uint8_t* hq_hi = nullptr;
+  uint8_t* hq_lo = nullptr;
+  uint8_t* hq_sc = nullptr;
 };
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -148,6 +153,45 @@ __device__ __forceinline__ void prep_a_mx_store(const uint4 (&v)[4], int rows, i
       *reinterpret_cast<uint2*>(lo + o) = uint2{(uint32_t)l0, (uint32_t)l1};
       if ((r & 31) == 0) sc[(size_t)row * (K / 32) + r / 32] = (uint8_t)(127 + e);
     }
+  }
+}
+
+// Max over the 16 lanes of each DPP row; every lane receives its row's value.
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t x) {
+  int v = (int)x;
+  auto mx = [](int a, int b) { return (int)((uint32_t)a > (uint32_t)b ? (uint32_t)a : (uint32_t)b); };
+  v = mx(v, dpp_i32<0xB1>(0, v));   // quad_perm [1,0,3,2]
+  v = mx(v, dpp_i32<0x4E>(0, v));   // quad_perm [2,3,0,1]
+  v = mx(v, dpp_i32<0x141>(0, v));  // row_half_mirror
+  v = mx(v, dpp_i32<0x140>(0, v));  // row_mirror
+  return (uint32_t)v;
+}
+
+// Gate/up epilogue of the block-scaled prefill kernels: one row's 32-column
+// block of h, held by the 16 lanes of one DPP row as (lane l16, half j) =
+// column 16 j + l16 of the block starting at column c0.  Rounds the values to
+// bf16 and writes the E4M3 hi / lo bytes (A order) and the E8M0 scale that
+// prep_a_mx_store makes from those bf16 values, the down GEMM's A operand.
+// Every lane of the row takes part (the maximum crosses lanes); `store` must
+// be the same for all 16.
+__device__ __forceinline__ void h32_split_store(float h0, float h1, bool store, int l16, int c0,
+                                                uint8_t* hi_row, uint8_t* lo_row,
+                                                uint8_t* sc_row) {
+  const float f0 = bf16_to_f32(f32_to_bf16_rne(h0)), f1 = bf16_to_f32(f32_to_bf16_rne(h1));
+  const uint32_t m0 = __float_as_uint(f0) & 0x7fffffffu, m1 = __float_as_uint(f1) & 0x7fffffffu;
+  const uint32_t am = row16_max_u32(m0 > m1 ? m0 : m1);
+  int e = am ? (int)(am >> 23) - 127 - 7 : 0;
+  e = e < -127 ? -127 : e;
+  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);
+  int hw, lw;
+  e4m3_hi_lo(f0 * inv, f1 * inv, 0.0f, 0.0f, hw, lw);
+  if (store) {
+    const int o0 = a_order(c0 + l16), o1 = a_order(c0 + 16 + l16);
+    hi_row[o0] = (uint8_t)hw;
+    lo_row[o0] = (uint8_t)lw;
+    hi_row[o1] = (uint8_t)(hw >> 8);
+    lo_row[o1] = (uint8_t)(lw >> 8);
+    if (l16 == 0) sc_row[c0 / 32] = (uint8_t)(127 + e);
   }
 }
 
