@@ -155,8 +155,9 @@ int moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t k, int3
  *   variant         0 = choose by size, 1 = small-batch (decode) kernels,
  *                   2 = tiled (prefill) kernels; all give the same result up
  *                   to fp32 summation order
- * ws: device, >= moe_expert_ffn_workspace(W, T, k): h bf16 [T*k][I], and
- *     for MXFP4 / FP8 weights the split activations of both GEMMs.          */
+ * ws: device, >= moe_expert_ffn_workspace(W, T, k): h bf16 [T*k][I], or,
+ *     on the MXFP4 / FP8 prefill path, the split activations of both GEMMs
+ *     in the same space (that path never forms bf16 h).                     */
 size_t moe_expert_ffn_workspace(const moe_experts* W, int32_t T, int32_t k);
 int moe_expert_ffn(const moe_experts* W, const int32_t* slot_of_expert, const uint16_t* x,
                    int32_t T, int32_t k, const int32_t* counts, const int32_t* offsets,

@@ -1529,9 +1529,10 @@ static bool pipe_ok(const FfnArgs& a) { return a.H % 256 == 0 && a.I % 256 == 0;
 
 static int64_t al256(int64_t n) { return (n + 255) / 256 * 256; }
 
-// Workspace of one moe_expert_ffn call: h (bf16 [A][I]), then for the
-// block-scaled prefill formats the split A operands of both GEMMs: h as
-// hi [A][I], lo [A][I], scales [A][I/32], then x as hi [T][H], lo, scales.
+// Workspace of one moe_expert_ffn call: h (bf16 [A][I]); or, on the
+// block-scaled prefill path (which never forms bf16 h), the split A operands
+// of both GEMMs from the same start: h as hi [A][I], lo [A][I], scales
+// [A][I/32], then x as hi [T][H], lo, scales.  The size covers both.
 struct FfnWs {
   int64_t h, hq_hi, hq_lo, hq_sc, xq_hi, xq_lo, xq_sc, total;
 };
@@ -1539,17 +1540,19 @@ static bool quantized_prefill_fmt(int fmt) { return fmt == MOE_W_MXFP4 || fmt ==
 static FfnWs ffn_ws(int fmt, int64_t T, int64_t k, int H, int I) {
   FfnWs w{};
   const int64_t A = T * k;
-  int64_t p = 0;
-  w.h = p; p += al256(A * I * 2);
+  w.h = 0;
+  int64_t end = al256(A * I * 2);
   if (quantized_prefill_fmt(fmt)) {
+    int64_t p = 0;
     w.hq_hi = p; p += al256(A * I);
     w.hq_lo = p; p += al256(A * I);
     w.hq_sc = p; p += al256(A * I / 32);
     w.xq_hi = p; p += al256(T * H);
     w.xq_lo = p; p += al256(T * H);
     w.xq_sc = p; p += al256(T * H / 32);
+    end = end > p ? end : p;
   }
-  w.total = p + 256;
+  w.total = end + 256;
   return w;
 }
 
