@@ -75,7 +75,6 @@ struct SgArgs {
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ void pin_acc(f32x16& acc) { asm volatile("" : "+a"(acc)); }
 
 template <bool GATED>
 __global__ __launch_bounds__(64 * kSgWaves) void shared_gemm_kernel(SgArgs p) {

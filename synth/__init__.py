@@ -335,10 +335,6 @@ def algorithmic_expert_bytes(fmt: str, H: int, I: int) -> int:
     return record_layout(fmt, H, I)["payload"]
 
 
-def flops_per_assignment(H: int, I: int) -> int:
-    return 2 * 3 * H * I
-
-
 def describe(wl: Workload) -> dict:
     d = dataclasses.asdict(wl)
     d["record_stride"] = record_layout(wl.fmt, wl.H, wl.I)["stride"]
