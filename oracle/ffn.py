@@ -31,12 +31,6 @@ def swiglu(X: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray) -> np.
     return (silu(G) * U) @ np.asarray(Wd, dtype=np.float64).T
 
 
-def swiglu_hidden(X, Wg, Wu) -> np.ndarray:
-    """The SiLU(G)*U intermediate alone (rows of X times the gate/up pair)."""
-    X = np.asarray(X, dtype=np.float64)
-    return silu(X @ np.asarray(Wg).T) * (X @ np.asarray(Wu).T)
-
-
 def expert_ffn(x_tokens: np.ndarray, k: int, offsets: np.ndarray, sorted_idx: np.ndarray,
                expert_weights, experts=None) -> np.ndarray:
     """Y_perm [A, H]: row p = FFN_e(x[token(p)]) for the expert e owning row p.

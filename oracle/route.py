@@ -24,12 +24,6 @@ from __future__ import annotations
 import numpy as np
 
 
-def expert_order(logits_row: np.ndarray) -> np.ndarray:
-    """All experts of one token, best first (stable on ties -> lower index first)."""
-    l = np.asarray(logits_row, dtype=np.float64)
-    return np.argsort(-l, kind="stable")
-
-
 def route(logits: np.ndarray, k: int, renorm: bool = True):
     """logits fp32 [T,E] -> (ids int32 [T,k], weights float64 [T,k])."""
     lg = np.asarray(logits, dtype=np.float32)
