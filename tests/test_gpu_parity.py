@@ -394,6 +394,46 @@ def test_layer_full_size_sampled_tokens(name, tokens):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("fmt", synth.FORMATS)
+def test_prefill_layer_graph_replays_match_eager(fmt):
+    """The prefill layer (route+permute, expert FFN, shared expert, combine)
+    captured in one graph over three batches: every replay, with eager calls of
+    the same layer between replays, gives the eager results bit for bit."""
+    wl = synth.Workload(f"graph_{fmt}", T=300, H=512, E=16, I=768, k=2, fmt=fmt, seed=170,
+                        zipf=0.8, shared_I=256)
+    flush(f"[prefill-graph] fmt={fmt}")
+    case = Case(wl)
+    layer = moe.MoELayer(fmt, wl.E, wl.H, wl.I, wl.k, wl.T, case.stride, shared_I=wl.shared_I,
+                         shared_stride=case.shared.shape[1])
+    W = layer.weights(case.records)
+    Ws = moe.experts("bf16", 1, wl.H, wl.shared_I, case.shared, case.shared.shape[1])
+    batches = []
+    for b in range(3):
+        lg = torch.from_numpy(synth.make_logits(wl, 300 + b)).to(DEV)
+        x = torch.from_numpy(synth.make_x(wl, 300 + b).view(np.int16)).to(DEV).view(torch.bfloat16)
+        batches.append((lg, x))
+    eager = [layer.forward(lg, x, W, Ws, variant="prefill").clone() for lg, x in batches]
+    torch.cuda.synchronize()
+    ref = OL.forward(synth.make_logits(wl, 300), synth.make_x(wl, 300), wl.k, case.oracle_experts(),
+                     case.oracle_shared())
+    assert rel_err(bf16_to_np(eager[0]), ref["y"]) <= TOL
+    outs = [torch.empty(wl.T, wl.H, dtype=torch.bfloat16, device=DEV) for _ in batches]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for (lg, x), o in zip(batches, outs):
+            layer.forward(lg, x, W, Ws, variant="prefill")
+            o.copy_(layer.y[:wl.T])
+    for rep in range(4):
+        for o in outs:
+            o.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o.view(torch.int16), e.view(torch.int16)), f"replay {rep}"
+        layer.forward(batches[2][0], batches[2][1], W, Ws, variant="prefill")  # eager work between
+        torch.cuda.synchronize()
+
+
 def test_layer_empty_batch():
     wl = SMALL["mxfp4"]
     case = Case(wl)
