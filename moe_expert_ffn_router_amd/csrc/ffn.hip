@@ -446,7 +446,7 @@ __global__ __launch_bounds__(256) void ffn_down_tile_kernel(FfnArgs a) {
 // of 8 m-tiles column block by column block, each super-tile on one XCD
 // (tile_of_block).
 // ----------------------------------------------------------------------------
-constexpr int kSuperM = 8;  // m-tiles per super-tile (prefill block order)
+constexpr int kSuperM = 8;  // m-tiles per super-tile (prefill block order), bf16 kernels
 
 // Block b -> (m-tile, column block) for the prefill grids.  The grid holds
 // whole super-tiles (SM m-tiles x nnb column blocks, walked column block by
@@ -466,7 +466,8 @@ __device__ __forceinline__ void tile_of_block(int b, int nnb, int& tile, int& nb
   nb = gi / SM;
 }
 // m-tiles of a grid: the bound rounded up to whole groups of 8 super-tiles
-static int64_t grid_m_tiles(int64_t bound) { return (bound + 8 * kSuperM - 1) / (8 * kSuperM) * (8 * kSuperM); }
+// of SM m-tiles
+static int64_t grid_m_tiles(int64_t bound, int SM) { return (bound + 8 * SM - 1) / (8 * SM) * (8 * SM); }
 
 template <int FMT, bool GATED, int MSUB, int MH>
 __device__ __forceinline__ void ffn_pipe_body(const FfnArgs& a) {
@@ -698,6 +699,9 @@ constexpr int QP = KC + 16;  // LDS row pitch of the hi / lo bytes
 // A lane's raw weight bytes of one chunk in the MFMA's B order: E2M1, K
 // [32g, 32g+32) (16 bytes); E4M3, K [16g, 16g+16) and [64+16g, 64+16g+16)
 // (2 x 16 bytes).  Their scales are staged through LDS.
+// m-tiles per super-tile of the register-staged block-scaled kernels (4: FP8
+// hit path 0.79 -> 0.74 ms against 8; 2 measured 0.75)
+constexpr int kMxSuperM = 4;
 template <int FMT>
 struct QRaw {
   uint4 q[FMT == MOE_W_FP8_B128 ? 2 : 1];
@@ -713,11 +717,11 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
   const int K = GATED ? a.H : a.I, nch = K / KC;
   const int nnb = N_out / NCOLB;
   const int b = (int)blockIdx.x;
-  // super-tiles of kSuperM m-tiles x all column blocks, walked column block
-  // by column block: the blocks one XCD runs at a time share both the A rows
-  // of a few m-tiles and the weights of a few column blocks in its L2
+  // super-tiles of kMxSuperM m-tiles x all column blocks, walked column
+  // block by column block: the blocks one XCD runs at a time share both the
+  // A rows of a few m-tiles and the weights of a few column blocks in its L2
   int tile, nb;
-  tile_of_block<kSuperM>(b, nnb, tile, nb);
+  tile_of_block<kMxSuperM>(b, nnb, tile, nb);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
 
   __shared__ __attribute__((aligned(16))) uint8_t Sh[2][BM * QP];
@@ -972,8 +976,11 @@ __global__ __launch_bounds__(256) void ffn_down_mx_kernel(FfnArgs a) {
 // (vmcnt) and for its LDS reads of chunk c-1 (lgkmcnt), then one barrier
 // makes all copies visible and frees chunk c-1's stage for chunk c+1.
 // ---------------------------------------------------------------------------
-// m-tiles per super-tile (8, 16, 32 and 64 measured within 4 %; 8 best)
-constexpr int kDmaSuperM = kSuperM;
+// m-tiles per super-tile of the copy-pipeline kernels: MXFP4 4 (large prefill
+// FFN 9.87 -> 9.81 ms against 8; 16, 32 and 64 within 4 % and slower), NVFP4 8
+// (4 and 2 measured 1 % slower)
+constexpr int kDmaSuperM = 4;
+constexpr int kNvSuperM = 8;
 template <int BM, int BN>
 struct MxDmaStage {
   uint8_t ah[BM * 128];  // A hi [row][128 B]: 16-byte unit u stored at u ^ a_swz(row)
@@ -1260,7 +1267,7 @@ __device__ __forceinline__ void ffn_nv_dma_body(const FfnArgs& a, NvDmaStage<MB 
   const int nnb = N_out / NCOLB;
   const int b = (int)blockIdx.x;
   int tile, nb;
-  tile_of_block<kDmaSuperM>(b, nnb, tile, nb);
+  tile_of_block<kNvSuperM>(b, nnb, tile, nb);
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int mh = wave / NWG, nw = wave % NWG;
@@ -1518,7 +1525,7 @@ static void fill_args(FfnArgs& a, const moe_experts* W, const Layout& L) {
 template <int MSUB, int MH, typename K1, typename K2>
 static void launch_pipe(const FfnArgs& a, K1 k1, K2 k2, hipStream_t s) {
   // whole super-tiles: the grid is then a multiple of 8 as well
-  const int64_t mt = grid_m_tiles(max_tiles_for(a.A, a.E, MSUB * 16 * MH));
+  const int64_t mt = grid_m_tiles(max_tiles_for(a.A, a.E, MSUB * 16 * MH), kSuperM);
   k1<<<(unsigned)(mt * (a.I / 128)), 256 * MH, 0, s>>>(a);
   k2<<<(unsigned)(mt * (a.H / 256)), 256 * MH, 0, s>>>(a);
 }
@@ -1578,11 +1585,11 @@ static void launch_ffn(const FfnArgs& a, bool decode, hipStream_t s) {
       if (FMT == MOE_W_MXFP4 && a.I % (kDmaBN / 2) == 0 && a.H % kDmaBN == 0) {
         // 128-row tiles on the LDS-DMA pipeline
         const int64_t mt =
-            grid_m_tiles(max_tiles_for(a.A, a.E, kDmaBM));
+            grid_m_tiles(max_tiles_for(a.A, a.E, kDmaBM), kDmaSuperM);
         ffn_gateup_mxd_kernel<<<(unsigned)(mt * (a.I / (kDmaBN / 2))), kDmaWaves * 64, 0, s>>>(g);
         ffn_down_mxd_kernel<<<(unsigned)(mt * (a.H / kDmaBN)), kDmaWaves * 64, 0, s>>>(d);
       } else {
-        const int64_t mt = grid_m_tiles(max_tiles_for(a.A, a.E, 64));
+        const int64_t mt = grid_m_tiles(max_tiles_for(a.A, a.E, 64), kMxSuperM);
         ffn_gateup_mx_kernel<FMT><<<(unsigned)(mt * (a.I / 128)), 256, 0, s>>>(g);
         ffn_down_mx_kernel<FMT><<<(unsigned)(mt * (a.H / 256)), 256, 0, s>>>(d);
       }
@@ -1600,7 +1607,7 @@ static void launch_ffn(const FfnArgs& a, bool decode, hipStream_t s) {
                         (int64_t)a.A * a.I * 2 < (1ll << 32);
       if (fits && a.I % (kNvBN / 2) == 0 && a.H % kNvBN == 0) {
         const int64_t mt =
-            grid_m_tiles(max_tiles_for(a.A, a.E, kNvMB * 64));
+            grid_m_tiles(max_tiles_for(a.A, a.E, kNvMB * 64), kNvSuperM);
         ffn_gateup_nvd_kernel<<<(unsigned)(mt * (a.I / (kNvBN / 2))), kNvWaves * 64, 0, s>>>(a);
         ffn_down_nvd_kernel<<<(unsigned)(mt * (a.H / kNvBN)), kNvWaves * 64, 0, s>>>(a);
         return;
