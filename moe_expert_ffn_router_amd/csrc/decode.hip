@@ -1,6 +1,13 @@
-// The MoE layer for decode-sized batches in four launches.  Kernel
-// boundaries are the only waits between workgroups.
+// The MoE layer for decode-sized batches (moe_forward_decode).  Kernel
+// boundaries are the only waits between workgroups.  Three forms:
 //
+//  * one weight stream (MXFP4, T <= 16, T*k*(I/128) a multiple of 256): two
+//    launches, dec_fused_tok_kernel (a workgroup per (token, slot, 128 h
+//    columns) routes its token, computes that h slice and its share of the
+//    down projection as fp32 partials) and dec_fused_combine_kernel;
+//  * token-major (T <= 16, H <= 2048): two launches, dec_gateup_tok_kernel
+//    (routing inside) and dec_down_tok_kernel (combine folded in);
+//  * tile-major (larger T), four launches:
 //  1. route + permute: one workgroup (route_permute_small_kernel).
 //  2. gate/up: a persistent grid sized by occupancy.  Each workgroup stages x,
 //     sorted_idx and the 16-row tile list in LDS in one round trip, then takes

@@ -1,6 +1,6 @@
-// Per-expert SwiGLU FFN over the permuted rows (grouped GEMM on the bf16 MFMA
-// V_MFMA_F32_16X16X32_BF16): one launch for gate/up with the SiLU*mul
-// epilogue, one for down.
+// Per-expert SwiGLU FFN over the permuted rows (grouped GEMMs on MFMA): one
+// launch for gate/up with the SiLU*mul epilogue, one for down (plus, on the
+// block-scaled prefill path, one pass that splits x).
 //
 // Work unit = (m-tile of one expert's rows, block of output columns).  Each
 // workgroup finds its (expert, first row) from `counts` itself (a wave-wide
@@ -8,26 +8,33 @@
 // needed and the whole call can be captured into a graph.
 //
 // Operands.  A = activations: bf16 rows gathered by token (gate/up) or the
-// contiguous h rows (down).  B = expert weights, read from HBM into registers
-// in their stored format and decoded there to bf16 (every MXFP4 value, NVFP4
-// E2M1 x E4M3 product and E4M3 value is exact in bf16); FP8 block scales and
-// NVFP4 tensor scales multiply fp32 partial sums.
+// contiguous h rows (down); on the block-scaled paths (MXFP4, FP8) each row
+// is split once into E4M3 hi + lo with one E8M0 scale per 32.  B = expert
+// weights in their stored format: fed to the block-scaled MFMA as stored
+// (E2M1 with its E8M0 scales, E4M3 with a unit scale), or decoded in
+// registers to bf16 for the bf16 MFMA (every MXFP4 value, NVFP4 E2M1 x E4M3
+// product and E4M3 value is exact in bf16); FP8 block scales and NVFP4
+// tensor scales multiply fp32 partial sums.
 //
-// K mapping.  For a 128-wide K chunk, lane group g = lane/16 owns the 32
-// consecutive K values [32g, 32g+32) of its row; MFMA step s consumes values
-// [32g+8s, 32g+8s+8).  A and B use the same mapping, so each output is the
-// full dot product whatever the instruction's internal K order.
+// K mapping of the 16x16x32 bf16 kernels.  For a 128-wide K chunk, lane
+// group g = lane/16 owns the 32 consecutive K values [32g, 32g+32) of its
+// row; MFMA step s consumes values [32g+8s, 32g+8s+8).  A and B use the same
+// mapping, so each output is the full dot product whatever the instruction's
+// internal K order.
 //
-// Two kernel families:
+// Kernel families:
 //  * decode (few rows per expert): m-tile = 16 rows; the 4 waves of a
 //    workgroup split K (chunks w, w+4, ...), each wave issues the loads of
 //    up to 4 chunks before consuming any (16 KB in flight per wave), and the
 //    4 partial sums are added in wave order through LDS (deterministic).
 //    Bandwidth-bound: each touched expert's weights are read once.
-//  * prefill (many rows): m-tile = 64 rows staged in LDS, each wave owns
-//    16 x 4 output columns over the full K.  MXFP4 prefill takes 128-row
-//    tiles on 8 waves whose operands are copied into LDS by the memory path
-//    itself (no registers hold loads in flight), three K chunks deep.
+//  * prefill, register-staged (BF16, FP8, and the MXFP4 / NVFP4 shapes the
+//    copy kernels do not take): m-tile = 64 rows, the A chunk staged in LDS,
+//    the weight chunk raw in registers one chunk ahead.
+//  * prefill, copy pipeline (MXFP4: 128-row tiles on 8 waves; NVFP4: 64-row
+//    tiles on 4 waves): every operand byte copied from global memory into
+//    LDS by global_load_lds, two K chunks deep, so no registers hold loads in
+//    flight.
 #include "ffn_common.h"
 #include "lds_copy.h"
 

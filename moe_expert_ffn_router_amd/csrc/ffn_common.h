@@ -1,6 +1,8 @@
 // Device pieces shared by the expert-FFN kernels: argument block, the K
-// mapping of a 128-wide chunk onto MFMA lanes, raw weight loads and their
-// in-register decode to bf16.
+// mapping of a 128-wide chunk onto MFMA lanes, the block-scaled MFMA, the
+// split of bf16 activation rows into E4M3 hi + lo with E8M0 scales (as a pass
+// and as the gate/up epilogue), raw weight loads and their in-register
+// decode to bf16.
 #pragma once
 
 #include "moe_internal.h"

@@ -7,14 +7,15 @@
 // K-major, so both GEMMs are C[M][N] = A[M][K] . B[N][K]^T.
 //
 // Tiling (gfx950, 160 KB LDS per CU): 256 output rows x 256 weight rows per
-// workgroup of 4 waves (2 x 2), each wave 128 x 128 outputs as 4 x 4 blocks of
-// 32 x 32 (16 accumulators of 16 fp32, kept in AGPRs: one wave per SIMD).
-// Operands are copied from global memory straight into LDS
-// (global_load_lds_dwordx4) in K steps of kSgBK (kSgStages stages: the next
-// kSgStages-1 chunks are in flight while one is computed), one barrier per
-// chunk.  Gate/up tiles take 128 h columns: the 256 weight rows
-// are, per wave half, 64 gate rows followed by the matching 64 up rows, so
-// SiLU(gate) * up is formed in registers.  Workgroups are mapped to
+// workgroup of kSgWaves waves, 2 along the rows x kSgWaves/2 along the weight
+// rows (default 8 waves, two per SIMD: each wave 128 x 64 outputs as 4 x 2
+// blocks of 32 x 32, accumulators in AGPRs).  Operands are copied from global
+// memory straight into LDS (global_load_lds_dwordx4) in K steps of kSgBK
+// (kSgStages stages, default two of 64: the next kSgStages-1 chunks are in
+// flight while one is computed), one barrier per chunk.  Gate/up tiles take
+// 128 h columns: each wave column group's weight rows are 16*kSgNJ gate rows
+// followed by the matching 16*kSgNJ up rows, so SiLU(gate) * up is formed in
+// registers.  Workgroups are mapped to
 // rectangles of tiles per XCD (consecutive workgroups of one XCD share their
 // A rows or weight rows in its L2).
 //   32x32x16 operands: lane l holds row (A) / column (B) l % 32 and the 8
