@@ -701,7 +701,7 @@ __global__ __launch_bounds__(256 * MH) void ffn_down_pipe_kernel(FfnArgs a) {
 //   4 A-scale bytes per row, and the chunk's weight scales (MXFP4: 4 E8M0
 //   bytes per weight row; FP8: the two fp32 block scales), staged with A.
 // ----------------------------------------------------------------------------
-constexpr int QP = KC + 16;  // LDS row pitch of the hi / lo bytes
+constexpr int QP = KC;  // LDS row pitch of the hi / lo bytes (16-byte units XOR-swizzled by a_swz)
 
 // A lane's raw weight bytes of one chunk in the MFMA's B order: E2M1, K
 // [32g, 32g+32) (16 bytes); E4M3, K [16g, 16g+16) and [64+16g, 64+16g+16)
@@ -832,10 +832,12 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
       if (tid < 2) fsv = reinterpret_cast<const float*>(sc)[(size_t)fsrow * (K / 128) + c];
   };
   auto a_store = [&](int buf) {
-    *reinterpret_cast<uint4*>(&Sh[buf][ar0 * QP + acol]) = h0;
-    *reinterpret_cast<uint4*>(&Sl[buf][ar0 * QP + acol]) = l0;
-    *reinterpret_cast<uint4*>(&Sh[buf][ar1 * QP + acol]) = h1;
-    *reinterpret_cast<uint4*>(&Sl[buf][ar1 * QP + acol]) = l1;
+    const int p0 = ar0 * QP + ((acol >> 4) ^ a_swz(ar0)) * 16;
+    const int p1 = ar1 * QP + ((acol >> 4) ^ a_swz(ar1)) * 16;
+    *reinterpret_cast<uint4*>(&Sh[buf][p0]) = h0;
+    *reinterpret_cast<uint4*>(&Sl[buf][p0]) = l0;
+    *reinterpret_cast<uint4*>(&Sh[buf][p1]) = h1;
+    *reinterpret_cast<uint4*>(&Sl[buf][p1]) = l1;
     if (tid < BM) *reinterpret_cast<uint32_t*>(&Ss[buf][tid * 4]) = sv;
     if constexpr (FMT == MOE_W_MXFP4) Bs[buf][tid] = bsv;
     if constexpr (FMT == MOE_W_FP8_B128)
@@ -858,10 +860,15 @@ __device__ __forceinline__ void ffn_mx_pipe_body(const FfnArgs& a) {
   // B subtiles; accumulators pinned after each step
   auto compute = [&](int buf, const QRaw<FMT> (&r)[NSUB]) {
     auto frag = [&](int i, i32x8& h, i32x8& l, int& sa) {
-      const int o = (i * 16 + l16) * QP + g * 32;
-      h = *reinterpret_cast<const i32x8*>(&Sh[buf][o]);
-      l = *reinterpret_cast<const i32x8*>(&Sl[buf][o]);
-      sa = Ss[buf][(i * 16 + l16) * 4 + g];
+      const int rw = i * 16 + l16, sw = a_swz(rw);
+      const int o0 = rw * QP + ((2 * g) ^ sw) * 16, o1 = rw * QP + ((2 * g + 1) ^ sw) * 16;
+      const i32x4 h0 = *reinterpret_cast<const i32x4*>(&Sh[buf][o0]);
+      const i32x4 h1 = *reinterpret_cast<const i32x4*>(&Sh[buf][o1]);
+      const i32x4 l0 = *reinterpret_cast<const i32x4*>(&Sl[buf][o0]);
+      const i32x4 l1 = *reinterpret_cast<const i32x4*>(&Sl[buf][o1]);
+      h = i32x8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+      l = i32x8{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+      sa = Ss[buf][rw * 4 + g];
     };
     i32x8 ah, al;
     int sa;
